@@ -1,0 +1,275 @@
+"""Verify-step benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3|4] [--no-cpu-baseline]
+
+A step is one pass of the whole verify path over one batch of synthetic input:
+64 layers of 4-bit (config 3) or 8-bit (config 4) affine group-quantized
+projections of 27B-like shape, multi-row attention over a bf16 KV cache on
+every fourth layer, the float32 lm_head and exact acceptance over the
+vocabulary (logits mode). The step is captured once into a HIP graph and
+replayed; inputs are resident in HBM when timing starts.
+
+Printed (one JSON line): verify-step HBM GB/s over the step's algorithmic bytes
+(weights once + K/V once per attention layer + the logit rows), its fraction of
+the 8 TB/s peak, ms per step, cost(M=8)/cost(M=1) of the 64-layer weight
+stream, a roofline record of the dominant kernel (the skinny QMM, timed per
+launch with HIP events on its stream) and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "verify-step HBM GB/s (% of peak) and cost(M=8)/cost(M=1) at 27B shapes"
+
+CONFIGS = {
+    3: dict(bits=4, lm_bits=4, M=4, ctx=16384, temperature=0.7, top_k=0, top_p=0.95,
+            workload="27B-shaped dense verify step: 64 layers 4-bit g64 (hidden 5120, MLP 17408, q/k/v/o, "
+                     "gate/up/down), attention on 16 layers over bf16 KV at 16k context (Hq 24, Hkv 4, D 256), "
+                     "M=4 rows (K=3 drafts), lm_head 248320 fp32 logits, exact acceptance T=0.7 top-p 0.95"),
+    4: dict(bits=8, lm_bits=8, M=8, ctx=131072, temperature=1.0, top_k=20, top_p=0.95,
+            workload="27B-shaped dense verify step, 8-bit pack: 64 layers 8-bit g64, attention on 16 layers over "
+                     "bf16 KV at 128k context, M=8 rows (K=7 drafts), lm_head 248320 fp32 logits, exact acceptance "
+                     "T=1.0 top-k 20 + top-p 0.95"),
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_weights(cfg, torch, seed: int, T_cap: int):
+    """Synthetic packs on the device: uniform code words, scales N(0.02, 0.005), biases N(0, 0.01);
+    KV caches N(0, 1)."""
+    from speculative_decoding_verify_vq_amd.stack import QPack, StackWeights
+    from synth import bf16_normal_torch, random_words_torch
+    dev = torch.device("cuda")
+    w = StackWeights()
+    sh = cfg.shapes()
+    s = seed
+    for li in range(cfg.layers):
+        lay = {}
+        for name in ("qkv", "o", "gate_up", "down"):
+            N, K = sh[name]
+            s += 1
+            lay[name] = QPack(random_words_torch(N * K * cfg.bits // 32, s, dev),
+                              bf16_normal_torch((N, K // 64), 0.02, 0.005, s + 100000, dev),
+                              bf16_normal_torch((N, K // 64), 0.0, 0.01, s + 200000, dev), N, K, cfg.bits)
+        w.layers.append(lay)
+    N, K = sh["lm_head"]
+    w.lm_head = QPack(random_words_torch(N * K * cfg.lm_bits // 32, seed + 7, dev),
+                      bf16_normal_torch((N, K // 64), 0.02, 0.005, seed + 8, dev),
+                      bf16_normal_torch((N, K // 64), 0.0, 0.01, seed + 9, dev), N, K, cfg.lm_bits)
+    for a in range(cfg.n_attn):
+        w.k_cache.append(bf16_normal_torch((cfg.Hkv, T_cap, cfg.D), 0.0, 1.0, seed + 300000 + a, dev))
+        w.v_cache.append(bf16_normal_torch((cfg.Hkv, T_cap, cfg.D), 0.0, 1.0, seed + 400000 + a, dev))
+    torch.cuda.synchronize()
+    return w
+
+
+def capture(torch, fn):
+    """Warm up fn once on a side stream, then capture it into a graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, steps: int, warmup: int) -> float:
+    """ms per replay over exactly `steps` replays after `warmup` untimed ones."""
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def qmm_roofline(torch, vq, stack, reps: int = 3):
+    """Average duration of the skinny-QMM launches of one step, each launch
+    bracketed by HIP events on the stream it runs on; algorithmic bytes per
+    launch from the packed codes, scales, biases, activations and outputs."""
+    from speculative_decoding_verify_vq_amd.stack import qmm_algorithmic_bytes as algorithmic_bytes
+    cfg = stack.cfg
+    stream = torch.cuda.current_stream()
+    launches = []
+    for _ in range(reps):
+        for li, lay in enumerate(stack.w.layers):
+            for name, x, out in (("qkv", stack.a, stack.qkv), ("o", stack.qkv[:, : cfg.q_width], stack.proj),
+                                 ("gate_up", stack.a, stack.gu), ("down", stack.act, stack.proj)):
+                p = lay[name]
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                stack._qmm(x, p, out)
+                e1.record(stream)
+                launches.append((e0, e1, algorithmic_bytes(cfg.M, p.N, p.K, p.bits)))
+        p = stack.w.lm_head
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        stack._qmm(stack.a, p, stack.logits[0])
+        e1.record(stream)
+        launches.append((e0, e1, algorithmic_bytes(cfg.M, p.N, p.K, p.bits, out_bytes=4)))
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1, _ in launches]
+    nbytes = [b for _, _, b in launches]
+    avg_ms = float(np.mean(ms))
+    avg_bytes = float(np.mean(nbytes))
+    return {"avg_ms": avg_ms, "avg_bytes": avg_bytes, "launches": len(launches),
+            "achieved_GBs": avg_bytes / (avg_ms * 1e-3) / 1e9}
+
+
+def cpu_baseline(cfg_id: int, cfg, step_bytes: float) -> dict:
+    """The oracle timed on a bounded sample of the same workload on this host's cores:
+    one o projection (5120 x 6144) at the step's M, two attention rows at the step's
+    context, and one acceptance over the full vocabulary. Rate = algorithmic bytes of
+    the sample / CPU seconds, in GB/s (the step rate is extrapolated from the same
+    bytes-per-second)."""
+    import oracle.accept as oacc
+    import oracle.attn as oattn
+    import oracle.qmm as oqmm
+    from synth import accept_logits, attn_inputs, qmm_activations, qmm_weights, uniforms24
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    M = cfg.M
+    w = qmm_weights(1, 5120, 6144, cfg.bits)
+    x = qmm_activations(1, M, 6144)
+    t0 = time.perf_counter()
+    oqmm.skinny_qmm(x, w["wq"], w["scales"], w["biases"], cfg.bits, 64, M, 5120, 6144)
+    t_qmm = time.perf_counter() - t0
+    b_qmm = oqmm.algorithmic_bytes(M, 5120, 6144, cfg.bits)
+    T = cfg.ctx + M
+    q, k, v = attn_inputs(2, M, cfg.Hq, cfg.Hkv, cfg.D, T)
+    t0 = time.perf_counter()
+    oattn.multirow_attention(q, k, v, M, cfg.Hq, cfg.Hkv, cfg.D, T, T, cfg.D ** -0.5, pairs=[(0, 0), (M - 1, 6)])
+    t_attn = time.perf_counter() - t0
+    b_attn = 2 * 2 * T * cfg.D * 2  # the K and V rows of one KV head read for the two rows
+    K = M - 1
+    pl, ql = accept_logits(cfg_id, K, cfg.vocab)
+    P, Q = oacc.probs_f32(pl, cfg.temperature), oacc.probs_f32(ql, cfg.temperature)
+    us = uniforms24(cfg_id, (K + 1,))
+    t0 = time.perf_counter()
+    oacc.spec_accept(P, Q, [1, 2, 3, 4, 5, 6, 7][:K], us, cfg.top_k, cfg.top_p)
+    t_acc = time.perf_counter() - t0
+    b_acc = (2 * K + 1) * cfg.vocab * 4
+    secs = t_qmm + t_attn + t_acc
+    nbytes = b_qmm + b_attn + b_acc
+    rate = nbytes / secs / 1e9
+    return {"value": round(rate, 4), "unit": "GB/s", "cores": cores, "blas_threads": blas_threads,
+            "kind": "oracle",
+            "sample": f"o projection 5120x6144 {cfg.bits}-bit at M={M} ({t_qmm:.2f} s), 2 attention rows at "
+                      f"T={T} ({t_attn:.2f} s), one acceptance over V={cfg.vocab} ({t_acc:.2f} s); "
+                      f"{nbytes / 1e6:.1f} MB in {secs:.2f} s",
+            "ms_per_step_extrapolated": round(step_bytes / (rate * 1e9) * 1e3, 1)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=[3, 4])
+    ap.add_argument("--layers", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ratio", action="store_true", help="skip the M=1 / M=8 weight-stream ratio")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the verify step; runs on more than one GPU are not "
+              "part of this build (see DESIGN.md for how the path would shard).", file=sys.stderr)
+        return 2
+
+    import torch
+    from speculative_decoding_verify_vq_amd import vq
+    from speculative_decoding_verify_vq_amd.stack import DenseVerifyStack, StackConfig
+    from synth import accept_logits, uniforms24
+
+    c = CONFIGS[args.config]
+    cfg = StackConfig(layers=args.layers, bits=c["bits"], lm_bits=c["lm_bits"], M=c["M"], ctx=c["ctx"],
+                      temperature=c["temperature"], top_k=c["top_k"], top_p=c["top_p"])
+    T_cap = cfg.ctx + 16
+    log(f"config {args.config}: generating weights and KV caches on the device")
+    w = make_weights(cfg, torch, 1000 * args.config, T_cap)
+    stack = DenseVerifyStack(cfg, w)
+    dev = torch.device("cuda")
+    M, K, V = cfg.M, cfg.M - 1, cfg.vocab
+    h_in = (torch.randn((M, cfg.hidden), generator=torch.Generator(device=dev).manual_seed(5), device=dev)
+            .to(torch.bfloat16))
+    pl, ql = accept_logits(args.config, K, V)
+    draft_logits = torch.from_numpy(ql[None]).to(dev)
+    drafts = torch.tensor([[int(np.argmax(ql[i])) for i in range(K)]], dtype=torch.int32, device=dev)
+    uniforms = torch.from_numpy(uniforms24(args.config, (1, K + 1))).to(dev)
+
+    log("capturing the verify step")
+    g = capture(torch, lambda: stack.step(h_in, draft_logits, drafts, uniforms))
+    log(f"timing {args.steps} steps after {args.warmup} warmup")
+    ms = time_graph(torch, g, args.steps, args.warmup)
+    nbytes = stack.bytes_per_step()
+    gbs = nbytes["total"] / (ms * 1e-3) / 1e9
+    tok, n = stack.tokens.cpu().tolist(), int(stack.n_acc.item())
+    log(f"step {ms:.3f} ms, {gbs:.1f} GB/s; tokens {tok} n_accepted {n}")
+
+    ratio = None
+    if not args.no_ratio:
+        res = {}
+        for m in (1, 8):
+            cm = StackConfig(**{**cfg.__dict__, "M": m})
+            st = DenseVerifyStack(cm, w)
+            hm = torch.randn((m, cfg.hidden), device=dev).to(torch.bfloat16)
+            gm = capture(torch, lambda: st.forward_hidden(hm))
+            res[m] = time_graph(torch, gm, max(5, args.steps // 2), 2)
+            del gm, st
+        ratio = res[8] / res[1]
+        log(f"64-layer stack: M=1 {res[1]:.3f} ms, M=8 {res[8]:.3f} ms, ratio {ratio:.3f}")
+
+    roof = qmm_roofline(torch, vq, stack)
+    log(f"QMM per launch: {roof['avg_ms'] * 1e3:.1f} us, {roof['achieved_GBs']:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(args.config, cfg, nbytes["total"])
+
+    out = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": c["workload"], "layers": cfg.layers, "M": M, "ctx": cfg.ctx, "bits": cfg.bits,
+                   "vocab": V, "bytes_per_step": nbytes},
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "cost_ratio_m8_m1": None if ratio is None else round(ratio, 4),
+        "roofline": {"bound": "hbm", "achieved": round(roof["achieved_GBs"], 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(roof["achieved_GBs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "qmm_kernel", "avg_launch_us": round(roof["avg_ms"] * 1e3, 2),
+                     "avg_algorithmic_bytes": int(roof["avg_bytes"]), "launches_timed": roof["launches"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

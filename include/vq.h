@@ -1,0 +1,192 @@
+/*
+ * vq.h — C ABI of the batched K-token verify pass of MTP speculative decoding
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Three operations, as the pages state the problem:
+ *   vq_skinny_qmm     M = 1..16 bf16 rows times a 4-bit or 8-bit affine
+ *                     group-quantized weight matrix, the weights read from HBM
+ *                     once for all rows (page "Speculative decoding and MTP on
+ *                     Apple silicon", Facts: the stock quantized matmul re-reads
+ *                     the weights for every row of the M = 2..8 verify window; a
+ *                     small-M kernel shares them across up to 16 rows; page "The
+ *                     fastest way to run local LLMs on a Mac", section "Why
+ *                     native MTP doubles decode": the verify pass reads the
+ *                     weights once).
+ *   vq_multirow_attn  M query rows, causal among the drafted rows, grouped-query
+ *                     attention over a long bf16 KV cache, each KV tile read once
+ *                     for all rows (same page, Facts: decode attention re-reads
+ *                     the KV cache per query row; a multi-row kernel reads each
+ *                     KV tile once).
+ *   vq_spec_accept    exact Leviathan–Chen acceptance: accept with probability
+ *                     min(1, p/q), resample from (p - q)+ at the first rejection,
+ *                     identical top-k / top-p truncation of p and q (page "The
+ *                     fastest way to run local LLMs on a Mac", section "Why exact
+ *                     acceptance matters"; page "Speculative decoding and MTP on
+ *                     Apple silicon", Facts: rejection sampling and identical
+ *                     truncation of draft and verify distributions).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer named as data is a device pointer owned by the caller. The
+ *     library never allocates device memory in a call: scratch space comes from
+ *     the caller's `workspace`, sized by the matching *_workspace() query.
+ *   - A workspace holds a region of completion counters that must be zero
+ *     before its first use (allocate it zero-filled). Every call leaves those
+ *     counters zero again when it completes, so the same workspace can be
+ *     reused by later calls on the same stream. Calls that run concurrently
+ *     must not share a workspace.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and does not synchronise the host. Outputs are valid once the
+ *     stream has reached the call. Outputs must not alias inputs.
+ *   - All shapes, strides, pointers and parameters are validated on the host
+ *     before anything is launched; a failed check returns VQ_ERR_INVALID_ARG
+ *     and launches nothing. A launch failure returns VQ_ERR_HIP. The detail of
+ *     the last error on the calling thread is in vq_last_error().
+ *   - No call prints, aborts or throws across the ABI.
+ *   - The library runs on gfx950 only.
+ */
+#ifndef VQ_H_
+#define VQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define VQ_OK 0
+#define VQ_ERR_INVALID_ARG 1
+#define VQ_ERR_HIP 2
+#define VQ_ERR_UNSUPPORTED_DEVICE 3
+
+/* Output element types for vq_skinny_qmm. */
+#define VQ_BF16 0
+#define VQ_F32 1
+
+/* Input kinds for vq_spec_accept. */
+#define VQ_PROBS 0
+#define VQ_LOGITS 1
+
+/* Limits. */
+#define VQ_MAX_ROWS 16      /* M of vq_skinny_qmm and vq_multirow_attn        */
+#define VQ_MAX_DRAFTS 15    /* K of vq_spec_accept (M = K + 1 <= 16)          */
+#define VQ_MAX_VOCAB (1 << 20)
+
+/* Short text for a status code (static storage). */
+const char* vq_status_string(int status);
+
+/* Detail of the last failed call on the calling thread ("" if none). */
+const char* vq_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* vq_version(void);
+
+/* ------------------------------------------------------------------------
+ * Skinny quantized matmul
+ *
+ *   y[m, n] = sum_k x[m, k] * (s[n, k / gs] * q[n, k] + b[n, k / gs])
+ *
+ * x        bf16, M rows of K elements, row stride ldx (elements, >= K).
+ * wq       packed unsigned codes of W[N, K], row-major by output n, each row
+ *          K * bits / 8 bytes:
+ *            bits = 4: element k of row n is the nibble at bits 4*(k%8) ..
+ *                      4*(k%8)+3 of little-endian 32-bit word k/8 of that row;
+ *            bits = 8: element k of row n is byte k of that row.
+ * scales,  bf16 [N, K / gs] row-major: one affine scale s and bias b per group of
+ * biases   gs consecutive elements along K.
+ * bits     4 or 8.  gs: 64 (the only group size built).
+ * M        1 .. 16 rows.  N >= 1.  K: a positive multiple of 64.
+ * y        M rows of N outputs, row stride ldy (elements, >= N); y_dtype is
+ *          VQ_BF16 (round to nearest even) or VQ_F32.
+ * Alignment: x, wq and each row start of x must be 16-byte aligned (ldx a
+ * multiple of 8); scales and biases 4-byte aligned; y 4-byte aligned.
+ * Accumulation is float32 with a fixed reduction order, so repeated calls give
+ * bit-identical results.
+ * ---------------------------------------------------------------------- */
+size_t vq_skinny_qmm_workspace(int bits, int group_size, int M, int N, int K);
+
+int vq_skinny_qmm(const void* x, int64_t ldx,
+                  const void* wq, const void* scales, const void* biases,
+                  int bits, int group_size, int M, int N, int K,
+                  void* y, int64_t ldy, int y_dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Multi-row decode attention
+ *
+ * For query row i in [0, M), query head h, KV head g = h / (Hq / Hkv):
+ *   out[i, h] = sum_{j <= T - M + i} softmax_j(scale * <q[i, h], k[g, j]>) v[g, j]
+ * i.e. the M query rows are the last M of the T valid positions (causal among
+ * the drafted rows, bottom-right aligned).
+ *
+ * q        bf16 [M, Hq, D]: heads of one row contiguous, consecutive rows
+ *          q_row_stride elements apart (>= Hq * D, a multiple of 8).
+ * k_cache, bf16 [Hkv, T_cap, D]: row stride D elements, head stride
+ * v_cache  kv_head_stride elements (>= T * D, a multiple of 8).
+ * M        1 .. 16.  Hq % Hkv == 0, Hq / Hkv * M <= 128.  D: 64, 128 or 256.
+ * T        number of valid keys, M <= T.
+ * out      bf16 [M, Hq, D], rows out_row_stride elements apart (>= Hq * D,
+ *          a multiple of 8).
+ * Alignment: q, k_cache, v_cache and out 16-byte aligned.
+ * Float32 scores, softmax and accumulation; P is rounded to bf16 for the PV
+ * product; deterministic.
+ * ---------------------------------------------------------------------- */
+size_t vq_multirow_attn_workspace(int M, int Hq, int Hkv, int D, int T);
+
+int vq_multirow_attn(const void* q, int64_t q_row_stride, const void* k_cache,
+                     const void* v_cache, int64_t kv_head_stride, int M, int Hq, int Hkv,
+                     int D, int T, float scale, void* out, int64_t out_row_stride,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Exact speculative acceptance
+ *
+ * One verify per batch entry b in [0, B):
+ *   target rows  p + b * p_batch_stride : K+1 rows of V float32
+ *   draft rows   q + b * q_batch_stride : K rows of V float32
+ * (a stride of 0 shares the same rows across the batch).
+ * input_kind   VQ_PROBS: rows are probabilities in [0, 1];
+ *              VQ_LOGITS: rows are logits and p = softmax(logits / temperature)
+ *              is computed in float32 first (temperature > 0). In VQ_PROBS mode
+ *              temperature is ignored.
+ * draft        int32 [B, K] drafted token ids.
+ * uniforms     float32 [B, K+1] in [0, 1): u_0..u_{K-1} for the K accept tests,
+ *              u_K for the final draw.
+ * top_k        0 = off, else keep the top_k most probable tokens (ties: lower id).
+ * top_p        (0, 1]: then keep the shortest prefix (same order) whose mass
+ *              reaches top_p of the top-k mass; 1 = off.
+ * out_tokens   int32 [B, K+1]: accepted drafts, then the drawn token, then -1.
+ * out_n_accepted int32 [B]: number of accepted drafts, or -1 for an invalid
+ *              entry (a NaN or a probability outside [0, 1], a row that keeps no
+ *              mass, a draft id outside [0, V), a uniform outside [0, 1)); an
+ *              invalid entry has every token -1.
+ * probs_out    nullable; in VQ_LOGITS mode receives the float32 probabilities
+ *              of every row, [B', 2K+1, V] (target rows then draft rows), with
+ *              B' = 1 if both strides are 0 and B otherwise.
+ * Limits       1 <= B, 0 <= K <= 15, 2 <= V <= 2^20.
+ *
+ * Decision arithmetic (bit-exact, reproducible on any implementation): masses
+ * m(x) = floor(p(x) * 2^40); order by (p descending, id ascending); top-k keeps
+ * the first top_k; top-p keeps token t iff (kept mass before t) * 2^24 <
+ * max(1, floor(top_p * 2^24)) * (top-k mass); Z = kept mass. Draft d_i is
+ * accepted iff floor(u_i*2^24) * mQ(d_i) * ZP < mP(d_i) * ZQ * 2^24. At the
+ * first rejection j the token is drawn from r = max(0, mP_j*ZQ_j - mQ_j*ZP_j)
+ * (from mP_j if r is all zero), after K acceptances from mP_K, as the smallest
+ * t with r[0] + .. + r[t] > floor(floor(u_K*2^24) * sum(r) / 2^24).
+ * ---------------------------------------------------------------------- */
+size_t vq_spec_accept_workspace(int B, int K, int V, int input_kind,
+                                int64_t p_batch_stride, int64_t q_batch_stride);
+
+int vq_spec_accept(const float* p, const float* q, int input_kind,
+                   int64_t p_batch_stride, int64_t q_batch_stride,
+                   const int32_t* draft, const float* uniforms,
+                   int B, int K, int V, float temperature, int top_k, float top_p,
+                   int32_t* out_tokens, int32_t* out_n_accepted, float* probs_out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VQ_H_ */

@@ -1,0 +1,335 @@
+// Multi-row decode attention for gfx950.
+//
+// For query row i < M, query head h, KV head g = h / G (G = Hq / Hkv):
+//   out[i, h] = sum_{j <= T-M+i} softmax_j(scale * <q[i,h], k[g,j]>) * v[g,j]
+//
+// Stock decode attention re-reads the KV cache once per query row; a
+// multi-row kernel reads each KV tile once for all rows (page "Speculative
+// decoding and MTP on Apple silicon", Facts). Here one workgroup owns one KV
+// head and one contiguous range of keys; all M*G query rows that share the KV
+// head are processed against each K/V tile while it sits in LDS, so every KV
+// byte is read from HBM once per call.
+//
+// Per 32-key tile:
+//   * the tile is loaded with coalesced 16-byte loads into registers one tile
+//     ahead, then written to LDS row-major;
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q rows
+//     from LDS); in the output layout each lane holds 16 keys of one query row,
+//     so the online-softmax statistics of a row live in one lane pair;
+//   * O^T += V^T P^T on the same MFMA: B = P (this lane's own probabilities,
+//     rounded to bf16), A = V gathered from LDS along the key axis with 16-bit
+//     reads, so the row rescaling stays lane-local.
+// Waves split the query rows into tiles of 32 and, when there are few rows,
+// the head dimension of O across waves (each of those waves recomputes the
+// same S tile, which costs MFMA time the memory-bound kernel has to spare).
+// With several key ranges per head, unnormalised partial O and the (max, sum)
+// statistics go to the workspace and a combine kernel merges them.
+#include <math.h>
+
+#include "vq_internal.h"
+
+namespace vq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kTileKeys = 32;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+
+template <int D, int RT>
+struct AttnCfg {
+  static constexpr int DS0 = (RT == 1) ? 4 : (RT == 2) ? 2 : 1;
+  static constexpr int DS = DS0 < D / 32 ? DS0 : D / 32;  // head-dim slices per row tile
+  static constexpr int DW = D / DS;                         // head dims per wave
+  static constexpr int DT = DW / 32;                        // 32-wide d tiles per wave
+  static constexpr int LD = D + 8;                          // LDS row stride (elements)
+  static constexpr int UNITS = kTileKeys * D / 8;           // 16-byte units per K (or V) tile
+  static constexpr int PER_THREAD = (UNITS + kThreads - 1) / kThreads;
+};
+
+template <int D, int RT>
+__global__ __launch_bounds__(kThreads) void attn_partial_kernel(
+    const uint16_t* __restrict__ q, int64_t q_rs, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, int64_t kv_head_stride, int M, int Hq, int Hkv, int T, float scale_log2,
+    int keys_per_split, int splits, uint16_t* __restrict__ out, int64_t out_rs, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  using C = AttnCfg<D, RT>;
+  __shared__ uint16_t q_lds[RT * 32 * C::LD];
+  __shared__ uint16_t k_lds[kTileKeys * C::LD];
+  __shared__ uint16_t v_lds[kTileKeys * C::LD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kq = lane >> 5;
+  const int l32 = lane & 31;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int rows = M * G;
+  const int j0 = split * keys_per_split;
+  const int j1 = min(T, j0 + keys_per_split);
+
+  // Stage the query rows of this KV head: row i = (position i / G, head kvh*G + i % G).
+  for (int u = tid; u < RT * 32 * (D / 8); u += kThreads) {
+    const int i = u / (D / 8);
+    const int dc = u % (D / 8);
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (i < rows) {
+      const int m = i / G, g = i % G;
+      val = *reinterpret_cast<const uint4*>(q + (size_t)m * q_rs + ((size_t)kvh * G + g) * D + dc * 8);
+    }
+    *reinterpret_cast<uint4*>(&q_lds[i * C::LD + dc * 8]) = val;
+  }
+
+  const uint16_t* kh = kc + (size_t)kvh * kv_head_stride;
+  const uint16_t* vh = vc + (size_t)kvh * kv_head_stride;
+  uint4 kr[C::PER_THREAD], vr[C::PER_THREAD];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int e = 0; e < C::PER_THREAD; ++e) {
+      const int u = tid + e * kThreads;
+      kr[e] = make_uint4(0, 0, 0, 0);
+      vr[e] = make_uint4(0, 0, 0, 0);
+      if (u < C::UNITS) {
+        const int key = t0 + u / (D / 8);
+        const int dc = u % (D / 8);
+        if (key < j1) {
+          kr[e] = *reinterpret_cast<const uint4*>(kh + (size_t)key * D + dc * 8);
+          vr[e] = *reinterpret_cast<const uint4*>(vh + (size_t)key * D + dc * 8);
+        }
+      }
+    }
+  };
+  if (j0 < j1) fetch(j0);
+
+  const int rt = wave / C::DS;
+  const int dpart = wave % C::DS;
+  const bool active = wave < RT * C::DS;
+  const int row = rt * 32 + l32;             // this lane's query row (softmax owner)
+  const bool row_ok = row < rows;
+  const int mpos = row_ok ? row / G : 0;
+  const int limit = row_ok ? T - M + mpos : T - 1;  // last visible key of the row
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 o[C::DT];
+#pragma unroll
+  for (int t = 0; t < C::DT; ++t) o[t] = f32x16{};
+
+  for (int t0 = j0; t0 < j1; t0 += kTileKeys) {
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < C::PER_THREAD; ++e) {
+      const int u = tid + e * kThreads;
+      if (u < C::UNITS) {
+        const int key = u / (D / 8);
+        const int dc = u % (D / 8);
+        *reinterpret_cast<uint4*>(&k_lds[key * C::LD + dc * 8]) = kr[e];
+        *reinterpret_cast<uint4*>(&v_lds[key * C::LD + dc * 8]) = vr[e];
+      }
+    }
+    __syncthreads();
+    if (t0 + kTileKeys < j1) fetch(t0 + kTileKeys);
+    if (!active) continue;
+
+    // S^T[key][row] = sum_d K[key][d] Q[row][d]
+    f32x16 s = {};
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[l32 * C::LD + 16 * i + 8 * kq]);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&q_lds[row * C::LD + 16 * i + 8 * kq]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s, 0, 0, 0);
+    }
+    // Scale, mask, online softmax for this lane's row (keys split between lanes l, l^32).
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = t0 + 8 * (r >> 2) + 4 * kq + (r & 3);
+      const float v = (j < j1 && j <= limit) ? s[r] * scale_log2 : -INFINITY;
+      s[r] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = exp2f(s[r] - m_use);
+      psum += s[r];
+    }
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    u32x4 pw0, pw1;
+    pw0[0] = pack_bf16x2(s[0], s[1]);
+    pw0[1] = pack_bf16x2(s[2], s[3]);
+    pw0[2] = pack_bf16x2(s[4], s[5]);
+    pw0[3] = pack_bf16x2(s[6], s[7]);
+    pw1[0] = pack_bf16x2(s[8], s[9]);
+    pw1[1] = pack_bf16x2(s[10], s[11]);
+    pw1[2] = pack_bf16x2(s[12], s[13]);
+    pw1[3] = pack_bf16x2(s[14], s[15]);
+    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, pw0);
+    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, pw1);
+
+    // O^T[d][row] += sum_key V[key][d] P[row][key]. For MFMA c, element j of
+    // this lane covers key 16c + 8*(j/4) + 4*kq + j%4, matching P's layout.
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      const int d = dpart * C::DW + t * 32 + l32;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        u32x4 aw;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int k0 = 16 * c + 8 * ((2 * jj) >> 2) + 4 * kq + ((2 * jj) & 3);
+          const uint32_t lo = v_lds[k0 * C::LD + d];
+          const uint32_t hi = v_lds[(k0 + 1) * C::LD + d];
+          aw[jj] = lo | (hi << 16);
+        }
+        const bf16x8 a = __builtin_bit_cast(bf16x8, aw);
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, c ? pb1 : pb0, o[t], 0, 0, 0);
+      }
+    }
+  }
+
+  if (!active || !row_ok) return;
+  const int g = row % G;
+  const int h = kvh * G + g;
+  if (splits == 1) {
+    const float inv = 1.f / l_run;
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = dpart * C::DW + t * 32 + 8 * a4 + 4 * kq;
+        uint2 w;
+        w.x = pack_bf16x2(o[t][4 * a4] * inv, o[t][4 * a4 + 1] * inv);
+        w.y = pack_bf16x2(o[t][4 * a4 + 2] * inv, o[t][4 * a4 + 3] * inv);
+        *reinterpret_cast<uint2*>(out + (size_t)mpos * out_rs + (size_t)h * D + d) = w;
+      }
+    }
+    return;
+  }
+  float* po = part_o + (((size_t)split * Hkv + kvh) * rows + row) * D;
+#pragma unroll
+  for (int t = 0; t < C::DT; ++t) {
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d = dpart * C::DW + t * 32 + 8 * a4 + 4 * kq;
+      *reinterpret_cast<float4*>(po + d) =
+          make_float4(o[t][4 * a4], o[t][4 * a4 + 1], o[t][4 * a4 + 2], o[t][4 * a4 + 3]);
+    }
+  }
+  if (dpart == 0 && kq == 0) {
+    float* pml = part_ml + (((size_t)split * Hkv + kvh) * rows + row) * 2;
+    pml[0] = m_run;
+    pml[1] = l_run;
+  }
+}
+
+// Merge the per-range partials of one (query row, KV head): one thread per head dim.
+__global__ __launch_bounds__(256) void attn_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int M, int Hq, int Hkv, int D,
+    int splits, uint16_t* __restrict__ out, int64_t out_rs) {
+  const int row = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int rows = M * G;
+  float mmax = -INFINITY;
+  for (int s = 0; s < splits; ++s)
+    mmax = fmaxf(mmax, part_ml[(((size_t)s * Hkv + kvh) * rows + row) * 2]);
+  const int m = row / G;
+  const int h = kvh * G + row % G;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const size_t base = ((size_t)s * Hkv + kvh) * rows + row;
+      const float ms = part_ml[base * 2];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - mmax);
+      den += w * part_ml[base * 2 + 1];
+      num += w * part_o[base * D + d];
+    }
+    out[(size_t)m * out_rs + (size_t)h * D + d] = f32_to_bf16_rne(num / den);
+  }
+}
+
+}  // namespace
+
+AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T) {
+  AttnPlan p{};
+  p.rows = M * (Hq / Hkv);
+  p.row_tiles = (p.rows + 31) / 32;
+  // About two workgroups per compute unit, at least 128 keys per range.
+  const int tiles = (T + kTileKeys - 1) / kTileKeys;
+  int s = (2 * kNumCU + Hkv - 1) / Hkv;
+  int max_s = (tiles + 3) / 4;
+  s = s > max_s ? max_s : s;
+  s = s < 1 ? 1 : s;
+  const int tiles_per = (tiles + s - 1) / s;
+  p.keys_per_split = tiles_per * kTileKeys;
+  p.splits = (T + p.keys_per_split - 1) / p.keys_per_split;
+  p.partial_bytes = p.splits > 1 ? align_up((size_t)p.splits * Hkv * p.rows * (D + 2) * sizeof(float), 256) : 0;
+  (void)D;
+  return p;
+}
+
+hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const void* k, const void* v,
+                       int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T, float scale,
+                       void* out, int64_t out_rs, void* workspace, hipStream_t stream) {
+  float* part_o = reinterpret_cast<float*>(workspace);
+  float* part_ml = plan.splits > 1
+                       ? part_o + (size_t)plan.splits * Hkv * plan.rows * D
+                       : nullptr;
+  dim3 grid(plan.splits, Hkv);
+  auto* qp = reinterpret_cast<const uint16_t*>(q);
+  auto* kp = reinterpret_cast<const uint16_t*>(k);
+  auto* vp = reinterpret_cast<const uint16_t*>(v);
+  auto* op = reinterpret_cast<uint16_t*>(out);
+  const float sl2 = scale * kLog2e;
+#define VQ_ATTN(DV, RTV)                                                                        \
+  hipLaunchKernelGGL((attn_partial_kernel<DV, RTV>), grid, dim3(kThreads), 0, stream, qp, q_rs, kp, vp, \
+                     kv_head_stride, M, Hq, Hkv, T, sl2, plan.keys_per_split, plan.splits, op,         \
+                     out_rs, part_o, part_ml)
+#define VQ_ATTN_RT(DV)                         \
+  switch (plan.row_tiles) {                    \
+    case 1: VQ_ATTN(DV, 1); break;             \
+    case 2: VQ_ATTN(DV, 2); break;             \
+    case 3: VQ_ATTN(DV, 3); break;             \
+    default: VQ_ATTN(DV, 4); break;            \
+  }
+  if (D == 64) {
+    VQ_ATTN_RT(64)
+  } else if (D == 128) {
+    VQ_ATTN_RT(128)
+  } else {
+    VQ_ATTN_RT(256)
+  }
+#undef VQ_ATTN_RT
+#undef VQ_ATTN
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.splits == 1) return e;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(plan.rows, Hkv), dim3(D < 256 ? D : 256), 0, stream,
+                     part_o, part_ml, M, Hq, Hkv, D, plan.splits, op, out_rs);
+  return hipGetLastError();
+}
+
+}  // namespace vq

@@ -1,0 +1,258 @@
+// Host side of the C ABI: argument validation, workspace sizing, dispatch and
+// error reporting. Every check runs before any HIP call, so an invalid call
+// returns VQ_ERR_INVALID_ARG without touching the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "vq.h"
+#include "vq_glue.h"
+#include "vq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  snprintf(g_err, sizeof(g_err), "%s: %s", what, hipGetErrorString(e));
+  return VQ_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(VQ_ERR_UNSUPPORTED_DEVICE, "device index %d out of range", dev);
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+    if (st == 2) return fail(VQ_ERR_UNSUPPORTED_DEVICE, "device %d is %s; this library is built for gfx950 only", dev,
+                             prop.gcnArchName);
+  }
+  if (st == 2) return fail(VQ_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+  return VQ_OK;
+}
+
+int check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return VQ_OK;
+  if (ws == nullptr) return fail(VQ_ERR_INVALID_ARG, "workspace is NULL but %zu bytes are needed", need);
+  if (!aligned(ws, 256)) return fail(VQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (have < need) return fail(VQ_ERR_INVALID_ARG, "workspace has %zu bytes, %zu needed", have, need);
+  return VQ_OK;
+}
+
+bool qmm_shape_ok(int bits, int group_size, int M, int N, int K) {
+  return (bits == 4 || bits == 8) && group_size == 64 && M >= 1 && M <= VQ_MAX_ROWS && N >= 1 && K >= 64 &&
+         K % 64 == 0 && N <= (1 << 26) && K <= (1 << 24);
+}
+
+bool attn_shape_ok(int M, int Hq, int Hkv, int D, int T) {
+  return M >= 1 && M <= VQ_MAX_ROWS && Hkv >= 1 && Hkv <= 65535 && Hq >= Hkv && Hq % Hkv == 0 &&
+         (Hq / Hkv) * M <= 128 && (D == 64 || D == 128 || D == 256) && T >= M && T <= (1 << 26);
+}
+
+bool accept_shape_ok(int B, int K, int V, int input_kind, int64_t ps, int64_t qs) {
+  if (B < 1 || K < 0 || K > VQ_MAX_DRAFTS || V < 2 || V > VQ_MAX_VOCAB) return false;
+  if (input_kind != VQ_PROBS && input_kind != VQ_LOGITS) return false;
+  if (ps < 0 || qs < 0) return false;
+  if (ps != 0 && ps < (int64_t)(K + 1) * V) return false;
+  if (qs != 0 && qs < (int64_t)K * V) return false;
+  const bool shared = ps == 0 && qs == 0;
+  if (!shared && B > 65535) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vq_status_string(int status) {
+  switch (status) {
+    case VQ_OK: return "ok";
+    case VQ_ERR_INVALID_ARG: return "invalid argument";
+    case VQ_ERR_HIP: return "HIP runtime error";
+    case VQ_ERR_UNSUPPORTED_DEVICE: return "unsupported device";
+    default: return "unknown status";
+  }
+}
+
+const char* vq_last_error(void) { return g_err; }
+
+const char* vq_version(void) { return "0.1.0"; }
+
+// ------------------------------------------------------------------ QMM
+size_t vq_skinny_qmm_workspace(int bits, int group_size, int M, int N, int K) {
+  if (!qmm_shape_ok(bits, group_size, M, N, K)) return 0;
+  const vq::QmmPlan p = vq::qmm_plan(bits, M, N, K);
+  return p.counter_bytes + p.partial_bytes;
+}
+
+int vq_skinny_qmm(const void* x, int64_t ldx, const void* wq, const void* scales, const void* biases, int bits,
+                  int group_size, int M, int N, int K, void* y, int64_t ldy, int y_dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!x || !wq || !scales || !biases || !y) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: NULL data pointer");
+  if (bits != 4 && bits != 8) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: bits must be 4 or 8 (got %d)", bits);
+  if (group_size != 64) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: group_size must be 64 (got %d)", group_size);
+  if (M < 1 || M > VQ_MAX_ROWS) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: M must be in [1, 16] (got %d)", M);
+  if (!qmm_shape_ok(bits, group_size, M, N, K))
+    return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: unsupported shape N=%d K=%d (K a positive multiple of 64)", N, K);
+  if (ldx < K || ldx % 8 != 0) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: ldx must be >= K and a multiple of 8");
+  if (ldy < N) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: ldy must be >= N");
+  if (y_dtype != VQ_BF16 && y_dtype != VQ_F32) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: bad y_dtype %d", y_dtype);
+  if (!aligned(x, 16) || !aligned(wq, 16))
+    return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: x and wq must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(biases, 2) || !aligned(y, y_dtype == VQ_F32 ? 4 : 2))
+    return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: misaligned scales, biases or y");
+  const vq::QmmPlan plan = vq::qmm_plan(bits, M, N, K);
+  int rc = check_workspace(workspace, workspace_bytes, plan.counter_bytes + plan.partial_bytes);
+  if (rc) return rc;
+  if ((rc = check_device())) return rc;
+  hipError_t e = vq::qmm_launch(plan, x, ldx, wq, scales, biases, bits, M, N, K, y, ldy, y_dtype == VQ_F32,
+                                workspace, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_skinny_qmm launch");
+}
+
+// ------------------------------------------------------------ attention
+size_t vq_multirow_attn_workspace(int M, int Hq, int Hkv, int D, int T) {
+  if (!attn_shape_ok(M, Hq, Hkv, D, T)) return 0;
+  return vq::attn_plan(M, Hq, Hkv, D, T).partial_bytes;
+}
+
+int vq_multirow_attn(const void* q, int64_t q_row_stride, const void* k_cache, const void* v_cache,
+                     int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T, float scale, void* out,
+                     int64_t out_row_stride, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!q || !k_cache || !v_cache || !out) return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn: NULL data pointer");
+  if (!attn_shape_ok(M, Hq, Hkv, D, T))
+    return fail(VQ_ERR_INVALID_ARG,
+                "vq_multirow_attn: unsupported shape M=%d Hq=%d Hkv=%d D=%d T=%d (M in [1,16], Hq %% Hkv == 0, "
+                "M*Hq/Hkv <= 128, D in {64,128,256}, T >= M)",
+                M, Hq, Hkv, D, T);
+  if (kv_head_stride < (int64_t)T * D || kv_head_stride % 8 != 0)
+    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn: kv_head_stride must be >= T*D and a multiple of 8");
+  if (q_row_stride < (int64_t)Hq * D || q_row_stride % 8 != 0 || out_row_stride < (int64_t)Hq * D ||
+      out_row_stride % 8 != 0)
+    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn: row strides must be >= Hq*D and multiples of 8");
+  if (!isfinite(scale)) return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn: scale must be finite");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn: q, caches and out must be 16-byte aligned");
+  const vq::AttnPlan plan = vq::attn_plan(M, Hq, Hkv, D, T);
+  int rc = check_workspace(workspace, workspace_bytes, plan.partial_bytes);
+  if (rc) return rc;
+  if ((rc = check_device())) return rc;
+  hipError_t e = vq::attn_launch(plan, q, q_row_stride, k_cache, v_cache, kv_head_stride, M, Hq, Hkv, D, T, scale,
+                                 out, out_row_stride, workspace, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_multirow_attn launch");
+}
+
+// ----------------------------------------------------------- acceptance
+size_t vq_spec_accept_workspace(int B, int K, int V, int input_kind, int64_t p_batch_stride,
+                                int64_t q_batch_stride) {
+  if (!accept_shape_ok(B, K, V, input_kind, p_batch_stride, q_batch_stride)) return 0;
+  const vq::AcceptPlan p = vq::accept_plan(B, K, V, input_kind, p_batch_stride, q_batch_stride);
+  return p.meta_bytes + p.probs_bytes + p.table_bytes;
+}
+
+int vq_spec_accept(const float* p, const float* q, int input_kind, int64_t p_batch_stride, int64_t q_batch_stride,
+                   const int32_t* draft, const float* uniforms, int B, int K, int V, float temperature, int top_k,
+                   float top_p, int32_t* out_tokens, int32_t* out_n_accepted, float* probs_out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!p || !uniforms || !out_tokens || !out_n_accepted)
+    return fail(VQ_ERR_INVALID_ARG, "vq_spec_accept: NULL data pointer");
+  if (K > 0 && (!q || !draft)) return fail(VQ_ERR_INVALID_ARG, "vq_spec_accept: q and draft are required for K > 0");
+  if (!accept_shape_ok(B, K, V, input_kind, p_batch_stride, q_batch_stride))
+    return fail(VQ_ERR_INVALID_ARG,
+                "vq_spec_accept: unsupported arguments B=%d K=%d V=%d kind=%d strides=(%lld,%lld) (B >= 1, "
+                "K in [0,15], V in [2, 2^20], strides 0 or >= the rows of one entry, B <= 65535 unless both "
+                "strides are 0)",
+                B, K, V, input_kind, (long long)p_batch_stride, (long long)q_batch_stride);
+  if (top_k < 0) return fail(VQ_ERR_INVALID_ARG, "vq_spec_accept: top_k must be >= 0");
+  if (!(top_p > 0.f && top_p <= 1.f)) return fail(VQ_ERR_INVALID_ARG, "vq_spec_accept: top_p must be in (0, 1]");
+  if (input_kind == VQ_LOGITS && !(temperature > 0.f && isfinite(temperature)))
+    return fail(VQ_ERR_INVALID_ARG, "vq_spec_accept: temperature must be finite and > 0 for logits");
+  if (!aligned(p, 4) || (q && !aligned(q, 4)) || (draft && !aligned(draft, 4)) || !aligned(uniforms, 4) ||
+      !aligned(out_tokens, 4) || !aligned(out_n_accepted, 4) || (probs_out && !aligned(probs_out, 4)))
+    return fail(VQ_ERR_INVALID_ARG, "vq_spec_accept: misaligned pointer");
+  const vq::AcceptPlan plan = vq::accept_plan(B, K, V, input_kind, p_batch_stride, q_batch_stride);
+  int rc = check_workspace(workspace, workspace_bytes, plan.meta_bytes + plan.probs_bytes + plan.table_bytes);
+  if (rc) return rc;
+  if ((rc = check_device())) return rc;
+  hipError_t e = vq::accept_launch(plan, p, q, input_kind, p_batch_stride, q_batch_stride, draft, uniforms, B, K, V,
+                                   temperature, top_k, top_p, out_tokens, out_n_accepted, probs_out, workspace,
+                                   reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_spec_accept launch");
+}
+
+// ----------------------------------------------------------------- glue
+int vq_rmsnorm_bf16(const void* x, int64_t ldx, void* y, int64_t ldy, int M, int N, float eps, void* stream) {
+  g_err[0] = 0;
+  if (!x || !y || M < 1 || N < 1 || N > 65536 || ldx < N || ldy < N || !(eps >= 0.f) || !aligned(x, 2) ||
+      !aligned(y, 2))
+    return fail(VQ_ERR_INVALID_ARG, "vq_rmsnorm_bf16: invalid arguments");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = vq::glue_rmsnorm(x, ldx, y, ldy, M, N, eps, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_rmsnorm_bf16 launch");
+}
+
+int vq_add_bf16(const void* a, const void* b, void* y, int64_t n, void* stream) {
+  g_err[0] = 0;
+  if (!a || !b || !y || n < 0 || !aligned(a, 2) || !aligned(b, 2) || !aligned(y, 2))
+    return fail(VQ_ERR_INVALID_ARG, "vq_add_bf16: invalid arguments");
+  if (n == 0) return VQ_OK;
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = vq::glue_add(a, b, y, n, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_add_bf16 launch");
+}
+
+int vq_silu_mul_bf16(const void* gu, int64_t ldgu, void* y, int64_t ldy, int M, int I, void* stream) {
+  g_err[0] = 0;
+  if (!gu || !y || M < 1 || M > 65535 || I < 1 || ldgu < 2 * (int64_t)I || ldy < I || !aligned(gu, 2) ||
+      !aligned(y, 2))
+    return fail(VQ_ERR_INVALID_ARG, "vq_silu_mul_bf16: invalid arguments");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = vq::glue_silu_mul(gu, ldgu, y, ldy, M, I, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_silu_mul_bf16 launch");
+}
+
+int vq_kv_append_bf16(const void* src, int64_t ld_src, int k_off, int v_off, void* k_cache, void* v_cache,
+                      int64_t kv_head_stride, int M, int Hkv, int D, int pos, void* stream) {
+  g_err[0] = 0;
+  if (!src || !k_cache || !v_cache || M < 1 || Hkv < 1 || D < 8 || D % 8 || k_off < 0 || v_off < 0 ||
+      k_off % 8 || v_off % 8 || ld_src % 8 || ld_src < (int64_t)k_off + (int64_t)Hkv * D ||
+      ld_src < (int64_t)v_off + (int64_t)Hkv * D || pos < 0 || kv_head_stride % 8 ||
+      kv_head_stride < (int64_t)(pos + M) * D || !aligned(src, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(VQ_ERR_INVALID_ARG, "vq_kv_append_bf16: invalid arguments");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = vq::glue_kv_append(src, ld_src, k_off, v_off, k_cache, v_cache, kv_head_stride, M, Hkv, D, pos,
+                                    reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_kv_append_bf16 launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Internal declarations shared by the host API layer and the kernel files.
+// Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vq {
+
+// The library is built for one chip: 256 compute units in 8 XCDs (gfx950).
+constexpr int kNumCU = 256;
+constexpr int kNumXCD = 8;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- skinny QMM
+struct QmmPlan {
+  int mt;          // padded row count of the kernel variant (8 or 16)
+  int cols_per_wg; // output columns per workgroup
+  int n_blocks;    // column blocks
+  int splits;      // K splits (workgroups per column block)
+  int groups_per_split;
+  size_t counter_bytes;  // zeroed completion counters at the start of the workspace
+  size_t partial_bytes;  // float32 partial sums [splits][M][N]
+};
+QmmPlan qmm_plan(int bits, int M, int N, int K);
+hipError_t qmm_launch(const QmmPlan& plan, const void* x, int64_t ldx, const void* wq,
+                      const void* scales, const void* biases, int bits, int M, int N, int K,
+                      void* y, int64_t ldy, int y_f32, void* workspace, hipStream_t stream);
+
+// ----------------------------------------------------------- attention
+struct AttnPlan {
+  int rows;        // M * G query rows per KV head
+  int row_tiles;   // ceil(rows / 32)
+  int splits;      // KV splits per head
+  int keys_per_split;
+  size_t partial_bytes;
+};
+AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T);
+hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const void* k, const void* v,
+                       int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T, float scale,
+                       void* out, int64_t out_rs, void* workspace, hipStream_t stream);
+
+// ---------------------------------------------------------- acceptance
+struct AcceptPlan {
+  int entries;        // batch entries whose rows are prepared (1 if all rows shared)
+  int rows_per_entry; // 2K + 1
+  bool shared;        // both strides zero: per-position tables, one thread per trial
+  size_t meta_bytes;  // per-row results of truncation
+  size_t probs_bytes; // float32 probabilities (logits mode without probs_out)
+  size_t table_bytes; // shared mode: 128-bit running sums [K+1][V]
+};
+AcceptPlan accept_plan(int B, int K, int V, int input_kind, int64_t p_stride, int64_t q_stride);
+hipError_t accept_launch(const AcceptPlan& plan, const float* p, const float* q, int input_kind,
+                         int64_t p_stride, int64_t q_stride, const int32_t* draft,
+                         const float* uniforms, int B, int K, int V, float temperature, int top_k,
+                         float top_p, int32_t* out_tokens, int32_t* out_n, float* probs_out,
+                         void* workspace, hipStream_t stream);
+
+// ------------------------------------------------------------- stack glue
+hipError_t glue_rmsnorm(const void* x, int64_t ldx, void* y, int64_t ldy, int M, int N, float eps,
+                        hipStream_t s);
+hipError_t glue_add(const void* a, const void* b, void* y, int64_t n, hipStream_t s);
+hipError_t glue_silu_mul(const void* gu, int64_t ldgu, void* y, int64_t ldy, int M, int I, hipStream_t s);
+hipError_t glue_kv_append(const void* src, int64_t ld, int k_off, int v_off, void* kc, void* vc, int64_t hs,
+                          int M, int Hkv, int D, int pos, hipStream_t s);
+
+}  // namespace vq

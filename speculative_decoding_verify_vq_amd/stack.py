@@ -1,0 +1,196 @@
+"""One verify step of a dense pre-norm stack, composed from the library's kernels.
+
+The verify pass of MTP speculative decoding runs the last committed token and
+the K drafted tokens (M = K + 1 rows) through one forward pass, then accepts or
+rejects the drafts exactly (page "The fastest way to run local LLMs on a Mac",
+sections "Why native MTP doubles decode" and "Why exact acceptance matters").
+Per layer:
+
+    a   = rmsnorm(h)
+    qkv = skinny_qmm(a, W_qkv)                      fused q | k | v
+    attention layers: append k, v at positions ctx .. ctx+M-1, then
+          c = multirow_attn(q, K cache, V cache, T = ctx + M)
+    other layers (their recurrent state is out of scope): c = q
+    h  += skinny_qmm(c, W_o)
+    gu  = skinny_qmm(rmsnorm(h), W_gate_up)         fused gate | up
+    h  += skinny_qmm(silu(gate) * up, W_down)
+
+then float32 logits = skinny_qmm(rmsnorm(h), W_lm) feed spec_accept in logits
+mode together with the draft logits. Every launch goes to one stream, so the
+whole step can be captured once into a HIP graph and replayed.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+from . import vq
+
+
+def qmm_algorithmic_bytes(M: int, N: int, K: int, bits: int, group_size: int = 64, out_bytes: int = 2) -> int:
+    """Minimum HBM bytes of one skinny-QMM call: packed codes + bf16 scale and bias
+    per group + bf16 activations in + outputs."""
+    return N * K * bits // 8 + 4 * N * (K // group_size) + 2 * M * K + out_bytes * M * N
+
+
+@dataclass
+class StackConfig:
+    layers: int = 64
+    hidden: int = 5120
+    inter: int = 17408
+    Hq: int = 24
+    Hkv: int = 4
+    D: int = 256
+    vocab: int = 248320
+    bits: int = 4
+    lm_bits: int = 4
+    attn_every: int = 4          # attention on layers attn_every-1, 2*attn_every-1, ...
+    ctx: int = 16384             # committed positions in every KV cache
+    M: int = 4                   # verify rows = K + 1
+    temperature: float = 0.7
+    top_k: int = 0
+    top_p: float = 0.95
+    group_size: int = 64
+
+    def is_attn(self, layer: int) -> bool:
+        return layer % self.attn_every == self.attn_every - 1
+
+    @property
+    def q_width(self) -> int:
+        return self.Hq * self.D
+
+    @property
+    def qkv_width(self) -> int:
+        return (self.Hq + 2 * self.Hkv) * self.D
+
+    @property
+    def n_attn(self) -> int:
+        return sum(self.is_attn(i) for i in range(self.layers))
+
+    def shapes(self) -> dict:
+        """Output/input sizes (N, K) of each projection of a layer, and of the lm_head."""
+        return {"qkv": (self.qkv_width, self.hidden), "o": (self.hidden, self.q_width),
+                "gate_up": (2 * self.inter, self.hidden), "down": (self.hidden, self.inter),
+                "lm_head": (self.vocab, self.hidden)}
+
+
+@dataclass
+class QPack:
+    """One quantized weight matrix W[N, K] in the library's packed layout."""
+    wq: torch.Tensor       # int32 words, N * K * bits / 32
+    scales: torch.Tensor   # bf16 [N, K / group_size]
+    biases: torch.Tensor   # bf16 [N, K / group_size]
+    N: int
+    K: int
+    bits: int
+
+    def nbytes(self) -> int:
+        return self.wq.numel() * 4 + self.scales.numel() * 2 + self.biases.numel() * 2
+
+
+@dataclass
+class StackWeights:
+    layers: list = field(default_factory=list)   # per layer: dict name -> QPack
+    lm_head: QPack | None = None
+    k_cache: list = field(default_factory=list)  # per attention layer: bf16 [Hkv, T_cap, D]
+    v_cache: list = field(default_factory=list)
+
+    def weight_bytes(self) -> int:
+        return sum(p.nbytes() for lay in self.layers for p in lay.values()) + self.lm_head.nbytes()
+
+
+class DenseVerifyStack:
+    """Preallocated buffers and workspaces for one verify step (M rows)."""
+
+    def __init__(self, cfg: StackConfig, weights: StackWeights, device="cuda"):
+        self.cfg = cfg
+        self.w = weights
+        dev = torch.device(device)
+        M = cfg.M
+        bf = torch.bfloat16
+        self.h = torch.empty((M, cfg.hidden), dtype=bf, device=dev)
+        self.a = torch.empty((M, cfg.hidden), dtype=bf, device=dev)
+        self.qkv = torch.empty((M, cfg.qkv_width), dtype=bf, device=dev)
+        self.ctx_out = torch.empty((M, cfg.q_width), dtype=bf, device=dev)
+        self.proj = torch.empty((M, cfg.hidden), dtype=bf, device=dev)
+        self.gu = torch.empty((M, 2 * cfg.inter), dtype=bf, device=dev)
+        self.act = torch.empty((M, cfg.inter), dtype=bf, device=dev)
+        self.logits = torch.empty((1, M, cfg.vocab), dtype=torch.float32, device=dev)
+        self.probs = torch.empty((1, 2 * M - 1, cfg.vocab), dtype=torch.float32, device=dev)
+        self.tokens = torch.empty((1, M), dtype=torch.int32, device=dev)
+        self.n_acc = torch.empty((1,), dtype=torch.int32, device=dev)
+        sh = cfg.shapes()
+        qmm_ws = max(vq.qmm_workspace_bytes(b, M, N, K)
+                     for name, (N, K) in sh.items()
+                     for b in ([cfg.lm_bits] if name == "lm_head" else [cfg.bits]))
+        T = cfg.ctx + M
+        attn_ws = vq.attn_workspace_bytes(M, cfg.Hq, cfg.Hkv, cfg.D, T)
+        acc_ws = vq.accept_workspace_bytes(1, M - 1, cfg.vocab, vq.VQ_LOGITS, M * cfg.vocab, (M - 1) * cfg.vocab)
+        z = lambda n: torch.zeros(n + 256, dtype=torch.uint8, device=dev) if n else None
+        self._ws = {"qmm": z(qmm_ws), "attn": z(attn_ws), "accept": z(acc_ws)}
+
+    def _wsv(self, kind):
+        buf = self._ws[kind]
+        if buf is None:
+            return None
+        off = (-buf.data_ptr()) % 256
+        return buf[off:]
+
+    def _qmm(self, x, pack: QPack, out):
+        vq.skinny_qmm(x, pack.wq, pack.scales, pack.biases, pack.bits, pack.N, pack.K, self.cfg.group_size,
+                      out=out, workspace=self._wsv("qmm"))
+
+    def forward_hidden(self, h_in: torch.Tensor) -> torch.Tensor:
+        """Runs the layers on h_in [M, hidden] (bf16); returns the final hidden rows."""
+        cfg = self.cfg
+        self.h.copy_(h_in)
+        ai = 0
+        for li, lay in enumerate(self.w.layers):
+            vq.rmsnorm(self.h, out=self.a)
+            self._qmm(self.a, lay["qkv"], self.qkv)
+            q = self.qkv[:, : cfg.q_width]
+            if cfg.is_attn(li):
+                kc, vc = self.w.k_cache[ai], self.w.v_cache[ai]
+                ai += 1
+                vq.kv_append(self.qkv, cfg.q_width, cfg.q_width + cfg.Hkv * cfg.D, kc, vc, cfg.ctx)
+                qv = q.view(cfg.M, cfg.Hq, cfg.D) if q.is_contiguous() else q.as_strided(
+                    (cfg.M, cfg.Hq, cfg.D), (self.qkv.stride(0), cfg.D, 1))
+                ov = self.ctx_out.view(cfg.M, cfg.Hq, cfg.D)
+                vq.multirow_attn(qv, kc, vc, cfg.ctx + cfg.M, cfg.D ** -0.5, out=ov, workspace=self._wsv("attn"))
+                c = self.ctx_out
+            else:
+                c = q
+            self._qmm(c, lay["o"], self.proj)
+            vq.add_(self.h, self.proj)
+            vq.rmsnorm(self.h, out=self.a)
+            self._qmm(self.a, lay["gate_up"], self.gu)
+            vq.silu_mul(self.gu, out=self.act)
+            self._qmm(self.act, lay["down"], self.proj)
+            vq.add_(self.h, self.proj)
+        return self.h
+
+    def step(self, h_in, draft_logits, drafts, uniforms):
+        """One verify step: layers, lm_head, exact acceptance.
+
+        h_in bf16 [M, hidden]; draft_logits float32 [1, K, V]; drafts int32 [1, K];
+        uniforms float32 [1, K+1]. Returns (tokens int32 [1, K+1], n_accepted int32 [1]).
+        """
+        cfg = self.cfg
+        self.forward_hidden(h_in)
+        vq.rmsnorm(self.h, out=self.a)
+        self._qmm(self.a, self.w.lm_head, self.logits[0])
+        vq.spec_accept(self.logits, draft_logits, drafts, uniforms, logits=True, temperature=cfg.temperature,
+                       top_k=cfg.top_k, top_p=cfg.top_p, probs_out=self.probs, out_tokens=self.tokens,
+                       out_n=self.n_acc, workspace=self._wsv("accept"))
+        return self.tokens, self.n_acc
+
+    def bytes_per_step(self) -> dict:
+        """Algorithmic HBM bytes of one step: weights once, KV (K and V) once per
+        attention layer, and the logits/probability rows of the acceptance step."""
+        cfg = self.cfg
+        T = cfg.ctx + cfg.M
+        kv = cfg.n_attn * 4 * cfg.Hkv * T * cfg.D
+        acc = (2 * cfg.M - 1) * cfg.vocab * 4
+        return {"weights": self.w.weight_bytes(), "kv": kv, "accept_rows": acc,
+                "total": self.w.weight_bytes() + kv + acc}

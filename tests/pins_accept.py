@@ -159,12 +159,9 @@ PINS = [pin_truncation_golden, pin_accept_golden, pin_dyadic_exact, pin_special_
 
 
 # ------------------------------------------------------------ distribution check
-def chisquare_trials(mod, config, K, V, T, top_k, top_p, n_trials, seed=0, alpha=1e-3,
-                     corr=None, min_reach=2000):
-    """10**6-trial chi-square of the emitted tokens against p~ per position (for every
-    position that at least ``min_reach`` trials reach), plus the acceptance rate at
-    position 0 against sum_x min(p~_0, q~_0) (within 4 sigma). ``corr`` = noise std of
-    draft logits correlated with the target's (None: independent logits)."""
+def make_trials(mod, config, K, V, T, top_k, top_p, n_trials, seed=0, corr=None):
+    """Shared rows (oracle float32 probabilities of synthetic logits), drafts drawn
+    from q~ per position, and the acceptance uniforms of ``n_trials`` verifies."""
     if corr is None:
         pl, ql = accept_logits(config, K, V, seed=seed)
     else:
@@ -179,7 +176,16 @@ def chisquare_trials(mod, config, K, V, T, top_k, top_p, n_trials, seed=0, alpha
     for i in range(K):
         kept, Z = sr.rowsQ[i]
         drafts[:, i] = np.searchsorted(mod.cdf_edges(kept, Z), mu_d[:, i], side="right")
-    toks, n = sr.run(drafts, u_a)
+    return dict(P=P, Q=Q, logits=(pl, ql), sr=sr, drafts=drafts, uniforms=u_a)
+
+
+def check_distribution(sr, toks, n, K, V, alpha=1e-3, min_reach=2000):
+    """Chi-square of the emitted tokens against p~ per position (positions reached by
+    at least ``min_reach`` trials) and the position-0 acceptance rate against
+    sum_x min(p~_0, q~_0) within 4 sigma. Returns the p-values by position."""
+    toks = np.asarray(toks, dtype=np.int64)
+    n = np.asarray(n, dtype=np.int64)
+    n_trials = n.size
     assert np.all(n >= 0)
     pvals = {}
     for i in range(K + 1):
@@ -198,11 +204,20 @@ def chisquare_trials(mod, config, K, V, T, top_k, top_p, n_trials, seed=0, alpha
         o, e = o[keep], e[keep]
         e *= o.sum() / e.sum()
         pvals[i] = float(stats.chisquare(o, e).pvalue)
-    kP, ZP = sr.rowsP[0]
-    kQ, ZQ = sr.rowsQ[0]
-    rate = sum(min(Fraction(int(a), ZP), Fraction(int(b), ZQ)) for a, b in zip(kP, kQ) if a and b)
-    obs_rate = float((n >= 1).mean())
-    sigma = np.sqrt(float(rate) * (1 - float(rate)) / n_trials)
-    assert abs(obs_rate - float(rate)) <= 4 * sigma + 1e-12, (obs_rate, float(rate))
+    if K > 0:
+        kP, ZP = sr.rowsP[0]
+        kQ, ZQ = sr.rowsQ[0]
+        rate = sum(min(Fraction(int(a), ZP), Fraction(int(b), ZQ)) for a, b in zip(kP, kQ) if a and b)
+        obs_rate = float((n >= 1).mean())
+        sigma = np.sqrt(float(rate) * (1 - float(rate)) / n_trials)
+        assert abs(obs_rate - float(rate)) <= 4 * sigma + 1e-12, (obs_rate, float(rate))
     assert 0 in pvals and all(pv > alpha for pv in pvals.values()), pvals
-    return pvals, obs_rate, float(rate)
+    return pvals
+
+
+def chisquare_trials(mod, config, K, V, T, top_k, top_p, n_trials, seed=0, alpha=1e-3,
+                     corr=None, min_reach=2000):
+    """10**6-trial distribution check of the oracle itself (see ``check_distribution``)."""
+    tr = make_trials(mod, config, K, V, T, top_k, top_p, n_trials, seed, corr)
+    toks, n = tr["sr"].run(tr["drafts"], tr["uniforms"])
+    return check_distribution(tr["sr"], toks, n, K, V, alpha, min_reach), None, None

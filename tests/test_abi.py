@@ -1,0 +1,113 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, and
+rejects invalid arguments on the host before any HIP call."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def vqmod():
+    from speculative_decoding_verify_vq_amd import vq
+    return vq
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(vq_\w+)\s*\(", src))
+    return sorted(names)
+
+
+def test_every_declared_symbol_exported(vqmod):
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(vqmod.lib, n), n
+
+
+def test_status_strings(vqmod):
+    assert vqmod.status_string(0) == "ok"
+    assert vqmod.status_string(1) == "invalid argument"
+    assert vqmod.version() == "0.1.0"
+
+
+A16 = 1 << 20  # a fake, 256-byte-aligned "device address": never dereferenced (validation fails first)
+
+
+def _qmm(vq, **kw):
+    a = dict(x=A16, ldx=1024, wq=A16, s=A16, b=A16, bits=4, gs=64, M=4, N=512, K=1024, y=A16, ldy=512,
+             yd=0, ws=A16, wsz=1 << 30, stream=None)
+    a.update(kw)
+    return vq.lib.vq_skinny_qmm(a["x"], a["ldx"], a["wq"], a["s"], a["b"], a["bits"], a["gs"], a["M"], a["N"],
+                                a["K"], a["y"], a["ldy"], a["yd"], a["ws"], a["wsz"], a["stream"])
+
+
+@pytest.mark.parametrize("bad", [
+    dict(x=None), dict(wq=None), dict(y=None), dict(bits=3), dict(bits=16), dict(gs=32), dict(M=0), dict(M=17),
+    dict(N=0), dict(K=96), dict(K=0), dict(ldx=1000), dict(ldx=1028), dict(ldy=100), dict(yd=7),
+    dict(x=A16 + 8), dict(wq=A16 + 4), dict(y=A16 + 1), dict(ws=None, N=64, K=8192), dict(wsz=16, N=64, K=8192),
+    dict(ws=A16 + 64, N=64, K=8192),
+])
+def test_qmm_rejects(vqmod, bad):
+    assert _qmm(vqmod, **bad) == vqmod.VQ_ERR_INVALID_ARG
+    assert vqmod.last_error()
+
+
+def _attn(vq, **kw):
+    a = dict(q=A16, qrs=128, k=A16, v=A16, hs=256 * 64, M=4, Hq=2, Hkv=2, D=64, T=256, scale=0.125, out=A16,
+             ors=128, ws=A16, wsz=1 << 30)
+    a.update(kw)
+    return vq.lib.vq_multirow_attn(a["q"], a["qrs"], a["k"], a["v"], a["hs"], a["M"], a["Hq"], a["Hkv"], a["D"],
+                                   a["T"], a["scale"], a["out"], a["ors"], a["ws"], a["wsz"], None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(q=None), dict(out=None), dict(M=0), dict(M=17), dict(Hq=3), dict(Hkv=0), dict(D=96), dict(T=3),
+    dict(hs=256 * 64 - 8), dict(hs=256 * 64 + 4), dict(scale=float("inf")), dict(scale=float("nan")),
+    dict(q=A16 + 2), dict(Hq=48, Hkv=1, M=4), dict(T=100000, ws=None), dict(qrs=120), dict(qrs=132),
+    dict(ors=64),
+])
+def test_attn_rejects(vqmod, bad):
+    assert _attn(vqmod, **bad) == vqmod.VQ_ERR_INVALID_ARG
+
+
+def _acc(vq, **kw):
+    a = dict(p=A16, q=A16, kind=0, ps=0, qs=0, d=A16, u=A16, B=4, K=3, V=1000, T=1.0, tk=0, tp=1.0, ot=A16,
+             on=A16, po=None, ws=A16, wsz=1 << 30)
+    a.update(kw)
+    return vq.lib.vq_spec_accept(a["p"], a["q"], a["kind"], a["ps"], a["qs"], a["d"], a["u"], a["B"], a["K"],
+                                 a["V"], a["T"], a["tk"], a["tp"], a["ot"], a["on"], a["po"], a["ws"], a["wsz"], None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(p=None), dict(u=None), dict(ot=None), dict(on=None), dict(q=None), dict(d=None), dict(B=0), dict(K=-1),
+    dict(K=16), dict(V=1), dict(V=(1 << 20) + 1), dict(kind=2), dict(tk=-1), dict(tp=0.0), dict(tp=1.5),
+    dict(tp=float("nan")), dict(kind=1, T=0.0), dict(kind=1, T=float("inf")), dict(ps=3999), dict(qs=10),
+    dict(ps=-1), dict(ps=4000, qs=3000, B=70000), dict(p=A16 + 2), dict(ws=None),
+])
+def test_accept_rejects(vqmod, bad):
+    assert _acc(vqmod, **bad) == vqmod.VQ_ERR_INVALID_ARG
+
+
+def test_valid_call_without_gpu_is_a_clean_error(vqmod):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc = _qmm(vqmod)
+    assert rc in (vqmod.VQ_ERR_HIP, vqmod.VQ_ERR_UNSUPPORTED_DEVICE) and vqmod.last_error()
+
+
+def test_workspace_queries_are_pure(vqmod):
+    vq = vqmod
+    assert vq.qmm_workspace_bytes(4, 4, 8192, 5120) == vq.qmm_workspace_bytes(4, 4, 8192, 5120) > 0
+    assert vq.qmm_workspace_bytes(4, 4, 8192, 96) == 0          # invalid shape -> 0
+    assert vq.attn_workspace_bytes(4, 2, 2, 64, 256) >= 0
+    assert vq.accept_workspace_bytes(1, 3, 1000, 0, 0, 0) > 0
+    assert vq.accept_workspace_bytes(1, 3, 1000, 1, 0, 0) > vq.accept_workspace_bytes(1, 3, 1000, 0, 0, 0)

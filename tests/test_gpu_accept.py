@@ -1,0 +1,139 @@
+"""GPU parity of vq_spec_accept: bit-exact decisions and tokens against the
+exact-integer oracle given the same float32 probabilities and uniforms, the
+10**6-trial distribution check on the GPU's own outputs, and the float32
+softmax of logits mode within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.accept as oacc
+from synth import accept_logits, accept_logits_correlated, uniforms24
+from tests import pins_accept
+from tests.gpu_util import f32_tensor, i32_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+def _entries(config, B, K, V, T, top_k, top_p, corr=None):
+    """B independent verifies: rows, drafts drawn from q~, uniforms (numpy)."""
+    P = np.empty((B, K + 1, V), np.float32)
+    Q = np.empty((B, K, V), np.float32)
+    D = np.empty((B, K), np.int64)
+    U = uniforms24(config, (B, K + 1), stream="accept-u", extra=7)
+    ud = uniforms24(config, (B, K), stream="draft-u", extra=7)
+    for b in range(B):
+        if corr is None:
+            pl, ql = accept_logits(config, K, V, extra=b)
+        else:
+            pl, ql = accept_logits_correlated(config, K, V, noise=corr, extra=b)
+        P[b], Q[b] = oacc.probs_f32(pl, T), oacc.probs_f32(ql, T)
+        for i in range(K):
+            D[b, i] = oacc.sample_truncated(Q[b, i], top_k, top_p, ud[b, i])
+    return P, Q, D, U
+
+
+def _gpu(vq, P, Q, D, U, **kw):
+    toks, n = vq.spec_accept(f32_tensor(P), f32_tensor(Q) if Q.size else None,
+                             i32_tensor(D) if D.size else None, f32_tensor(U), **kw)
+    torch.cuda.synchronize()
+    return toks.cpu().numpy().astype(np.int64), n.cpu().numpy().astype(np.int64)
+
+
+def _oracle(P, Q, D, U, top_k, top_p):
+    res = [oacc.spec_accept(P[b], Q[b], list(D[b]), U[b], top_k, top_p) for b in range(P.shape[0])]
+    return np.array([r[0] for r in res], np.int64), np.array([r[1] for r in res], np.int64)
+
+
+TRUNC = [(0, 1.0), (20, 0.95), (0, 0.95), (5, 1.0), (1, 1.0), (50, 0.5)]
+
+
+@pytest.mark.parametrize("top_k,top_p", TRUNC)
+@pytest.mark.parametrize("corr", [None, 0.5])
+def test_config0_entries_bit_exact(vq, top_k, top_p, corr):
+    P, Q, D, U = _entries(0, 48, 3, 1000, 1.0, top_k, top_p, corr)
+    got = _gpu(vq, P, Q, D, U, top_k=top_k, top_p=top_p)
+    ref = _oracle(P, Q, D, U, top_k, top_p)
+    assert np.array_equal(got[1], ref[1]) and np.array_equal(got[0], ref[0])
+
+
+@pytest.mark.parametrize("K,T,top_k,top_p", [(3, 0.7, 0, 0.95), (7, 1.0, 20, 0.95)])
+def test_full_vocab_entries_bit_exact(vq, K, T, top_k, top_p):
+    """Configs 3 and 4 sampler settings at V = 248320."""
+    P, Q, D, U = _entries(3 if K == 3 else 4, 3, K, 248320, T, top_k, top_p, corr=0.3)
+    got = _gpu(vq, P, Q, D, U, top_k=top_k, top_p=top_p)
+    ref = _oracle(P, Q, D, U, top_k, top_p)
+    assert np.array_equal(got[1], ref[1]) and np.array_equal(got[0], ref[0])
+
+
+def test_invalid_entries_and_edges(vq):
+    K, V = 3, 1000
+    P, Q, D, U = _entries(0, 8, K, V, 1.0, 0, 1.0)
+    P[1, 2, 17] = np.nan
+    Q[2, 0, 3] = -1e-8
+    D[3, 1] = V
+    U[4, 3] = 1.0
+    P[5, 1, :] = 0.0
+    Q[6, 2, 9] = 1.5
+    got = _gpu(vq, P, Q, D, U)
+    ref = _oracle(P, Q, D, U, 0, 1.0)
+    assert np.array_equal(got[1], ref[1]) and np.array_equal(got[0], ref[0])
+    assert list(got[1][1:7]) == [-1] * 6 and got[1][0] >= 0 and got[1][7] >= 0
+
+
+def test_k0_plain_sampling(vq):
+    P, Q, D, U = _entries(0, 16, 0, 1000, 1.0, 0, 1.0)
+    got = _gpu(vq, P, Q, D, U, top_k=10, top_p=0.9)
+    ref = _oracle(P, Q, D, U, 10, 0.9)
+    assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+def test_tiny_vocab_and_hand_examples(vq):
+    import json, os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "accept_hand.json")) as f:
+        cases = json.load(f)["accept"]
+    for c in cases:
+        P = np.array([c["P"]], np.float32)
+        K = len(c["drafts"])
+        Q = np.array(c["Q"], np.float32).reshape(1, K, P.shape[2])
+        D = np.array([c["drafts"]], np.int64).reshape(1, K)
+        U = np.array([c["uniforms"]], np.float32)
+        toks, n = _gpu(vq, P, Q, D, U, top_k=c["top_k"], top_p=c["top_p"])
+        assert list(toks[0]) == c["tokens"] and int(n[0]) == c["n_accepted"], c["why"]
+
+
+@pytest.mark.parametrize("name,cfg", [
+    ("config0", dict(config=0, K=3, V=1000, T=1.0, top_k=0, top_p=1.0)),
+    ("config0 correlated", dict(config=0, K=3, V=1000, T=1.0, top_k=0, top_p=1.0, corr=0.5)),
+    ("config4 V=248320 K=7 top-k 20 top-p 0.95", dict(config=4, K=7, V=248320, T=1.0, top_k=20, top_p=0.95, corr=0.3)),
+])
+def test_shared_rows_1e6_trials(vq, name, cfg):
+    """10**6 trials of one verify: GPU tokens bit-exact against the oracle and
+    distributed as p~ per position (chi-square)."""
+    tr = pins_accept.make_trials(oacc, n_trials=10**6, **cfg)
+    toks, n = vq.spec_accept(f32_tensor(tr["P"]), f32_tensor(tr["Q"]), i32_tensor(tr["drafts"]),
+                             f32_tensor(tr["uniforms"]), top_k=cfg["top_k"], top_p=cfg["top_p"])
+    torch.cuda.synchronize()
+    toks, n = toks.cpu().numpy().astype(np.int64), n.cpu().numpy().astype(np.int64)
+    rt, rn = tr["sr"].run(tr["drafts"], tr["uniforms"])
+    assert np.array_equal(n, rn) and np.array_equal(toks, rt)
+    pins_accept.check_distribution(tr["sr"], toks, n, cfg["K"], cfg["V"])
+
+
+@pytest.mark.parametrize("V,T,top_k,top_p", [(1000, 1.0, 0, 1.0), (248320, 0.7, 0, 0.95), (248320, 1.0, 20, 0.95)])
+def test_logits_mode(vq, V, T, top_k, top_p):
+    """float32 softmax against the float64 oracle; tokens valid and, over 10**6
+    shared-row trials, distributed as the oracle's p~."""
+    K = 3
+    tr = pins_accept.make_trials(oacc, config=3, K=K, V=V, T=T, top_k=top_k, top_p=top_p, n_trials=10**6, corr=0.3)
+    pl, ql = tr["logits"]
+    probs = torch.empty((1, 2 * K + 1, V), dtype=torch.float32, device="cuda")
+    toks, n = vq.spec_accept(f32_tensor(pl), f32_tensor(ql), i32_tensor(tr["drafts"]), f32_tensor(tr["uniforms"]),
+                             logits=True, temperature=T, top_k=top_k, top_p=top_p, probs_out=probs)
+    torch.cuda.synchronize()
+    ref = np.concatenate([oacc.softmax_f64(pl, T), oacc.softmax_f64(ql, T)])
+    got = probs[0].cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    assert err.max() <= 1e-2 * ref.max() + 1e-3
+    assert np.all(err <= 1e-4 * ref + 1e-12), float((err / (ref + 1e-30)).max())
+    toks, n = toks.cpu().numpy().astype(np.int64), n.cpu().numpy().astype(np.int64)
+    pins_accept.check_distribution(tr["sr"], toks, n, K, V)

@@ -1,0 +1,59 @@
+"""GPU parity of vq_multirow_attn against the float64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.attn as oa
+from synth import attn_inputs
+from tests.gpu_util import assert_close, bf16_tensor, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(vq, q, k, v, T, scale):
+    out = vq.multirow_attn(bf16_tensor(q), bf16_tensor(k), bf16_tensor(v), T, scale)
+    torch.cuda.synchronize()
+    return to_f64(out)
+
+
+@pytest.mark.parametrize("M,Hq,Hkv,D,T,T_cap", [
+    (4, 2, 2, 64, 256, 256),       # config 0
+    (5, 12, 2, 64, 256, 260),      # GQA 6:1, T_cap > T
+    (1, 8, 8, 128, 100, 128),      # single row, ragged T
+    (3, 8, 2, 128, 67, 70),        # T not a multiple of the tile
+    (2, 24, 4, 256, 40, 40),       # config-2 heads, short context
+    (6, 24, 4, 256, 300, 320),     # 36 rows per KV head: two row tiles
+    (16, 24, 4, 256, 90, 96),      # 96 rows: three row tiles
+    (16, 8, 1, 256, 130, 130),     # 128 rows: four row tiles
+    (16, 16, 2, 128, 16, 16),      # T == M: every row sees a different prefix
+    (7, 4, 4, 64, 5000, 5000),     # many key ranges -> combine kernel
+])
+def test_shapes_full(vq, M, Hq, Hkv, D, T, T_cap):
+    q, k, v = attn_inputs(0 if (M, T) == (4, 256) else 20, M, Hq, Hkv, D, T_cap, extra=T)
+    scale = 1 / math.sqrt(D)
+    ref = oa.multirow_attention(q, k, v, M, Hq, Hkv, D, T, T_cap, scale)
+    assert_close(_run(vq, q, k, v, T, scale), ref, f"M={M} Hq={Hq} Hkv={Hkv} D={D} T={T}")
+
+
+@pytest.mark.parametrize("ctx", [8192, 32768])
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 6, 7, 8])
+def test_config2_sampled(vq, ctx, M):
+    """Config 2: Hq=24, Hkv=4, D=256, KV at ctx committed positions + M drafted rows."""
+    Hq, Hkv, D = 24, 4, 256
+    T = ctx + M
+    q, k, v = attn_inputs(2, M, Hq, Hkv, D, T, extra=ctx)
+    out = _run(vq, q, k, v, T, 1 / 16)
+    rng = np.random.default_rng(ctx + M)
+    pairs = [(m, int(h)) for m in range(M) for h in rng.choice(Hq, 3, replace=False)]
+    ref = oa.multirow_attention(q, k, v, M, Hq, Hkv, D, T, T, 1 / 16, pairs=pairs)
+    got = np.stack([out[m, h] for m, h in pairs])
+    assert_close(got, ref, f"ctx={ctx} M={M}")
+
+
+def test_deterministic(vq):
+    q, k, v = attn_inputs(21, 8, 24, 4, 256, 8200)
+    a = _run(vq, q, k, v, 8200, 1 / 16)
+    for _ in range(2):
+        assert np.array_equal(a, _run(vq, q, k, v, 8200, 1 / 16))
