@@ -25,10 +25,10 @@
 //     scale and bias are applied in float32:
 //         acc += s * D_g + (b - 128 s) * sum_{k in g} x     (4-bit)
 //         acc += s * D_g +  b         * sum_{k in g} x     (8-bit)
-//   * Parallelism beyond N/32 tiles comes from splitting K across workgroups;
-//     float32 partials go to the workspace and the last workgroup of a column
-//     block (integer completion counter) adds them in split order, so results
-//     are bit-identical run to run.
+//   * Parallelism beyond N/128 workgroups comes from splitting K across
+//     workgroups; float32 partials go to the workspace and the last workgroup of
+//     a column block (integer completion counter) adds them in split order, so
+//     results are bit-identical run to run.
 #include "vq_internal.h"
 
 namespace vq {
@@ -42,10 +42,24 @@ constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kTileN = 32;                // columns per wave
 constexpr int kColsWG = kWaves * kTileN;  // columns per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kChunkGroups = 16;          // groups of x staged in LDS at a time
-constexpr int kRowUnits = kChunkGroups * 8 + 1;  // 16-byte units per LDS row (+1 pad)
-constexpr size_t kCounterBytes = 4096;           // completion counters (split-K only)
-static_assert(2 * kNumCU * sizeof(int) <= kCounterBytes, "counter region too small");
+constexpr size_t kCounterBytes = 16384;   // completion counters (split-K only)
+constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(int));
+
+// Groups of x staged in LDS per chunk: 32 for up to 8 rows (32 KiB), 16 for 16 rows.
+template <int MT>
+struct ChunkCfg {
+  static constexpr int CG = MT <= 8 ? 32 : 16;
+  static constexpr int UNITS = CG * 8 + 1;  // 16-byte units per LDS row (+1 pad)
+};
+
+// Groups per pipeline block: 8 for 4-bit (one 16-byte load per lane per group),
+// 4 for 8-bit (two loads per group) -> 8 KiB of codes per wave in flight.
+template <int BITS>
+struct BlockCfg {
+  static constexpr int GB = BITS == 4 ? 8 : 4;
+  static constexpr int LPG = BITS / 4;  // 16-byte code loads per lane per group
+  static constexpr int NW = GB * LPG;   // code loads per block
+};
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -84,122 +98,167 @@ __device__ __forceinline__ bf16x8 unpack8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(bf16x8, t);
 }
 
-template <int BITS, int MT>
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// One pipeline block: the codes of GB groups of this lane's column, and their
+// scales and biases (bf16 bit patterns, GB of each).
+template <int BITS>
+struct Block {
+  uint4 w[BlockCfg<BITS>::NW];
+  uint32_t s[BlockCfg<BITS>::GB / 2];
+  uint32_t b[BlockCfg<BITS>::GB / 2];
+};
+
+template <int BITS, int MT, bool VEC>
 __global__ __launch_bounds__(kThreads) void qmm_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, int M, int N, int K,
     int splits, int groups_per_split, void* __restrict__ y, int64_t ldy, int y_f32,
     float* __restrict__ partial, int* __restrict__ counters) {
-  constexpr int kLoads = BITS / 4;  // 16-byte loads per lane per group
-  constexpr int PF = 4;             // groups prefetched ahead
-  constexpr int kUseful = MT / 2;   // accumulator registers that hold rows < MT
+  using BC = BlockCfg<BITS>;
+  using CC = ChunkCfg<MT>;
+  constexpr int GB = BC::GB;
+  constexpr int kUseful = MT / 2;  // accumulator registers that hold rows < MT
 
-  __shared__ uint4 xl[MT * kRowUnits];
-  __shared__ float xsum[kChunkGroups][16];
+  __shared__ uint4 xl[MT * CC::UNITS];
+  __shared__ float xsum[CC::CG][16];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int half = lane >> 5;  // which half of the group's K range this lane loads
+  const int half = lane >> 5;  // which half of each group's K range this lane loads
   const int cb = blockIdx.x;
   const int split = blockIdx.y;
   const int G = K >> 6;
   const int g0 = split * groups_per_split;
   const int g1 = min(G, g0 + groups_per_split);
+  const int nblk = (g1 - g0 + GB - 1) / GB;
 
   const int n = cb * kColsWG + wave * kTileN + (lane & 31);
   const bool n_ok = n < N;
   const int nc = n_ok ? n : N - 1;  // clamped row for loads; results discarded
-  const uint8_t* wrow = wq + (size_t)nc * (size_t)(K * BITS / 8);
+  const uint8_t* wrow = wq + (size_t)nc * (size_t)(K * BITS / 8) + half * 16;
   const uint16_t* srow = scales + (size_t)nc * G;
   const uint16_t* brow = biases + (size_t)nc * G;
-  const int arow = lane & 31;  // A-operand row (x row) of this lane
+  const int arow = (lane & 31) & (MT - 1);  // A-operand row; rows >= MT are never read back
+
+  // Loads for block bi (clamped to the last block, so every load is in bounds
+  // and issued unconditionally).
+  auto load_block = [&](Block<BITS>& B, int bi) {
+    const int gs = g0 + min(bi, nblk - 1) * GB;
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      const int g = min(gs + j, g1 - 1);
+#pragma unroll
+      for (int h = 0; h < BC::LPG; ++h)
+        B.w[j * BC::LPG + h] = *reinterpret_cast<const uint4*>(wrow + (size_t)g * (8 * BITS) + h * 32);
+    }
+    if constexpr (VEC) {
+      // gs is a multiple of GB and G % GB == 0, so the GB entries stay inside the row.
+      if constexpr (GB == 8) {
+        const uint4 sv = *reinterpret_cast<const uint4*>(srow + gs);
+        const uint4 bv = *reinterpret_cast<const uint4*>(brow + gs);
+        B.s[0] = sv.x; B.s[1] = sv.y; B.s[2] = sv.z; B.s[3] = sv.w;
+        B.b[0] = bv.x; B.b[1] = bv.y; B.b[2] = bv.z; B.b[3] = bv.w;
+      } else {
+        const uint2 sv = *reinterpret_cast<const uint2*>(srow + gs);
+        const uint2 bv = *reinterpret_cast<const uint2*>(brow + gs);
+        B.s[0] = sv.x; B.s[1] = sv.y;
+        B.b[0] = bv.x; B.b[1] = bv.y;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < GB / 2; ++j) {
+        const int ga = min(gs + 2 * j, g1 - 1), gb2 = min(gs + 2 * j + 1, g1 - 1);
+        B.s[j] = (uint32_t)srow[ga] | ((uint32_t)srow[gb2] << 16);
+        B.b[j] = (uint32_t)brow[ga] | ((uint32_t)brow[gb2] << 16);
+      }
+    }
+  };
+
+  // Stage x[:, groups gc .. gc+CG) into LDS (element order of the unpack) and the
+  // group sums. All loads of a thread are issued before any is consumed.
+  auto stage = [&](int gc) {
+    constexpr int kIters = MT * CC::CG * 8 / kThreads;
+    static_assert(kIters * kThreads == MT * CC::CG * 8, "staging loop must be uniform");
+    uint4 v[kIters];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int t = tid + it * kThreads;
+      const int m = t / (CC::CG * 8);
+      const int c = t % (CC::CG * 8);
+      const int gg = gc + (c >> 3);
+      v[it] = make_uint4(0, 0, 0, 0);
+      if (m < M && gg < g1)
+        v[it] = *reinterpret_cast<const uint4*>(x + (size_t)m * ldx + (size_t)gg * 64 + (c & 7) * 8);
+    }
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int t = tid + it * kThreads;
+      const int m = t / (CC::CG * 8);
+      const int c = t % (CC::CG * 8);
+      uint4 w = v[it];
+      float s8 = bf16_bits_to_f32(w.x & 0xFFFFu) + bf16_bits_to_f32(w.x >> 16) +
+                 bf16_bits_to_f32(w.y & 0xFFFFu) + bf16_bits_to_f32(w.y >> 16) +
+                 bf16_bits_to_f32(w.z & 0xFFFFu) + bf16_bits_to_f32(w.z >> 16) +
+                 bf16_bits_to_f32(w.w & 0xFFFFu) + bf16_bits_to_f32(w.w >> 16);
+      s8 += __shfl_xor(s8, 1);
+      s8 += __shfl_xor(s8, 2);
+      s8 += __shfl_xor(s8, 4);
+      if ((c & 7) == 0) xsum[c >> 3][m] = s8;
+      if (BITS == 4) {
+        uint4 o;
+        o.x = __builtin_amdgcn_perm(w.z, w.x, 0x05040100u);
+        o.y = __builtin_amdgcn_perm(w.z, w.x, 0x07060302u);
+        o.z = __builtin_amdgcn_perm(w.w, w.y, 0x05040100u);
+        o.w = __builtin_amdgcn_perm(w.w, w.y, 0x07060302u);
+        w = o;
+      }
+      xl[m * CC::UNITS + c] = w;
+    }
+  };
 
   float acc[kUseful];
 #pragma unroll
   for (int r = 0; r < kUseful; ++r) acc[r] = 0.f;
 
-  uint4 wb[PF][kLoads];
-  uint32_t sb[PF];
-  auto issue = [&](int slot, int g) {
-    if (g < g1) {
-#pragma unroll
-      for (int h = 0; h < kLoads; ++h)
-        wb[slot][h] = *reinterpret_cast<const uint4*>(wrow + (size_t)g * (8 * BITS) + h * 32 + half * 16);
-      sb[slot] = (uint32_t)srow[g] | ((uint32_t)brow[g] << 16);
-    }
-  };
-#pragma unroll
-  for (int p = 0; p < PF; ++p) issue(p, g0 + p);
-
   int chunk0 = g0;
-  for (int gb = g0; gb < g1; gb += PF) {
+  auto compute_block = [&](const Block<BITS>& B, int bi) {
+    const int gs = g0 + bi * GB;
+    if (gs != g0 && (gs - g0) % CC::CG == 0) {  // next x chunk (only for long K ranges)
+      chunk0 = gs;
+      __syncthreads();
+      stage(chunk0);
+      __syncthreads();
+    }
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int g = gb + p;
+    for (int j = 0; j < GB; ++j) {
+      const int g = gs + j;
       if (g >= g1) break;
-      if (((g - g0) % kChunkGroups) == 0) {
-        // Stage x[:, chunk] into LDS, permuted for the unpack order, plus group sums.
-        chunk0 = g;
-        __syncthreads();
-        for (int t = tid; t < MT * kChunkGroups * 8; t += kThreads) {
-          const int m = t / (kChunkGroups * 8);
-          const int c = t % (kChunkGroups * 8);
-          const int gg = chunk0 + (c >> 3);
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (m < M && gg < g1)
-            v = *reinterpret_cast<const uint4*>(x + (size_t)m * ldx + (size_t)gg * 64 + (c & 7) * 8);
-          float s8 = bf16_bits_to_f32(v.x & 0xFFFFu) + bf16_bits_to_f32(v.x >> 16) +
-                     bf16_bits_to_f32(v.y & 0xFFFFu) + bf16_bits_to_f32(v.y >> 16) +
-                     bf16_bits_to_f32(v.z & 0xFFFFu) + bf16_bits_to_f32(v.z >> 16) +
-                     bf16_bits_to_f32(v.w & 0xFFFFu) + bf16_bits_to_f32(v.w >> 16);
-          s8 += __shfl_xor(s8, 1);
-          s8 += __shfl_xor(s8, 2);
-          s8 += __shfl_xor(s8, 4);
-          if ((c & 7) == 0) xsum[c >> 3][m] = s8;
-          if (BITS == 4) {
-            uint4 o;
-            o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-            o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-            o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-            o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
-            v = o;
-          }
-          xl[m * kRowUnits + c] = v;
-        }
-        __syncthreads();
-      }
-
-      const uint4 w0 = wb[p][0];
-      uint4 w1 = w0;
-      if (kLoads == 2) w1 = wb[p][kLoads - 1];
-      const uint32_t sbv = sb[p];
-      issue(p, g + PF);
-
       const int gl = g - chunk0;
+      bf16x8 a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int unit = (BITS == 4) ? gl * 8 + half * 4 + i : gl * 8 + (i >> 1) * 4 + half * 2 + (i & 1);
+        a[i] = __builtin_bit_cast(bf16x8, xl[arow * CC::UNITS + unit]);
+      }
       f32x16 d = {};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        bf16x8 b;
-        int unit;  // 16-byte unit of x matching this MFMA's K slice
+        bf16x8 bv;
         if (BITS == 4) {
-          const uint32_t wi = i == 0 ? w0.x : i == 1 ? w0.y : i == 2 ? w0.z : w0.w;
-          b = unpack4(wi);
-          unit = gl * 8 + half * 4 + i;
+          bv = unpack4(word_of(B.w[j], i));
         } else {
-          const uint4 wh = (i < 2) ? w0 : w1;
-          const uint32_t lo = (i & 1) ? wh.z : wh.x;
-          const uint32_t hi = (i & 1) ? wh.w : wh.y;
-          b = unpack8(lo, hi);
-          unit = gl * 8 + (i >> 1) * 4 + half * 2 + (i & 1);
+          const uint4& wh = B.w[j * 2 + (i >> 1)];
+          bv = (i & 1) ? unpack8(wh.z, wh.w) : unpack8(wh.x, wh.y);
         }
-        bf16x8 a = {};
-        if (arow < MT) a = __builtin_bit_cast(bf16x8, xl[arow * kRowUnits + unit]);
-        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bv, d, 0, 0, 0);
       }
-      const float s = bf16_bits_to_f32(sbv & 0xFFFFu);
-      const float bb = bf16_bits_to_f32(sbv >> 16);
+      const float s = bf16_bits_to_f32((B.s[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+      const float bb = bf16_bits_to_f32((B.b[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
       const float c = (BITS == 4) ? __builtin_fmaf(-128.f, s, bb) : bb;
 #pragma unroll
       for (int r = 0; r < kUseful; ++r) {
@@ -207,6 +266,18 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(
         acc[r] = __builtin_fmaf(s, d[r], __builtin_fmaf(c, xsum[gl][m], acc[r]));
       }
     }
+  };
+
+  Block<BITS> A, Bk;
+  load_block(A, 0);
+  stage(g0);
+  __syncthreads();
+  for (int bi = 0; bi < nblk; bi += 2) {
+    load_block(Bk, bi + 1);
+    compute_block(A, bi);
+    if (bi + 1 >= nblk) break;
+    load_block(A, bi + 2);
+    compute_block(Bk, bi + 1);
   }
 
   // ------------------------------------------------------------------ epilogue
@@ -226,29 +297,37 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(
     }
     return;
   }
+  // Split-K completion without cache-wide fences. The partial sums are written
+  // with agent-scope (L2 write-through) stores and read back with agent-scope
+  // loads, and the counter is an agent-scope atomic; "s_waitcnt vmcnt(0)" before
+  // the barrier makes every partial store of the workgroup complete before its
+  // counter increment is issued. No store or load of this exchange goes through
+  // a possibly stale cache line, so no L2 writeback or invalidation is needed
+  // (which would evict the weight lines other waves are still streaming).
   float* part = partial + (size_t)split * M * N;
   if (n_ok) {
 #pragma unroll
     for (int r = 0; r < kUseful; ++r) {
       const int m = 8 * (r >> 2) + 4 * half + (r & 3);
-      if (m < M) part[(size_t)m * N + n] = acc[r];
+      if (m < M) __hip_atomic_store(&part[(size_t)m * N + n], acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&counters[cb], 1) == splits - 1);
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(&counters[cb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   for (int t = tid; t < M * kColsWG; t += kThreads) {
     const int m = t / kColsWG;
     const int col = cb * kColsWG + t % kColsWG;
     if (col >= N) continue;
     float v = 0.f;
-    for (int sp = 0; sp < splits; ++sp) v += __builtin_nontemporal_load(&partial[((size_t)sp * M + m) * N + col]);
+    for (int sp = 0; sp < splits; ++sp)
+      v += __hip_atomic_load(&partial[((size_t)sp * M + m) * N + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     store(m, col, v);
   }
-  if (tid == 0) counters[cb] = 0;
+  if (tid == 0) __hip_atomic_store(&counters[cb], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -259,23 +338,24 @@ QmmPlan qmm_plan(int bits, int M, int N, int K) {
   p.cols_per_wg = kColsWG;
   p.n_blocks = (N + kColsWG - 1) / kColsWG;
   const int G = K / 64;
-  // Aim for about two resident workgroups per compute unit, with at least four
-  // groups of K per workgroup so that the prefetch pipeline fills.
+  const int GB = bits == 4 ? 8 : 4;
+  const int CG = p.mt <= 8 ? 32 : 16;
+  // Enough workgroups for about two per compute unit, and a K range per
+  // workgroup that fits one LDS chunk of x. Split boundaries fall on pipeline
+  // blocks (multiples of GB groups).
   int s = (2 * kNumCU + p.n_blocks - 1) / p.n_blocks;
+  const int s_lds = (G + CG - 1) / CG;
+  s = s < s_lds ? s_lds : s;
   s = s < 1 ? 1 : s;
-  int max_s = G / 4 > 0 ? G / 4 : 1;
-  s = s > max_s ? max_s : s;
-  s = s > 64 ? 64 : s;
-  const int gps = (G + s - 1) / s;
+  int gps = (G + s - 1) / s;
+  gps = (gps + GB / 2) / GB * GB;  // nearest multiple of GB
+  if (gps < GB) gps = GB;
+  if (gps > CG) gps = CG;
+  if (p.n_blocks > kMaxCounters) gps = G;  // too many column blocks to count: no split
   p.groups_per_split = gps;
   p.splits = (G + gps - 1) / gps;
-  // Split-K only happens when there are fewer than 2 * kNumCU column blocks, so
-  // the counters always fit a fixed 4 KiB region at the start of the workspace:
-  // calls of different shapes that share a workspace never see each other's
-  // partial sums in their counter slots.
   p.counter_bytes = p.splits > 1 ? kCounterBytes : 0;
   p.partial_bytes = p.splits > 1 ? align_up((size_t)p.splits * M * N * sizeof(float), 256) : 0;
-  (void)bits;
   return p;
 }
 
@@ -292,14 +372,22 @@ hipError_t qmm_launch(const QmmPlan& plan, const void* x, int64_t ldx, const voi
   auto* wp = reinterpret_cast<const uint8_t*>(wq);
   auto* sp = reinterpret_cast<const uint16_t*>(scales);
   auto* bp = reinterpret_cast<const uint16_t*>(biases);
-#define VQ_QMM_LAUNCH(B, MTV)                                                                     \
-  hipLaunchKernelGGL((qmm_kernel<B, MTV>), grid, block, 0, stream, xp, ldx, wp, sp, bp, M, N, K, \
+  const int G = K / 64;
+  const int GB = bits == 4 ? 8 : 4;
+  const size_t va = bits == 4 ? 16 : 8;
+  const bool vec = (G % GB == 0) && (plan.groups_per_split % GB == 0) &&
+                   (reinterpret_cast<uintptr_t>(scales) % va == 0) && (reinterpret_cast<uintptr_t>(biases) % va == 0);
+#define VQ_QMM_LAUNCH(B, MTV, V)                                                                     \
+  hipLaunchKernelGGL((qmm_kernel<B, MTV, V>), grid, block, 0, stream, xp, ldx, wp, sp, bp, M, N, K, \
                      plan.splits, plan.groups_per_split, y, ldy, y_f32, partial, counters)
+#define VQ_QMM_MT(B, V) \
+  if (plan.mt == 8) VQ_QMM_LAUNCH(B, 8, V); else VQ_QMM_LAUNCH(B, 16, V);
   if (bits == 4) {
-    if (plan.mt == 8) VQ_QMM_LAUNCH(4, 8); else VQ_QMM_LAUNCH(4, 16);
+    if (vec) { VQ_QMM_MT(4, true) } else { VQ_QMM_MT(4, false) }
   } else {
-    if (plan.mt == 8) VQ_QMM_LAUNCH(8, 8); else VQ_QMM_LAUNCH(8, 16);
+    if (vec) { VQ_QMM_MT(8, true) } else { VQ_QMM_MT(8, false) }
   }
+#undef VQ_QMM_MT
 #undef VQ_QMM_LAUNCH
   return hipGetLastError();
 }
