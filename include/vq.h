@@ -96,7 +96,7 @@ const char* vq_version(void);
  * scales,  bf16 [N, K / gs] row-major: one affine scale s and bias b per group of
  * biases   gs consecutive elements along K.
  * bits     4 or 8.  gs: 64 (the only group size built).
- * M        1 .. 16 rows.  N >= 1.  K: a positive multiple of 64.
+ * M        1 .. 16 rows.  1 <= N <= 2^20.  K: a positive multiple of 64.
  * y        M rows of N outputs, row stride ldy (elements, >= N); y_dtype is
  *          VQ_BF16 (round to nearest even) or VQ_F32.
  * Alignment: x, wq and each row start of x must be 16-byte aligned (ldx a

@@ -64,7 +64,7 @@ int check_workspace(void* ws, size_t have, size_t need) {
 
 bool qmm_shape_ok(int bits, int group_size, int M, int N, int K) {
   return (bits == 4 || bits == 8) && group_size == 64 && M >= 1 && M <= VQ_MAX_ROWS && N >= 1 && K >= 64 &&
-         K % 64 == 0 && N <= (1 << 26) && K <= (1 << 24);
+         K % 64 == 0 && N <= (1 << 20) && K <= (1 << 24);
 }
 
 bool attn_shape_ok(int M, int Hq, int Hkv, int D, int T) {
