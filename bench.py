@@ -106,45 +106,79 @@ def time_graph(torch, g, steps: int, warmup: int) -> float:
     return t0.elapsed_time(t1) / steps
 
 
-def qmm_roofline(torch, vq, stack, reps: int = 3):
-    """Average duration of the skinny-QMM launches of one step, each launch
-    bracketed by HIP events on the stream it runs on; algorithmic bytes per
-    launch from the packed codes, scales, biases, activations and outputs."""
-    from speculative_decoding_verify_vq_amd.stack import qmm_algorithmic_bytes as algorithmic_bytes
+def qmm_roofline(torch, stack, reps: int = 5) -> dict:
+    """Average duration of the skinny-QMM launches of the verify step.
+
+    The QMM launches of each projection kind (the 64 qkv, o, gate_up and down
+    launches of the step, and the lm_head launch repeated 16 times) are captured
+    into a graph of their own, with the step's buffers and launch configuration;
+    each graph is replayed `reps` times between two HIP events on the stream it
+    runs on. The per-kind durations are weighted by the step's launch counts.
+    Algorithmic bytes per launch: packed codes, scales, biases, activations and
+    outputs."""
+    from speculative_decoding_verify_vq_amd.stack import qmm_algorithmic_bytes
     cfg = stack.cfg
-    stream = torch.cuda.current_stream()
-    launches = []
-    for _ in range(reps):
-        for li, lay in enumerate(stack.w.layers):
-            for name, x, out in (("qkv", stack.a, stack.qkv), ("o", stack.qkv[:, : cfg.q_width], stack.proj),
-                                 ("gate_up", stack.a, stack.gu), ("down", stack.act, stack.proj)):
-                p = lay[name]
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                stack._qmm(x, p, out)
-                e1.record(stream)
-                launches.append((e0, e1, algorithmic_bytes(cfg.M, p.N, p.K, p.bits)))
-        p = stack.w.lm_head
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        stack._qmm(stack.a, p, stack.logits[0])
-        e1.record(stream)
-        launches.append((e0, e1, algorithmic_bytes(cfg.M, p.N, p.K, p.bits, out_bytes=4)))
-    torch.cuda.synchronize()
-    ms = [e0.elapsed_time(e1) for e0, e1, _ in launches]
-    nbytes = [b for _, _, b in launches]
-    avg_ms = float(np.mean(ms))
-    avg_bytes = float(np.mean(nbytes))
-    return {"avg_ms": avg_ms, "avg_bytes": avg_bytes, "launches": len(launches),
+    kinds = {"qkv": (stack.a, stack.qkv), "o": (stack.qkv[:, : cfg.q_width], stack.proj),
+             "gate_up": (stack.a, stack.gu), "down": (stack.act, stack.proj)}
+    jobs = {name: ([lay[name] for lay in stack.w.layers], x, out) for name, (x, out) in kinds.items()}
+    jobs["lm_head"] = ([stack.w.lm_head] * 16, stack.a, stack.logits[0])
+    counts = {name: len(stack.w.layers) for name in kinds}
+    counts["lm_head"] = 1
+    per_kind = {}
+    tot_ms = tot_bytes = 0.0
+    for name, (packs, x, out) in jobs.items():
+        g = capture(torch, lambda: [stack._qmm(x, p, out) for p in packs])
+        ms = time_graph(torch, g, reps, 1) / len(packs)
+        del g
+        out_bytes = 4 if out.dtype == torch.float32 else 2
+        nb = qmm_algorithmic_bytes(cfg.M, packs[0].N, packs[0].K, packs[0].bits, out_bytes=out_bytes)
+        per_kind[name] = {"us": round(ms * 1e3, 2), "GBs": round(nb / (ms * 1e-3) / 1e9, 1)}
+        tot_ms += counts[name] * ms
+        tot_bytes += counts[name] * nb
+    n = sum(counts.values())
+    avg_ms, avg_bytes = tot_ms / n, tot_bytes / n
+    return {"avg_ms": avg_ms, "avg_bytes": avg_bytes, "launches": n, "per_kind": per_kind,
             "achieved_GBs": avg_bytes / (avg_ms * 1e-3) / 1e9}
+
+
+def qmm_traffic(avg_bytes: float):
+    """HBM bytes per QMM launch from the committed counter summary, if it was taken
+    on the current kernel source (else None): FETCH_SIZE + WRITE_SIZE per dispatch,
+    each scaled by what the counter reads for a copy of known size."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "qmm_traffic.json")
+    src = os.path.join(ROOT, "speculative_decoding_verify_vq_amd", "csrc", "qmm.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("qmm_hip_sha256") != digest:
+        return None
+    return {"bytes_per_launch": rec["hbm_bytes_per_launch"],
+            "ratio_to_algorithmic": round(rec["hbm_bytes_per_launch"] / avg_bytes, 3),
+            "source": "profiles/qmm_traffic.json"}
+
+
+def copy_calibration(torch, nbytes: int = 1 << 30) -> None:
+    """A plain device copy of known size (reads and writes nbytes), launched for
+    hardware counters to be scaled against."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(cfg_id: int, cfg, step_bytes: float) -> dict:
     """The oracle timed on a bounded sample of the same workload on this host's cores:
-    one o projection (5120 x 6144) at the step's M, two attention rows at the step's
-    context, and one acceptance over the full vocabulary. Rate = algorithmic bytes of
-    the sample / CPU seconds, in GB/s (the step rate is extrapolated from the same
-    bytes-per-second)."""
+    one layer's four projections (qkv, o, gate_up, down) at the step's M, one attention layer (every row and query head) at the
+    step's context, and one acceptance over the full vocabulary. Rate = algorithmic
+    bytes of the sample / CPU seconds, in GB/s (the step time is extrapolated from
+    the same bytes-per-second)."""
     import oracle.accept as oacc
     import oracle.attn as oattn
     import oracle.qmm as oqmm
@@ -156,34 +190,42 @@ def cpu_baseline(cfg_id: int, cfg, step_bytes: float) -> dict:
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
     M = cfg.M
-    w = qmm_weights(1, 5120, 6144, cfg.bits)
-    x = qmm_activations(1, M, 6144)
-    t0 = time.perf_counter()
-    oqmm.skinny_qmm(x, w["wq"], w["scales"], w["biases"], cfg.bits, 64, M, 5120, 6144)
-    t_qmm = time.perf_counter() - t0
-    b_qmm = oqmm.algorithmic_bytes(M, 5120, 6144, cfg.bits)
+    parts, secs, nbytes = [], 0.0, 0
+    sh = cfg.shapes()
+    for li, name in enumerate(("qkv", "o", "gate_up", "down")):
+        N, K = sh[name]
+        w = qmm_weights(1, N, K, cfg.bits, layer=li)
+        x = qmm_activations(1, M, K, extra=li)
+        t0 = time.perf_counter()
+        oqmm.skinny_qmm(x, w["wq"], w["scales"], w["biases"], cfg.bits, 64, M, N, K)
+        dt = time.perf_counter() - t0
+        b = oqmm.algorithmic_bytes(M, N, K, cfg.bits)
+        del w
+        parts.append(f"{name} {N}x{K} ({dt:.2f} s)")
+        secs += dt
+        nbytes += b
     T = cfg.ctx + M
     q, k, v = attn_inputs(2, M, cfg.Hq, cfg.Hkv, cfg.D, T)
     t0 = time.perf_counter()
-    oattn.multirow_attention(q, k, v, M, cfg.Hq, cfg.Hkv, cfg.D, T, T, cfg.D ** -0.5, pairs=[(0, 0), (M - 1, 6)])
-    t_attn = time.perf_counter() - t0
-    b_attn = 2 * 2 * T * cfg.D * 2  # the K and V rows of one KV head read for the two rows
+    oattn.multirow_attention(q, k, v, M, cfg.Hq, cfg.Hkv, cfg.D, T, T, cfg.D ** -0.5)
+    dt = time.perf_counter() - t0
+    parts.append(f"attention {M} rows x {cfg.Hq} heads at T={T} ({dt:.2f} s)")
+    secs += dt
+    nbytes += 2 * cfg.Hkv * T * cfg.D * 2  # K and V of every KV head, once
     K = M - 1
     pl, ql = accept_logits(cfg_id, K, cfg.vocab)
     P, Q = oacc.probs_f32(pl, cfg.temperature), oacc.probs_f32(ql, cfg.temperature)
     us = uniforms24(cfg_id, (K + 1,))
     t0 = time.perf_counter()
     oacc.spec_accept(P, Q, [1, 2, 3, 4, 5, 6, 7][:K], us, cfg.top_k, cfg.top_p)
-    t_acc = time.perf_counter() - t0
-    b_acc = (2 * K + 1) * cfg.vocab * 4
-    secs = t_qmm + t_attn + t_acc
-    nbytes = b_qmm + b_attn + b_acc
+    dt = time.perf_counter() - t0
+    parts.append(f"one acceptance over V={cfg.vocab} ({dt:.2f} s)")
+    secs += dt
+    nbytes += (2 * K + 1) * cfg.vocab * 4
     rate = nbytes / secs / 1e9
     return {"value": round(rate, 4), "unit": "GB/s", "cores": cores, "blas_threads": blas_threads,
             "kind": "oracle",
-            "sample": f"o projection 5120x6144 {cfg.bits}-bit at M={M} ({t_qmm:.2f} s), 2 attention rows at "
-                      f"T={T} ({t_attn:.2f} s), one acceptance over V={cfg.vocab} ({t_acc:.2f} s); "
-                      f"{nbytes / 1e6:.1f} MB in {secs:.2f} s",
+            "sample": "; ".join(parts) + f"; {nbytes / 1e6:.1f} MB in {secs:.2f} s",
             "ms_per_step_extrapolated": round(step_bytes / (rate * 1e9) * 1e3, 1)}
 
 
@@ -196,6 +238,8 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ratio", action="store_true", help="skip the M=1 / M=8 weight-stream ratio")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device copy first (for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the verify step; runs on more than one GPU are not "
@@ -211,6 +255,8 @@ def main() -> int:
     cfg = StackConfig(layers=args.layers, bits=c["bits"], lm_bits=c["lm_bits"], M=c["M"], ctx=c["ctx"],
                       temperature=c["temperature"], top_k=c["top_k"], top_p=c["top_p"])
     T_cap = cfg.ctx + 16
+    if args.copy_calibration:
+        copy_calibration(torch)
     log(f"config {args.config}: generating weights and KV caches on the device")
     w = make_weights(cfg, torch, 1000 * args.config, T_cap)
     stack = DenseVerifyStack(cfg, w)
@@ -245,8 +291,9 @@ def main() -> int:
         ratio = res[8] / res[1]
         log(f"64-layer stack: M=1 {res[1]:.3f} ms, M=8 {res[8]:.3f} ms, ratio {ratio:.3f}")
 
-    roof = qmm_roofline(torch, vq, stack)
-    log(f"QMM per launch: {roof['avg_ms'] * 1e3:.1f} us, {roof['achieved_GBs']:.0f} GB/s")
+    roof = qmm_roofline(torch, stack)
+    log(f"QMM per launch: {roof['avg_ms'] * 1e3:.1f} us, {roof['achieved_GBs']:.0f} GB/s; {roof['per_kind']}")
+    traffic = qmm_traffic(roof["avg_bytes"])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -262,9 +309,14 @@ def main() -> int:
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "cost_ratio_m8_m1": None if ratio is None else round(ratio, 4),
         "roofline": {"bound": "hbm", "achieved": round(roof["achieved_GBs"], 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(roof["achieved_GBs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(roof["achieved_GBs"] / PEAK_HBM_GBS, 4),
+                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                     "traffic_detail": traffic,
                      "kernel": "qmm_kernel", "avg_launch_us": round(roof["avg_ms"] * 1e3, 2),
-                     "avg_algorithmic_bytes": int(roof["avg_bytes"]), "launches_timed": roof["launches"]},
+                     "avg_algorithmic_bytes": int(roof["avg_bytes"]), "launches_timed": roof["launches"],
+                     "per_kind": roof["per_kind"],
+                     "timing": "HIP events around replays of graphs holding the step's QMM launches, "
+                               "per projection kind, weighted by the step's launch counts"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

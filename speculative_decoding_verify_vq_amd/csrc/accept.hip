@@ -32,43 +32,67 @@ namespace vq {
 namespace {
 
 typedef unsigned __int128 u128;
+typedef unsigned long long u64;
 
-constexpr int kRowThreads = 512;
+constexpr int kRowThreads = 1024;
 constexpr int kEntryThreads = 1024;
-constexpr int kDigitBits = 11;
+constexpr int kUnroll = 8;          // independent loads in flight per thread per pass
+constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;
-constexpr int kKeyShiftTop = 44;  // digits at bit 44, 33, 22, 11, 0 cover the 50-bit key
 constexpr float kLog2e = 1.4426950408889634f;
+// Radix levels over the 50-bit order key: bits [49:38], [37:26], [25:14], [13:2], [1:0].
+__constant__ int kLevelShift[5] = {38, 26, 14, 2, 0};
+__constant__ int kLevelBits[5] = {12, 12, 12, 12, 2};
 
 struct RowMeta {
-  unsigned long long thresh;  // kept <=> order key >= thresh
-  unsigned long long z;       // kept mass
-  int status;                 // 0 = valid, 1 = invalid
+  u64 thresh;  // kept <=> order key >= thresh
+  u64 z;       // kept mass
+  int status;  // 0 = valid, 1 = invalid
   int pad[3];
 };
 
 __device__ __forceinline__ bool prob_ok(float v) { return v >= 0.f && v <= 1.f; }  // false for NaN
 
-__device__ __forceinline__ unsigned long long mass_of(float v) {
+__device__ __forceinline__ u64 mass_of(float v) {
   // floor(v * 2^40): exact in double for a float v in [0, 1].
-  return (unsigned long long)((double)v * 1099511627776.0);
+  return (u64)((double)v * 1099511627776.0);
 }
 
-__device__ __forceinline__ unsigned long long key_of(float v, int x, int V) {
+__device__ __forceinline__ u64 key_of(float v, int x, int V) {
   const uint32_t b = (v == 0.f) ? 0u : __float_as_uint(v);
-  return ((unsigned long long)b << 20) | (unsigned long long)(V - 1 - x);
+  return ((u64)b << 20) | (u64)(V - 1 - x);
+}
+
+// Apply f(x, v) to every element of a row; thread t takes x = t + i*blockDim
+// (coalesced), kUnroll loads issued before any is used.
+template <typename F>
+__device__ __forceinline__ void for_row(const float* __restrict__ row, int V, F&& f) {
+  const int nt = blockDim.x;
+  for (int base = threadIdx.x; base < V; base += nt * kUnroll) {
+    float v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int x = base + u * nt;
+      v[u] = x < V ? row[x] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int x = base + u * nt;
+      if (x < V) f(x, v[u]);
+    }
+  }
 }
 
 // --------------------------------------------------------------- block scans
-__device__ __forceinline__ unsigned long long shfl_up_u64(unsigned long long v, int off) {
+__device__ __forceinline__ u64 shfl_up_u64(u64 v, int off) {
   const uint32_t lo = __shfl_up((uint32_t)v, off);
   const uint32_t hi = __shfl_up((uint32_t)(v >> 32), off);
-  return ((unsigned long long)hi << 32) | lo;
+  return ((u64)hi << 32) | lo;
 }
 
 __device__ __forceinline__ u128 shfl_up_u128(u128 v, int off) {
-  const unsigned long long lo = shfl_up_u64((unsigned long long)v, off);
-  const unsigned long long hi = shfl_up_u64((unsigned long long)(v >> 64), off);
+  const u64 lo = shfl_up_u64((u64)v, off);
+  const u64 hi = shfl_up_u64((u64)(v >> 64), off);
   return ((u128)hi << 64) | lo;
 }
 
@@ -124,80 +148,124 @@ __device__ float block_reduce_sum(float v, float* lds) {
 
 // ------------------------------------------------------------- radix select
 struct SelectLds {
-  unsigned long long hist[kBins];
-  unsigned long long scan[kRowThreads / 64 + 1];
-  unsigned long long res_key, res_above, res_total;
+  u64 mass[kBins];
+  uint32_t cnt[kBins];
+  u64 scan[kRowThreads / 64 + 1];
+  u64 res_key, res_above, res_total;
+  uint32_t res_cnt;
   int flag;
 };
 
 // Walking the row in order (key descending) among elements with key >= lo,
-// find the first element at which the running weight reaches `thr` (weight = 1
-// or the mass). For the mass walk, thr is derived from the first pass's total:
-// thr = ceil(tp * total / 2^24). Returns that element's key, the weight of the
-// elements before it, and the total weight of the elements with key >= lo.
-__device__ void radix_select(const float* row, int V, unsigned long long lo, bool by_mass, uint32_t tp,
-                             unsigned long long thr_count, SelectLds& s, unsigned long long& out_key,
-                             unsigned long long& out_above, unsigned long long& out_total) {
+// find the first element at which the running weight reaches `thr` (weight 1 for
+// count, the mass for by_mass). For the mass walk thr is derived from the
+// first level's total: thr = ceil(tp * total / 2^24). Returns the element's
+// key and mass, the weight before it and the total weight of the elements with
+// key >= lo. The walk ends at the first level whose crossing bin holds a single
+// element; one more pass then reads that element.
+__device__ void radix_select(const float* __restrict__ row, int V, u64 lo, bool by_mass, uint32_t tp,
+                             u64 thr_count, SelectLds& s, u64& out_key, u64& out_mass, u64& out_above,
+                             u64& out_total) {
   const int tid = threadIdx.x;
-  unsigned long long prefix = 0, above = 0, thr = thr_count, total = 0;
-  for (int shift = kKeyShiftTop; shift >= 0; shift -= kDigitBits) {
-    for (int b = tid; b < kBins; b += kRowThreads) s.hist[b] = 0;
-    __syncthreads();
-    for (int x = tid; x < V; x += kRowThreads) {
-      const float v = row[x];
-      const unsigned long long key = key_of(v, x, V);
-      if (key < lo) continue;
-      if (shift != kKeyShiftTop && (key >> (shift + kDigitBits)) != prefix) continue;
-      const unsigned long long w = by_mass ? mass_of(v) : 1ull;
-      if (w) atomicAdd(&s.hist[(key >> shift) & (kBins - 1)], w);
+  u64 prefix = 0, above = 0, thr = thr_count, total = 0;
+  int hi_shift = 50;  // bits above the current digit are fixed to `prefix`
+  for (int level = 0; level < 5; ++level) {
+    const int shift = kLevelShift[level];
+    const int bits = kLevelBits[level];
+    const int nb = 1 << bits;
+    for (int b = tid; b < nb; b += kRowThreads) {
+      s.mass[b] = 0;
+      s.cnt[b] = 0;
     }
     __syncthreads();
-    // Thread t owns bins [kBins - 4(t+1), kBins - 4t): prefix order = descending digit.
-    unsigned long long loc[4];
-    unsigned long long lsum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      loc[i] = s.hist[kBins - 1 - (4 * tid + i)];
-      lsum += loc[i];
+    for_row(row, V, [&](int x, float v) {
+      const u64 key = key_of(v, x, V);
+      if (key < lo) return;
+      if (level > 0 && (key >> hi_shift) != prefix) return;
+      const int bin = (int)((key >> shift) & (u64)(nb - 1));
+      atomicAdd(&s.cnt[bin], 1u);
+      if (by_mass) {
+        const u64 w = mass_of(v);
+        if (w) atomicAdd(&s.mass[bin], w);
+      }
+    });
+    __syncthreads();
+    // Thread t owns bins nb-1-4t, ..., nb-4-4t: thread order = descending digit.
+    u64 w0, w1, w2, w3;
+    uint32_t c0, c1, c2, c3;
+    {
+      const int b = nb - 1 - 4 * tid;
+      c0 = b >= 0 ? s.cnt[b] : 0u;
+      c1 = b >= 1 ? s.cnt[b - 1] : 0u;
+      c2 = b >= 2 ? s.cnt[b - 2] : 0u;
+      c3 = b >= 3 ? s.cnt[b - 3] : 0u;
+      if (by_mass) {
+        w0 = b >= 0 ? s.mass[b] : 0ull;
+        w1 = b >= 1 ? s.mass[b - 1] : 0ull;
+        w2 = b >= 2 ? s.mass[b - 2] : 0ull;
+        w3 = b >= 3 ? s.mass[b - 3] : 0ull;
+      } else {
+        w0 = c0; w1 = c1; w2 = c2; w3 = c3;
+      }
     }
-    unsigned long long tot;
-    const unsigned long long excl = block_excl_scan<unsigned long long, kRowThreads>(lsum, s.scan, tot);
-    if (shift == kKeyShiftTop) {
+    const u64 lsum = w0 + w1 + w2 + w3;
+    u64 tot;
+    const u64 excl = block_excl_scan<u64, kRowThreads>(lsum, s.scan, tot);
+    if (level == 0) {
       total = tot;
       if (by_mass) {
         const u128 t = (u128)tp * tot;
-        thr = (unsigned long long)((t + ((u128)1 << 24) - 1) >> 24);
+        thr = (u64)((t + ((u128)1 << 24) - 1) >> 24);
       }
     }
     if (tid == 0) s.flag = 0;
     __syncthreads();
-    if (above + excl < thr && thr <= above + excl + lsum) {
-      unsigned long long run = above + excl;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (run + loc[i] >= thr) {
-          s.res_key = (prefix << kDigitBits) | (unsigned long long)(kBins - 1 - (4 * tid + i));
-          s.res_above = run;
-          s.flag = 1;
-          break;
-        }
-        run += loc[i];
-      }
+    const u64 r0 = above + excl;
+    if (r0 < thr && thr <= r0 + lsum) {
+      const u64 r1 = r0 + w0, r2 = r1 + w1, r3 = r2 + w2;
+      int i;
+      u64 run;
+      uint32_t c;
+      if (r1 >= thr) { i = 0; run = r0; c = c0; }
+      else if (r2 >= thr) { i = 1; run = r1; c = c1; }
+      else if (r3 >= thr) { i = 2; run = r2; c = c2; }
+      else { i = 3; run = r3; c = c3; }
+      s.res_key = (prefix << bits) | (u64)(nb - 1 - (4 * tid + i));
+      s.res_above = run;
+      s.res_cnt = c;
+      s.flag = 1;
     }
     __syncthreads();
     if (!s.flag) {  // thr exceeds the total weight (only when thr == 0 or total == 0)
       out_key = 0;
+      out_mass = 0;
       out_above = 0;
       out_total = total;
       return;
     }
     prefix = s.res_key;
     above = s.res_above;
+    hi_shift = shift;
+    const uint32_t c = s.res_cnt;
     __syncthreads();
+    if (c == 1 || level == 4) {
+      // The crossing bin holds one element (always so once the whole key is fixed).
+      for_row(row, V, [&](int x, float v) {
+        const u64 key = key_of(v, x, V);
+        if (key >= lo && (key >> hi_shift) == prefix) {
+          s.res_key = key;
+          s.res_total = mass_of(v);
+        }
+      });
+      __syncthreads();
+      out_key = s.res_key;
+      out_mass = s.res_total;
+      out_above = above;
+      out_total = total;
+      __syncthreads();
+      return;
+    }
   }
-  out_key = prefix;
-  out_above = above;
-  out_total = total;
 }
 
 // ---------------------------------------------------------------- rows kernel
@@ -215,25 +283,44 @@ __global__ __launch_bounds__(kRowThreads) void accept_rows_kernel(
   const float* src = (r <= K) ? p + (int64_t)e * p_stride + (int64_t)r * V
                               : q + (int64_t)e * q_stride + (int64_t)(r - K - 1) * V;
   const float* row = src;
-  if (input_kind == 1) {  // logits -> float32 probabilities (each thread keeps its own elements)
-    float* dst = probs + ((int64_t)e * nrows + r) * V;
-    float mx = -INFINITY;
-    for (int x = tid; x < V; x += kRowThreads) mx = fmaxf(mx, src[x]);
-    mx = block_reduce_max(mx, red);
-    float sum = 0.f;
-    for (int x = tid; x < V; x += kRowThreads) sum += exp2f((src[x] - mx) * t_scale);
-    sum = block_reduce_sum(sum, red);
-    const float inv = 1.f / sum;
-    for (int x = tid; x < V; x += kRowThreads) dst[x] = exp2f((src[x] - mx) * t_scale) * inv;
-    __syncthreads();
-    row = dst;
-  }
   if (tid == 0) bad = 0;
-  __syncthreads();
   int local_bad = 0;
-  for (int x = tid; x < V; x += kRowThreads) local_bad |= !prob_ok(row[x]);
-  if (local_bad) bad = 1;
+  u64 msum = 0;  // mass of the whole row (used when nothing is truncated)
+  if (input_kind == 1) {
+    // float32 softmax(logits * t_scale in base 2): one pass for the running
+    // (max, sum) of every thread, merged over the block, one pass to write the
+    // probabilities, check them and sum their masses. A NaN logit gives a NaN
+    // probability, a +inf logit makes every probability NaN: both are invalid.
+    float* dst = probs + ((int64_t)e * nrows + r) * V;
+    float mx = -INFINITY, sm = 0.f;
+    for_row(src, V, [&](int, float v) {
+      const float a = v * t_scale;
+      if (a > mx) {
+        sm = sm * exp2f(mx - a) + 1.f;
+        mx = a;
+      } else if (a > -INFINITY) {
+        sm += exp2f(a - mx);
+      }
+    });
+    const float gmx = block_reduce_max(mx, red);
+    const float part = (mx == -INFINITY) ? 0.f : sm * exp2f(mx - gmx);
+    const float sum = block_reduce_sum(part, red);
+    const float inv = 1.f / sum;
+    for_row(src, V, [&](int x, float v) {
+      const float pv = exp2f(v * t_scale - gmx) * inv;
+      dst[x] = pv;
+      if (prob_ok(pv)) msum += mass_of(pv); else local_bad = 1;
+    });
+    row = dst;
+  } else {
+    for_row(row, V, [&](int, float v) {
+      if (prob_ok(v)) msum += mass_of(v); else local_bad = 1;
+    });
+  }
   __syncthreads();
+  if (local_bad) bad = 1;
+  u64 mtot;
+  block_excl_scan<u64, kRowThreads>(msum, s.scan, mtot);  // ends with a barrier
   RowMeta out{};
   if (bad) {
     if (tid == 0) {
@@ -244,35 +331,23 @@ __global__ __launch_bounds__(kRowThreads) void accept_rows_kernel(
   }
   const bool use_k = top_k > 0 && top_k < V;
   const bool use_p = tp < (1u << 24);
-  unsigned long long lo = 0, key, above, total;
+  u64 lo = 0, key, kmass, above, total;
   if (use_k) {
-    radix_select(row, V, 0, false, 0, (unsigned long long)top_k, s, key, above, total);
+    radix_select(row, V, 0, false, 0, (u64)top_k, s, key, kmass, above, total);
     lo = key;
   }
-  unsigned long long z;
-  unsigned long long thresh = lo;
+  u64 z = mtot;
+  u64 thresh = lo;
   if (use_p) {
-    radix_select(row, V, lo, true, tp, 0, s, key, above, total);
+    radix_select(row, V, lo, true, tp, 0, s, key, kmass, above, total);
     thresh = key;
-    // kept mass = mass before the crossing element + its own mass
-    if (tid == 0) s.res_total = 0;
-    __syncthreads();
-    unsigned long long mine = 0;
-    for (int x = tid; x < V; x += kRowThreads)
-      if (key_of(row[x], x, V) == key) mine = mass_of(row[x]);
-    if (mine) atomicAdd(&s.res_total, mine);
-    __syncthreads();
-    z = total ? above + s.res_total : 0;
-  } else {
-    // no top-p: kept mass = mass of every element with key >= lo
-    unsigned long long ms = 0;
-    for (int x = tid; x < V; x += kRowThreads) {
-      const float v = row[x];
+    z = total ? above + kmass : 0;  // kept mass = mass before the last kept element + its own
+  } else if (use_k) {
+    u64 ms = 0;
+    for_row(row, V, [&](int x, float v) {
       if (key_of(v, x, V) >= lo) ms += mass_of(v);
-    }
-    unsigned long long tot;
-    block_excl_scan<unsigned long long, kRowThreads>(ms, s.scan, tot);
-    z = tot;
+    });
+    block_excl_scan<u64, kRowThreads>(ms, s.scan, z);
   }
   if (tid == 0) {
     out.thresh = thresh;
@@ -283,25 +358,110 @@ __global__ __launch_bounds__(kRowThreads) void accept_rows_kernel(
 }
 
 // ---------------------------------------------------------- 128-bit helpers
-__device__ __forceinline__ unsigned long long kept_mass(const float* row, int x, int V, const RowMeta& m) {
-  const float v = row[x];
+__device__ __forceinline__ u64 kept_mass_v(float v, int x, int V, const RowMeta& m) {
   return key_of(v, x, V) >= m.thresh ? mass_of(v) : 0ull;
+}
+
+__device__ __forceinline__ u64 kept_mass(const float* row, int x, int V, const RowMeta& m) {
+  return kept_mass_v(row[x], x, V, m);
 }
 
 // floor(mu * R / 2^24) for mu < 2^24 and R < 2^120 without overflowing 128 bits.
 __device__ __forceinline__ u128 scaled_draw(uint32_t mu, u128 R) {
-  const unsigned long long rh = (unsigned long long)(R >> 64);
-  const unsigned long long rl = (unsigned long long)R;
+  const u64 rh = (u64)(R >> 64);
+  const u64 rl = (u64)R;
   return (((u128)mu * rh) << 40) + (((u128)mu * rl) >> 24);
 }
 
-__device__ __forceinline__ bool accept_test(uint32_t mu, unsigned long long mq, unsigned long long zp,
-                                            unsigned long long mp, unsigned long long zq) {
+__device__ __forceinline__ bool accept_test(uint32_t mu, u64 mq, u64 zp, u64 mp, u64 zq) {
   return (u128)mu * mq * zp < ((u128)mp * zq << 24);
 }
 
 __device__ __forceinline__ bool uniform_ok(float u) { return u >= 0.f && u < 1.f; }
 __device__ __forceinline__ uint32_t mu_of(float u) { return (uint32_t)((double)u * 16777216.0); }
+
+// Draw weight of token x: the residual max(0, mP*ZQ - mQ*ZP) or the mass mP.
+struct DrawRow {
+  const float* P;
+  const float* Q;  // null: weight = mP
+  RowMeta mp, mq;
+  int V;
+  __device__ __forceinline__ u128 w(int x, float pv, float qv) const {
+    const u64 a = kept_mass_v(pv, x, V, mp);
+    if (!Q) return (u128)a;
+    if (a == 0) return 0;
+    const u64 c = kept_mass_v(qv, x, V, mq);
+    const u128 lhs = (u128)a * mq.z, rhs = (u128)c * mp.z;
+    return lhs > rhs ? lhs - rhs : (u128)0;
+  }
+};
+
+// Smallest x with w(0) + ... + w(x) > floor(mu * R / 2^24), R = total weight.
+// Pass 1: every wave sums a contiguous chunk of ids (coalesced 64 at a time).
+// Pass 2: the whole block refines the one chunk that holds the draw, with a
+// contiguous sub-chunk per thread. Returns -1 if R == 0 (only then).
+__device__ int draw_token(const DrawRow& d, uint32_t mu, u128* scan, u128* wsum, int* s_tok) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NW = kEntryThreads / 64;
+  const int V = d.V;
+  const int chunk = (V + NW - 1) / NW;
+  const int c0 = min(V, wave * chunk), c1 = min(V, c0 + chunk);
+  u128 local = 0;
+  for (int base = c0 + lane; base < c1; base += 64 * 4) {
+    float pv[4], qv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = base + 64 * u;
+      pv[u] = x < c1 ? d.P[x] : 0.f;
+      qv[u] = (x < c1 && d.Q) ? d.Q[x] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = base + 64 * u;
+      if (x < c1) local += d.w(x, pv[u], qv[u]);
+    }
+  }
+  // wave total
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const u64 lo = (u64)local, hi = (u64)(local >> 64);
+    const u64 olo = ((u64)__shfl_xor((uint32_t)(lo >> 32), off) << 32) | __shfl_xor((uint32_t)lo, off);
+    const u64 ohi = ((u64)__shfl_xor((uint32_t)(hi >> 32), off) << 32) | __shfl_xor((uint32_t)hi, off);
+    local += ((u128)ohi << 64) | olo;
+  }
+  if (tid == 0) *s_tok = -1;
+  if (lane == 0) wsum[wave] = local;
+  __syncthreads();
+  u128 R = 0, before = 0;
+  int cw = -1;
+  for (int w = 0; w < NW; ++w) R += wsum[w];
+  if (R == 0) return -1;
+  const u128 tau = scaled_draw(mu, R);
+  for (int w = 0; w < NW; ++w) {  // the chunk that holds the draw
+    if (cw < 0 && before + wsum[w] > tau) cw = w;
+    if (cw < 0) before += wsum[w];
+  }
+  // Refine chunk cw: thread t sums a contiguous sub-chunk.
+  const int q0 = min(V, cw * chunk), q1 = min(V, q0 + chunk);
+  const int per = (q1 - q0 + kEntryThreads - 1) / kEntryThreads;
+  const int x0 = min(q1, q0 + tid * per), x1 = min(q1, x0 + per);
+  u128 mine = 0;
+  for (int x = x0; x < x1; ++x) mine += d.w(x, d.P[x], d.Q ? d.Q[x] : 0.f);
+  u128 tot;
+  const u128 excl = before + block_excl_scan<u128, kEntryThreads>(mine, scan, tot);
+  if (excl <= tau && tau < excl + mine) {
+    u128 run = excl;
+    for (int x = x0; x < x1; ++x) {
+      run += d.w(x, d.P[x], d.Q ? d.Q[x] : 0.f);
+      if (run > tau) {
+        *s_tok = x;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  return *s_tok;
+}
 
 // ---------------------------------------------------------------- entry kernel
 __global__ __launch_bounds__(kEntryThreads) void accept_entry_kernel(
@@ -310,8 +470,8 @@ __global__ __launch_bounds__(kEntryThreads) void accept_entry_kernel(
     const float* __restrict__ uniforms, int K, int V, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ out_n) {
   __shared__ u128 scan[kEntryThreads / 64 + 1];
+  __shared__ u128 wsum[kEntryThreads / 64];
   __shared__ int s_j, s_bad, s_tok;
-  __shared__ u128 s_tau;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const RowMeta* mrow = meta + (int64_t)b * meta_stride;
@@ -329,8 +489,8 @@ __global__ __launch_bounds__(kEntryThreads) void accept_entry_kernel(
       for (int i = 0; i < K; ++i) {
         const int d = dr[i];
         const RowMeta mp = mrow[i], mq = mrow[K + 1 + i];
-        const unsigned long long a = kept_mass(P + (int64_t)i * V, d, V, mp);
-        const unsigned long long c = kept_mass(Q + (int64_t)i * V, d, V, mq);
+        const u64 a = kept_mass(P + (int64_t)i * V, d, V, mp);
+        const u64 c = kept_mass(Q + (int64_t)i * V, d, V, mq);
         if (!accept_test(mu_of(us[i]), c, mp.z, a, mq.z)) {
           j = i;
           break;
@@ -339,7 +499,6 @@ __global__ __launch_bounds__(kEntryThreads) void accept_entry_kernel(
     }
     s_bad = bad;
     s_j = j;
-    s_tok = -1;
   }
   __syncthreads();
   const int j = s_j;
@@ -348,52 +507,26 @@ __global__ __launch_bounds__(kEntryThreads) void accept_entry_kernel(
     if (tid == 0) out_n[b] = -1;
     return;
   }
-  const float* Pj = P + (int64_t)j * V;
-  const RowMeta mp = mrow[j];
-  const bool resid = j < K;
-  const float* Qj = resid ? Q + (int64_t)j * V : nullptr;
-  const RowMeta mq = resid ? mrow[K + 1 + j] : RowMeta{};
-  // Contiguous chunk of ids per thread (token-id order).
-  const int per = (V + kEntryThreads - 1) / kEntryThreads;
-  const int x0 = min(V, tid * per), x1 = min(V, x0 + per);
-  auto weight = [&](int x, bool use_resid) -> u128 {
-    const unsigned long long a = kept_mass(Pj, x, V, mp);
-    if (!use_resid) return (u128)a;
-    const unsigned long long c = kept_mass(Qj, x, V, mq);
-    const u128 lhs = (u128)a * mq.z, rhs = (u128)c * mp.z;
-    return lhs > rhs ? lhs - rhs : (u128)0;
-  };
-  bool use_resid = resid;
-  u128 local = 0;
-  for (int x = x0; x < x1; ++x) local += weight(x, use_resid);
-  u128 R;
-  u128 excl = block_excl_scan<u128, kEntryThreads>(local, scan, R);
-  if (use_resid && R == 0) {  // p~_j == q~_j and the draft lay outside both supports: draw from p~_j
-    use_resid = false;
-    local = 0;
-    for (int x = x0; x < x1; ++x) local += weight(x, false);
-    excl = block_excl_scan<u128, kEntryThreads>(local, scan, R);
+  DrawRow d;
+  d.P = P + (int64_t)j * V;
+  d.mp = mrow[j];
+  d.Q = j < K ? Q + (int64_t)j * V : nullptr;
+  d.mq = j < K ? mrow[K + 1 + j] : RowMeta{};
+  d.V = V;
+  const uint32_t mu = mu_of(us[K]);
+  int tok = draw_token(d, mu, scan, wsum, &s_tok);
+  if (tok < 0) {  // p~_j == q~_j and the draft lay outside both supports: draw from p~_j
+    __syncthreads();
+    d.Q = nullptr;
+    tok = draw_token(d, mu, scan, wsum, &s_tok);
   }
-  const u128 tau = scaled_draw(mu_of(us[K]), R);
-  if (excl <= tau && tau < excl + local) {
-    u128 run = excl;
-    for (int x = x0; x < x1; ++x) {
-      run += weight(x, use_resid);
-      if (run > tau) {
-        s_tok = x;
-        break;
-      }
-    }
-  }
-  __syncthreads();
   for (int i = tid; i <= K; i += kEntryThreads) {
     int32_t t = -1;
     if (i < j) t = dr[i];
-    else if (i == j) t = s_tok;
+    else if (i == j) t = tok;
     out_tokens[(int64_t)b * (K + 1) + i] = t;
   }
   if (tid == 0) out_n[b] = j;
-  (void)s_tau;
 }
 
 // ------------------------------------------------------------- shared rows
@@ -407,35 +540,28 @@ __global__ __launch_bounds__(kEntryThreads) void accept_table_kernel(
   int bad = 0;
   for (int i = 0; i < 2 * K + 1; ++i) bad |= meta[i].status;
   if (bad) return;
-  const float* Pj = P + (int64_t)j * V;
-  const RowMeta mp = meta[j];
-  const bool resid = j < K;
-  const float* Qj = resid ? Q + (int64_t)j * V : nullptr;
-  const RowMeta mq = resid ? meta[K + 1 + j] : RowMeta{};
+  DrawRow d;
+  d.P = P + (int64_t)j * V;
+  d.mp = meta[j];
+  d.Q = j < K ? Q + (int64_t)j * V : nullptr;
+  d.mq = j < K ? meta[K + 1 + j] : RowMeta{};
+  d.V = V;
   const int per = (V + kEntryThreads - 1) / kEntryThreads;
   const int x0 = min(V, tid * per), x1 = min(V, x0 + per);
-  auto weight = [&](int x, bool use_resid) -> u128 {
-    const unsigned long long a = kept_mass(Pj, x, V, mp);
-    if (!use_resid) return (u128)a;
-    const unsigned long long c = kept_mass(Qj, x, V, mq);
-    const u128 lhs = (u128)a * mq.z, rhs = (u128)c * mp.z;
-    return lhs > rhs ? lhs - rhs : (u128)0;
-  };
-  bool use_resid = resid;
   u128 local = 0;
-  for (int x = x0; x < x1; ++x) local += weight(x, use_resid);
+  for (int x = x0; x < x1; ++x) local += d.w(x, d.P[x], d.Q ? d.Q[x] : 0.f);
   u128 R;
   u128 excl = block_excl_scan<u128, kEntryThreads>(local, scan, R);
-  if (use_resid && R == 0) {
-    use_resid = false;
+  if (d.Q && R == 0) {
+    d.Q = nullptr;
     local = 0;
-    for (int x = x0; x < x1; ++x) local += weight(x, false);
+    for (int x = x0; x < x1; ++x) local += d.w(x, d.P[x], 0.f);
     excl = block_excl_scan<u128, kEntryThreads>(local, scan, R);
   }
   u128* out = table + (int64_t)j * V;
   u128 run = excl;
   for (int x = x0; x < x1; ++x) {
-    run += weight(x, use_resid);
+    run += d.w(x, d.P[x], d.Q ? d.Q[x] : 0.f);
     out[x] = run;
   }
 }
@@ -462,8 +588,8 @@ __global__ __launch_bounds__(256) void accept_trials_kernel(
   for (int i = 0; i < K; ++i) {
     const int d = dr[i];
     const RowMeta mp = meta[i], mq = meta[K + 1 + i];
-    const unsigned long long a = kept_mass(P + (int64_t)i * V, d, V, mp);
-    const unsigned long long c = kept_mass(Q + (int64_t)i * V, d, V, mq);
+    const u64 a = kept_mass(P + (int64_t)i * V, d, V, mp);
+    const u64 c = kept_mass(Q + (int64_t)i * V, d, V, mq);
     if (!accept_test(mu_of(us[i]), c, mp.z, a, mq.z)) {
       j = i;
       break;
