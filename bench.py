@@ -49,27 +49,33 @@ def log(msg: str) -> None:
 
 
 def make_weights(cfg, torch, seed: int, T_cap: int):
-    """Synthetic packs on the device: uniform code words, scales N(0.02, 0.005), biases N(0, 0.01);
-    KV caches N(0, 1)."""
+    """Synthetic weights on the device: uniform code words, scales N(0.02, 0.005), biases N(0, 0.01),
+    generated row-major and packed into the tiled layout one matrix at a time; KV caches N(0, 1)."""
     from speculative_decoding_verify_vq_amd.stack import QPack, StackWeights
     from synth import bf16_normal_torch, random_words_torch
     dev = torch.device("cuda")
     w = StackWeights()
     sh = cfg.shapes()
+
+    def pack(N, K, bits, s):
+        wq = random_words_torch(N * K * bits // 32, s, dev)
+        sc = bf16_normal_torch((N, K // 64), 0.02, 0.005, s + 100000, dev)
+        bi = bf16_normal_torch((N, K // 64), 0.0, 0.01, s + 200000, dev)
+        p = QPack.from_rows(wq, sc, bi, bits, N, K)
+        torch.cuda.synchronize()
+        del wq, sc, bi
+        return p
+
     s = seed
     for li in range(cfg.layers):
         lay = {}
         for name in ("qkv", "o", "gate_up", "down"):
             N, K = sh[name]
             s += 1
-            lay[name] = QPack(random_words_torch(N * K * cfg.bits // 32, s, dev),
-                              bf16_normal_torch((N, K // 64), 0.02, 0.005, s + 100000, dev),
-                              bf16_normal_torch((N, K // 64), 0.0, 0.01, s + 200000, dev), N, K, cfg.bits)
+            lay[name] = pack(N, K, cfg.bits, s)
         w.layers.append(lay)
     N, K = sh["lm_head"]
-    w.lm_head = QPack(random_words_torch(N * K * cfg.lm_bits // 32, seed + 7, dev),
-                      bf16_normal_torch((N, K // 64), 0.02, 0.005, seed + 8, dev),
-                      bf16_normal_torch((N, K // 64), 0.0, 0.01, seed + 9, dev), N, K, cfg.lm_bits)
+    w.lm_head = pack(N, K, cfg.lm_bits, seed + 7)
     for a in range(cfg.n_attn):
         w.k_cache.append(bf16_normal_torch((cfg.Hkv, T_cap, cfg.D), 0.0, 1.0, seed + 300000 + a, dev))
         w.v_cache.append(bf16_normal_torch((cfg.Hkv, T_cap, cfg.D), 0.0, 1.0, seed + 400000 + a, dev))
@@ -110,27 +116,35 @@ def qmm_roofline(torch, stack, reps: int = 5) -> dict:
     """Average duration of the skinny-QMM launches of the verify step.
 
     The QMM launches of each projection kind (the 64 qkv, o, gate_up and down
-    launches of the step, and the lm_head launch repeated 16 times) are captured
-    into a graph of their own, with the step's buffers and launch configuration;
-    each graph is replayed `reps` times between two HIP events on the stream it
-    runs on. The per-kind durations are weighted by the step's launch counts.
-    Algorithmic bytes per launch: packed codes, scales, biases, activations and
-    outputs."""
+    launches of the step with their fused prologues and epilogues, and the
+    lm_head launch repeated 16 times) are captured into a graph of their own,
+    with the step's buffers and launch configuration; each graph is replayed
+    `reps` times between two HIP events on the stream it runs on. The per-kind
+    durations are weighted by the step's launch counts. Algorithmic bytes per
+    launch: packed codes, scales, biases, activations in, outputs (and the
+    residual read of the residual epilogue)."""
+    from speculative_decoding_verify_vq_amd import vq
     from speculative_decoding_verify_vq_amd.stack import qmm_algorithmic_bytes
     cfg = stack.cfg
-    kinds = {"qkv": (stack.a, stack.qkv), "o": (stack.qkv[:, : cfg.q_width], stack.proj),
-             "gate_up": (stack.a, stack.gu), "down": (stack.act, stack.proj)}
-    jobs = {name: ([lay[name] for lay in stack.w.layers], x, out) for name, (x, out) in kinds.items()}
-    jobs["lm_head"] = ([stack.w.lm_head] * 16, stack.a, stack.logits[0])
-    counts = {name: len(stack.w.layers) for name in kinds}
+    L = stack.w.layers
+    kinds = {
+        "qkv": (lambda p: stack._qmm(stack.h, p, stack.qkv, norm=True), [l["qkv"] for l in L], 2),
+        "o": (lambda p: stack._qmm(stack.qkv[:, : cfg.q_width], p, stack.h, epilogue=vq.VQ_EPI_RESIDUAL,
+                                   y_sumsq=stack.ss), [l["o"] for l in L], 4),
+        "gate_up": (lambda p: stack._qmm(stack.h, p, stack.act, norm=True, epilogue=vq.VQ_EPI_SWIGLU),
+                    [l["gate_up"] for l in L], 1),
+        "down": (lambda p: stack._qmm(stack.act, p, stack.h, epilogue=vq.VQ_EPI_RESIDUAL, y_sumsq=stack.ss),
+                 [l["down"] for l in L], 4),
+        "lm_head": (lambda p: stack._qmm(stack.h, p, stack.logits[0], norm=True), [stack.w.lm_head] * 16, 4),
+    }
+    counts = {name: len(L) for name in ("qkv", "o", "gate_up", "down")}
     counts["lm_head"] = 1
     per_kind = {}
     tot_ms = tot_bytes = 0.0
-    for name, (packs, x, out) in jobs.items():
-        g = capture(torch, lambda: [stack._qmm(x, p, out) for p in packs])
+    for name, (fn, packs, out_bytes) in kinds.items():
+        g = capture(torch, lambda: [fn(p) for p in packs])
         ms = time_graph(torch, g, reps, 1) / len(packs)
         del g
-        out_bytes = 4 if out.dtype == torch.float32 else 2
         nb = qmm_algorithmic_bytes(cfg.M, packs[0].N, packs[0].K, packs[0].bits, out_bytes=out_bytes)
         per_kind[name] = {"us": round(ms * 1e3, 2), "GBs": round(nb / (ms * 1e-3) / 1e9, 1)}
         tot_ms += counts[name] * ms

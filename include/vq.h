@@ -113,6 +113,61 @@ int vq_skinny_qmm(const void* x, int64_t ldx,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Skinny quantized matmul on a prepacked weight, with fused glue
+ *
+ * The same product as vq_skinny_qmm on a layout made once per weight by
+ * vq_qmm_pack: for every tile of 32 output rows and every block of 256 (4-bit)
+ * or 128 (8-bit) inputs, the tile's 32 x 128 bytes of codes followed by its
+ * scales and biases, so that the kernel reads each block as one contiguous
+ * run. Rows past N and groups past K are zero-filled. The pack is an opaque
+ * byte buffer of vq_qmm_pack_bytes() bytes, 16-byte aligned.
+ *
+ * Fused around the product, for the verify pass of a pre-norm stack (the
+ * verify rows go through every projection of every layer; page "The fastest
+ * way to run local LLMs on a Mac", section "Why native MTP doubles decode"):
+ *   prologue  if x_sumsq != NULL, x is RMS-normalised while it is staged:
+ *             x'[m, k] = bf16(x[m, k] / sqrt(S[m] / K + eps)), where S[m] is
+ *             the sum of x_sumsq[m * x_sumsq_parts + p] over the parts p
+ *             (1 <= parts <= 256), as written by a residual epilogue or by
+ *             vq_row_sumsq_bf16 (vq_glue.h). The weight of the norm is one.
+ *   epilogue  VQ_EPI_STORE     y = acc, bf16 or float32 (y_dtype);
+ *             VQ_EPI_RESIDUAL  y = bf16(residual + bf16(acc)), bf16; residual
+ *                              may be y itself (in place, then ldr == ldy);
+ *                              if y_sumsq != NULL, y_sumsq[m * P + c] = sum of
+ *                              y[m, n]^2 over the 128 columns of block c,
+ *                              P = vq_sumsq_parts(N) = ceil(N / 128);
+ *             VQ_EPI_SWIGLU    the N rows of the pack are, per block of 128,
+ *                              64 gate rows and then the 64 up rows of the
+ *                              same outputs; y has N / 2 columns (N a
+ *                              multiple of 128): y[m, j] = bf16(silu(g) * u)
+ *                              with g, u the bf16-rounded products.
+ * Shapes, strides and alignment as vq_skinny_qmm; bf16 outputs 2-byte aligned,
+ * float32 outputs and the sums of squares 4-byte aligned. Deterministic.
+ * ---------------------------------------------------------------------- */
+#define VQ_EPI_STORE 0
+#define VQ_EPI_RESIDUAL 1
+#define VQ_EPI_SWIGLU 2
+
+/* Bytes of the pack of a [N, K] weight (0 for an unsupported shape). */
+size_t vq_qmm_pack_bytes(int bits, int group_size, int N, int K);
+
+/* Writes the pack of (wq, scales, biases) — the row-major layout of
+ * vq_skinny_qmm — into `packed` (device, packed_bytes >= vq_qmm_pack_bytes). */
+int vq_qmm_pack(const void* wq, const void* scales, const void* biases, int bits, int group_size, int N,
+                int K, void* packed, size_t packed_bytes, void* stream);
+
+/* Number of sum-of-squares parts of an N-column bf16 matrix: ceil(N / 128). */
+int vq_sumsq_parts(int N);
+
+size_t vq_qmm_packed_workspace(int bits, int group_size, int M, int N, int K);
+
+int vq_qmm_packed(const void* x, int64_t ldx, const float* x_sumsq, int x_sumsq_parts, float eps,
+                  const void* packed, int bits, int group_size, int M, int N, int K,
+                  int epilogue, const void* residual, int64_t ldr,
+                  void* y, int64_t ldy, int y_dtype, float* y_sumsq,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Multi-row decode attention
  *
  * For query row i in [0, M), query head h, KV head g = h / (Hq / Hkv):

@@ -26,6 +26,11 @@ extern "C" {
 int vq_rmsnorm_bf16(const void* x, int64_t ldx, void* y, int64_t ldy, int M, int N, float eps,
                     void* stream);
 
+/* Per-row sums of squares of a bf16 matrix x [M, N] (row stride ldx) per block
+ * of 128 columns: out[m * P + c] = sum of x[m, n]^2 over the columns of block
+ * c, P = ceil(N / 128); the x_sumsq input of vq_qmm_packed (vq.h). */
+int vq_row_sumsq_bf16(const void* x, int64_t ldx, int M, int N, float* out, void* stream);
+
 /* y[i] = a[i] + b[i] for i < n (y may alias a or b). */
 int vq_add_bf16(const void* a, const void* b, void* y, int64_t n, void* stream);
 

@@ -245,30 +245,92 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
   }
 }
 
-// Merge the per-range partials of one (query row, KV head): one thread per head dim.
+// Merge the per-range partials of one (query row, KV head, 64 head dims).
+// 256 threads = 16 groups of 16 lanes; lane i of a group owns head dims
+// 4i..4i+3 of the block's 64 and group g sums the ranges g, g+16, ...; the
+// groups' sums are added in LDS in a fixed order (deterministic).
+constexpr int kCombineGroups = 16;
+constexpr int kMaxSplits = 1024;
+
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int M, int Hq, int Hkv, int D,
     int splits, uint16_t* __restrict__ out, int64_t out_rs) {
+  __shared__ float w_lds[kMaxSplits];
+  __shared__ float red[256 / 64];
+  __shared__ float4 acc_lds[kCombineGroups][16];
   const int row = blockIdx.x;
   const int kvh = blockIdx.y;
+  const int d0 = blockIdx.z * 64;
+  const int tid = threadIdx.x;
   const int G = Hq / Hkv;
   const int rows = M * G;
-  float mmax = -INFINITY;
-  for (int s = 0; s < splits; ++s)
-    mmax = fmaxf(mmax, part_ml[(((size_t)s * Hkv + kvh) * rows + row) * 2]);
-  const int m = row / G;
-  const int h = kvh * G + row % G;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const size_t base = ((size_t)s * Hkv + kvh) * rows + row;
-      const float ms = part_ml[base * 2];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - mmax);
-      den += w * part_ml[base * 2 + 1];
-      num += w * part_o[base * D + d];
+  const size_t s_stride = (size_t)Hkv * rows;  // partial rows between consecutive ranges
+  const size_t base = (size_t)kvh * rows + row;
+  // Range weights exp2(m_s - max) and the merged denominator.
+  float mloc = -INFINITY;
+  for (int s = tid; s < splits; s += 256) mloc = fmaxf(mloc, part_ml[(s * s_stride + base) * 2]);
+  for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+  if ((tid & 63) == 0) red[tid >> 6] = mloc;
+  __syncthreads();
+  const float mmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float dloc = 0.f;
+  for (int s = tid; s < splits; s += 256) {
+    const float ms = part_ml[(s * s_stride + base) * 2];
+    const float w = ms == -INFINITY ? 0.f : exp2f(ms - mmax);
+    w_lds[s] = w;
+    dloc += w * part_ml[(s * s_stride + base) * 2 + 1];
+  }
+  for (int off = 32; off > 0; off >>= 1) dloc += __shfl_xor(dloc, off);
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = dloc;
+  __syncthreads();
+  const float den = (red[0] + red[1]) + (red[2] + red[3]);
+  // Weighted sum of the partial O rows.
+  const int grp = tid >> 4;
+  const int d = d0 + 4 * (tid & 15);
+  const float* po = part_o + base * D + d;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int s = grp;
+  for (; s + 3 * kCombineGroups < splits; s += 4 * kCombineGroups) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = *reinterpret_cast<const float4*>(po + (s + u * kCombineGroups) * s_stride * D);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = w_lds[s + u * kCombineGroups];
+      acc.x += w * v[u].x;
+      acc.y += w * v[u].y;
+      acc.z += w * v[u].z;
+      acc.w += w * v[u].w;
     }
-    out[(size_t)m * out_rs + (size_t)h * D + d] = f32_to_bf16_rne(num / den);
+  }
+  for (; s < splits; s += kCombineGroups) {
+    const float4 v = *reinterpret_cast<const float4*>(po + s * s_stride * D);
+    const float w = w_lds[s];
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
+  }
+  acc_lds[grp][tid & 15] = acc;
+  __syncthreads();
+  if (tid < 16) {
+    float4 t = acc_lds[0][tid];
+    for (int g2 = 1; g2 < kCombineGroups; ++g2) {
+      const float4 u = acc_lds[g2][tid];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+    }
+    const float inv = 1.f / den;
+    const int m = row / G;
+    const int h = kvh * G + row % G;
+    uint2 o2;
+    o2.x = pack_bf16x2(t.x * inv, t.y * inv);
+    o2.y = pack_bf16x2(t.z * inv, t.w * inv);
+    *reinterpret_cast<uint2*>(out + (size_t)m * out_rs + (size_t)h * D + d0 + 4 * tid) = o2;
   }
 }
 
@@ -278,10 +340,10 @@ AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T) {
   AttnPlan p{};
   p.rows = M * (Hq / Hkv);
   p.row_tiles = (p.rows + 31) / 32;
-  // About two workgroups per compute unit, at least 128 keys per range.
+  // Up to two workgroups per compute unit, at least 256 keys per range.
   const int tiles = (T + kTileKeys - 1) / kTileKeys;
   int s = (2 * kNumCU + Hkv - 1) / Hkv;
-  int max_s = (tiles + 3) / 4;
+  int max_s = (tiles + 7) / 8;
   s = s > max_s ? max_s : s;
   s = s < 1 ? 1 : s;
   const int tiles_per = (tiles + s - 1) / s;
@@ -327,7 +389,7 @@ hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const 
 #undef VQ_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(plan.rows, Hkv), dim3(D < 256 ? D : 256), 0, stream,
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(plan.rows, Hkv, D / 64), dim3(256), 0, stream,
                      part_o, part_ml, M, Hq, Hkv, D, plan.splits, op, out_rs);
   return hipGetLastError();
 }

@@ -14,19 +14,28 @@
 //     (64 inputs each); each of its 4 waves owns 32 of the columns.
 //   * Codes stream in blocks of 128 bytes per row (4 groups of 4-bit codes, 2 of
 //     8-bit): one block of a wave is 32 rows x 128 B, fetched by 4 dwordx4
-//     instructions that each cover 8 whole 128-byte lines. Three blocks per
-//     wave are in flight. An arrived block is written to a per-wave LDS buffer
-//     (XOR-swizzled so writes and reads are bank-conflict free) and read back in
-//     the B-operand layout of v_mfma_f32_32x32x16_bf16: lane n (of 32) holds
-//     the codes of row n, lanes 0-31 the first half of the group's inputs and
-//     lanes 32-63 the second half, so a group is a chain of four MFMAs.
+//     instructions. Two (4-bit) or three (8-bit) blocks per wave are in flight.
+//     An arrived block is written to a per-wave LDS buffer (XOR-swizzled so
+//     writes and reads are bank-conflict free) and read back in the B-operand
+//     layout of v_mfma_f32_32x32x16_bf16: lane n (of 32) holds the codes of row
+//     n, lanes 0-31 the first half of the group's inputs and lanes 32-63 the
+//     second half, so a group is a chain of four MFMAs.
+//   * Two weight layouts. Row-major (the plain format: row n holds its codes,
+//     scales and biases are [N, K/64]): each instruction covers 8 rows x 128 B
+//     and each lane fetches the scales and biases of its own column. Tiled
+//     (made once by the pack kernel below): for every 32-row tile and every
+//     block, the 32 x 128 B of codes followed by the block's scales and biases
+//     row by row, so that a block is one contiguous run of 4.5 KiB (4-bit) and
+//     every fetch is a linear 1 KiB stretch. The tiled layout halves the memory
+//     requests per byte and keeps DRAM pages open; it is the fast path.
 //   * Codes become bf16 in registers. 4-bit: OR-ing a nibble into the mantissa
 //     of 128.0 gives the exact bf16 value 128 + q, two per 32-bit word, and the
 //     constant 128 is removed per group through the group sums of x. 8-bit:
 //     v_cvt_f32_ubyte + a byte permute gives the exact bf16 q.
 //   * x (zero-padded to MT = 8 or 16 rows) is staged in LDS once per workgroup,
-//     in the element order of the unpack, with its per-group sums; the scales
-//     and biases of the workgroup's rows and groups are preloaded into LDS too.
+//     in the element order of the unpack, with its per-group sums. Optionally it
+//     is RMS-normalised on the way in (x * 1/sqrt(mean(x^2) + eps), rounded to
+//     bf16), from per-row sums of squares that the producer of x wrote.
 //   * The MFMA gives D_g = sum_{k in g} x*q' per group; scale and bias apply in
 //     float32:
 //         acc += s * D_g + (b - 128 s) * sum_{k in g} x     (4-bit)
@@ -35,6 +44,12 @@
 //     workgroups; float32 partials go to the workspace and the last workgroup of
 //     a column block (integer completion counter) adds them in split order, so
 //     results are bit-identical run to run.
+//   * Epilogues: store (bf16 or float32); residual (y = bf16(r + bf16(acc)),
+//     with per-row sums of squares of y per 128-column block for the next
+//     RMSNorm); SwiGLU (rows packed as 64 gate rows then the 64 matching up
+//     rows per 128-row block; y = bf16(silu(bf16(g)) * bf16(u)), N/2 columns).
+#include <math.h>
+
 #include "vq_internal.h"
 
 namespace vq {
@@ -50,21 +65,48 @@ constexpr int kColsWG = kWaves * kTileN;  // columns per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kCG = 16;                   // max groups per workgroup (one LDS chunk of x)
 constexpr int kXUnits = kCG * 8 + 1;      // 16-byte units per LDS row of x (+1 pad)
-constexpr int kSBStride = kCG + 1;        // u32 (scale | bias << 16) per LDS row (+1 pad)
 constexpr int kRowBytes = 128;            // bytes per row per pipeline block
 constexpr int kLoads = 32 * kRowBytes / (64 * 16);  // dwordx4 per lane per block (= 4)
-constexpr int kInFlight = 3;              // blocks in flight per wave
 constexpr size_t kCounterBytes = 32768;   // completion counters (split-K only)
-constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(int));
 
-// Codes of one pipeline block held by one lane (4 x 16 bytes).
-struct Regs {
-  u32x4 w[kLoads];
-};
+enum { kLayoutRow = 0, kLayoutRowScalar = 1, kLayoutTiled = 2 };
 
 template <int BITS>
 struct BlockCfg {
-  static constexpr int GB = kRowBytes / (8 * BITS);  // groups per block: 4 (4-bit), 2 (8-bit)
+  static constexpr int GB = kRowBytes / (8 * BITS);            // groups per block: 4 (4-bit), 2 (8-bit)
+  static constexpr int SB = BITS == 4 ? 16 : 8;                // tiled scale|bias bytes per row per block
+  static constexpr int BYTES = 32 * kRowBytes + 32 * SB;       // tiled bytes per (tile, block)
+  static constexpr int IN_FLIGHT = BITS == 4 ? 2 : 3;          // blocks in flight per wave
+};
+
+// Everything a launch needs; passed by value in the kernel arguments.
+struct QmmArgs {
+  const uint16_t* x;
+  int64_t ldx;
+  const float* x_ss;  // RMSNorm prologue: sums of squares [M][ss_parts]
+  int ss_parts;
+  float eps;
+  const uint8_t* wq;  // row-major codes, or the tiled pack
+  const uint16_t* scales;
+  const uint16_t* biases;
+  int M, N, K;
+  int splits, groups_per_split;
+  void* y;
+  int64_t ldy;
+  int y_f32;
+  const uint16_t* res;  // residual epilogue
+  int64_t ldr;
+  float* y_ss;          // residual epilogue: sums of squares of y [M][ceil(N / 128)] (nullable)
+  float* partial;
+  int* counters;
+};
+
+// One pipeline block held by one lane: 4 x 16 bytes of codes and the scales
+// and biases of the block's groups for the lane's own output column (4 bf16
+// each for 4-bit, 2 for 8-bit).
+struct Regs {
+  u32x4 w[kLoads];
+  uint32_t s[2], b[2];
 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -74,6 +116,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+
+__device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_rne(f)); }
 
 // Eight nibbles -> eight bf16 values 128 + q, in the element order
 // (q0, q4, q1, q5, q2, q6, q3, q7).
@@ -110,19 +154,17 @@ __device__ __forceinline__ bf16x8 unpack8(uint32_t w0, uint32_t w1) {
 // over all LDS banks.
 __device__ __forceinline__ int tslot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
-template <int BITS, int MT, bool VEC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void qmm_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wq,
-    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, int M, int N, int K,
-    int splits, int groups_per_split, void* __restrict__ y, int64_t ldy, int y_f32,
-    float* __restrict__ partial, int* __restrict__ counters) {
+template <int BITS, int MT, int LAYOUT, int EPI, bool NORM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void qmm_kernel(const QmmArgs a) {
   constexpr int GB = BlockCfg<BITS>::GB;
+  constexpr int kInFlight = BlockCfg<BITS>::IN_FLIGHT;
   constexpr int kUseful = MT / 2;  // accumulator registers that hold rows < MT
 
   __shared__ u32x4 xl[MT * kXUnits];
   __shared__ float xsum[kCG][16];
-  __shared__ uint32_t sbl[kColsWG * kSBStride];
   __shared__ u32x4 tl[kWaves][32 * 8];
+  __shared__ float red[kWaves][16];
+  __shared__ float inv_rms[16];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
@@ -132,92 +174,160 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   const int l32 = lane & 31;
   const int cb = blockIdx.x;
   const int split = blockIdx.y;
-  const int G = K >> 6;
-  const size_t row_bytes = (size_t)K * BITS / 8;
-  const int g0 = split * groups_per_split;
-  const int g1 = min(G, g0 + groups_per_split);
+  const int M = a.M, N = a.N, K = a.K;
+  const int G = K >> 6;                                                // groups of the matrix
+  const int Gp = LAYOUT == kLayoutTiled ? (G + GB - 1) / GB * GB : G;  // groups of the layout
+  const int g0 = split * a.groups_per_split;
+  const int g1 = min(Gp, g0 + a.groups_per_split);
   const int ng = g1 - g0;
   const int nblk = (ng + GB - 1) / GB;
   const int n0 = cb * kColsWG;
 
-  // ---- coalesced code loads: instruction j, lane l -> row 8j + l/8, chunk l%8
+  // ---- code and scale/bias addresses
   const int lrow = lane >> 3;
   const int lchunk = lane & 7;
   const uint8_t* lptr[kLoads];
+  const uint8_t* tile_base = nullptr;
+  const uint16_t* srow = nullptr;
+  const uint16_t* brow = nullptr;
+  if constexpr (LAYOUT == kLayoutTiled) {
+    const int n_tiles = (N + 31) / 32;
+    const int tile = min((n0 + wave * kTileN) / 32, n_tiles - 1);
+    tile_base = a.wq + (size_t)tile * (Gp / GB) * BlockCfg<BITS>::BYTES;
+  } else {
+    const size_t row_bytes = (size_t)K * BITS / 8;
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) {
-    const int n = min(n0 + wave * kTileN + 8 * j + lrow, N - 1);
-    lptr[j] = wq + (size_t)n * row_bytes;
+    for (int j = 0; j < kLoads; ++j) {
+      const int n = min(n0 + wave * kTileN + 8 * j + lrow, N - 1);
+      lptr[j] = a.wq + (size_t)n * row_bytes;
+    }
+    // Scale / bias rows of this lane's output column (lanes l and l+32 share one).
+    const int ncol = min(n0 + wave * kTileN + l32, N - 1);
+    srow = a.scales + (size_t)ncol * G;
+    brow = a.biases + (size_t)ncol * G;
   }
-  // Byte offset of this lane's chunk in block bi (clamped inside [g0, g1)).
-  auto chunk_off = [&](int bi) __attribute__((always_inline)) -> size_t {
-    const int gchunk = g0 + bi * GB + (lchunk * 16) / (8 * BITS);
-    const int gc = min(gchunk, g1 - 1);
-    return (size_t)gc * (8 * BITS) + (lchunk * 16) % (8 * BITS);
-  };
   auto issue = [&](Regs& R, int bi) __attribute__((always_inline)) {
-    const size_t off = chunk_off(bi);
+    if constexpr (LAYOUT == kLayoutTiled) {
+      // Block index clamped inside [g0, g1); one contiguous run per block.
+      const int kb = min(g0 / GB + bi, (g1 - 1) / GB);
+      const uint8_t* blk = tile_base + (size_t)kb * BlockCfg<BITS>::BYTES;
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) R.w[j] = *reinterpret_cast<const u32x4*>(lptr[j] + off);
+      for (int j = 0; j < kLoads; ++j) R.w[j] = *reinterpret_cast<const u32x4*>(blk + j * 1024 + lane * 16);
+      if constexpr (BITS == 4) {
+        const u32x4 sb = *reinterpret_cast<const u32x4*>(blk + 32 * kRowBytes + l32 * 16);
+        R.s[0] = sb[0];
+        R.s[1] = sb[1];
+        R.b[0] = sb[2];
+        R.b[1] = sb[3];
+      } else {
+        const uint2 sb = *reinterpret_cast<const uint2*>(blk + 32 * kRowBytes + l32 * 8);
+        R.s[0] = sb.x;
+        R.b[0] = sb.y;
+        R.s[1] = R.b[1] = 0u;
+      }
+    } else {
+      // Byte offset of this lane's chunk (clamped inside [g0, g1)).
+      const int gc = min(g0 + bi * GB + (lchunk * 16) / (8 * BITS), g1 - 1);
+      const size_t off = (size_t)gc * (8 * BITS) + (lchunk * 16) % (8 * BITS);
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) R.w[j] = *reinterpret_cast<const u32x4*>(lptr[j] + off);
+      if constexpr (LAYOUT == kLayoutRow) {
+        // GB groups from a GB-aligned group index that stays inside [g0, g1).
+        const int gq = min(g0 + bi * GB, g1 - GB);
+        if constexpr (GB == 4) {
+          const uint2 sv = *reinterpret_cast<const uint2*>(srow + gq);
+          const uint2 bv = *reinterpret_cast<const uint2*>(brow + gq);
+          R.s[0] = sv.x;
+          R.s[1] = sv.y;
+          R.b[0] = bv.x;
+          R.b[1] = bv.y;
+        } else {
+          R.s[0] = *reinterpret_cast<const uint32_t*>(srow + gq);
+          R.b[0] = *reinterpret_cast<const uint32_t*>(brow + gq);
+          R.s[1] = R.b[1] = 0u;
+        }
+      } else {
+        uint32_t sw[4], bw[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          const int gq = min(g0 + bi * GB + (jb < GB ? jb : 0), g1 - 1);
+          sw[jb] = srow[gq];
+          bw[jb] = brow[gq];
+        }
+        R.s[0] = sw[0] | (sw[1] << 16);
+        R.s[1] = sw[2] | (sw[3] << 16);
+        R.b[0] = bw[0] | (bw[1] << 16);
+        R.b[1] = bw[2] | (bw[3] << 16);
+      }
+    }
   };
 
-  // Three code blocks in flight per wave. Every block load is issued
-  // unconditionally (block index clamped) and the block sequence is unrolled,
-  // so the wait counts the compiler derives are exact.
+  // Code blocks in flight per wave. Every block load is issued unconditionally
+  // (block index clamped) and the block sequence is unrolled, so the wait
+  // counts the compiler derives are exact.
   Regs R[kInFlight];
 
-  // ---- stage x (element order of the unpack) with group sums, and scale|bias
+  // ---- stage x (element order of the unpack) with group sums
   {
     constexpr int kIters = MT * kCG * 8 / kThreads;
     static_assert(kIters * kThreads == MT * kCG * 8, "staging loop must be uniform");
+    const int gx1 = min(g1, G);  // groups past G exist only as zero padding of the tiled layout
     u32x4 v[kIters];
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
       const int t = tid + it * kThreads;
       const int m = t / (kCG * 8);
       const int c = t % (kCG * 8);
-      const int gg = min(g0 + (c >> 3), g1 - 1);
-      v[it] = *reinterpret_cast<const u32x4*>(x + (size_t)min(m, M - 1) * ldx + (size_t)gg * 64 + (c & 7) * 8);
+      const int gg = max(0, min(g0 + (c >> 3), gx1 - 1));
+      v[it] = *reinterpret_cast<const u32x4*>(a.x + (size_t)min(m, M - 1) * a.ldx + (size_t)gg * 64 + (c & 7) * 8);
     }
-    if constexpr (VEC) {
-      // 4 groups of scales and of biases per 8-byte unit; kColsWG rows x (kCG / 4) units.
-      constexpr int kSBIters = kColsWG * (kCG / 4) / kThreads;
+    // RMSNorm prologue: wave w reduces the sums of squares of rows w, w+4, ...
+    // (4 parts per lane, butterfly order), loaded before the code blocks.
+    float ssv[NORM ? 4 : 1][NORM ? 4 : 1];
+    if constexpr (NORM) {
 #pragma unroll
-      for (int it = 0; it < kSBIters; ++it) {
-        const int t = tid + it * kThreads;
-        const int r = t / (kCG / 4);
-        const int u = t % (kCG / 4);
-        const int gl = 4 * u;
-        const int glc = min(gl, (ng - 1) & ~3);  // clamped: the load stays inside the row
-        const int n = min(n0 + r, N - 1);
-        const uint2 sv = *reinterpret_cast<const uint2*>(scales + (size_t)n * G + g0 + glc);
-        const uint2 bv = *reinterpret_cast<const uint2*>(biases + (size_t)n * G + g0 + glc);
-        uint32_t* d = &sbl[r * kSBStride + gl];
-        d[0] = (sv.x & 0xFFFFu) | (bv.x << 16);
-        d[1] = (sv.x >> 16) | (bv.x & 0xFFFF0000u);
-        d[2] = (sv.y & 0xFFFFu) | (bv.y << 16);
-        d[3] = (sv.y >> 16) | (bv.y & 0xFFFF0000u);
-      }
-    } else {
-      for (int t = tid; t < kColsWG * ng; t += kThreads) {
-        const int r = t / ng, gl = t % ng;
-        const int n = min(n0 + r, N - 1);
-        sbl[r * kSBStride + gl] =
-            (uint32_t)scales[(size_t)n * G + g0 + gl] | ((uint32_t)biases[(size_t)n * G + g0 + gl] << 16);
+      for (int i = 0; i < 4; ++i) {
+        const int m = wave + kWaves * i;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int p = lane + 64 * u;
+          ssv[i][u] = (m < M && p < a.ss_parts) ? a.x_ss[(size_t)m * a.ss_parts + p] : 0.f;
+        }
       }
     }
-    // The first code blocks go out after the x, scale and bias loads, so that
-    // waiting for those (in-order counter) leaves the code blocks in flight.
-    issue(R[0], 0);
-    issue(R[1], 1);
-    issue(R[2], 2);
+    // The first code blocks go out after the x loads, so that waiting for
+    // those (in-order counter) leaves the code blocks in flight.
+#pragma unroll
+    for (int i = 0; i < kInFlight; ++i) issue(R[i], i);
+    if constexpr (NORM) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float t = (ssv[i][0] + ssv[i][1]) + (ssv[i][2] + ssv[i][3]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
+        const int m = wave + kWaves * i;
+        if (lane == 0 && m < M) inv_rms[m] = 1.f / sqrtf(t / (float)K + a.eps);
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
       const int t = tid + it * kThreads;
       const int m = t / (kCG * 8);
       const int c = t % (kCG * 8);
       const int gg = g0 + (c >> 3);
-      u32x4 w = (m < M && gg < g1) ? v[it] : u32x4{0, 0, 0, 0};
+      u32x4 w = (m < M && gg < gx1) ? v[it] : u32x4{0, 0, 0, 0};
+      if constexpr (NORM) {
+        if (m < M) {
+          const float r = inv_rms[m];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = f32_to_bf16_rne(bf16_bits_to_f32(w[e] & 0xFFFFu) * r);
+            const uint32_t hi = f32_to_bf16_rne(bf16_bits_to_f32(w[e] >> 16) * r);
+            w[e] = lo | (hi << 16);
+          }
+        }
+      }
       float s8 = bf16_bits_to_f32(w[0] & 0xFFFFu) + bf16_bits_to_f32(w[0] >> 16) +
                  bf16_bits_to_f32(w[1] & 0xFFFFu) + bf16_bits_to_f32(w[1] >> 16) +
                  bf16_bits_to_f32(w[2] & 0xFFFFu) + bf16_bits_to_f32(w[2] >> 16) +
@@ -243,29 +353,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
   for (int r = 0; r < kUseful; ++r) acc[r] = 0.f;
   u32x4* tw = tl[wave];
-  const uint32_t* sbrow = &sbl[(wave * kTileN + l32) * kSBStride];
+  uint32_t cur_s[2], cur_b[2];  // scales / biases of the block being computed
   const bool a_live = l32 < MT;  // lanes whose A row is a real (possibly zero) x row
 
-  // Consume block bi held in R: transpose through LDS, then 4 (or 2) groups.
+  // Consume a block: transpose the codes through LDS, keep its scales / biases.
   auto consume = [&](const Regs& R) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) tw[tslot(8 * j + lrow, lchunk)] = R.w[j];
+    cur_s[0] = R.s[0];
+    cur_s[1] = R.s[1];
+    cur_b[0] = R.b[0];
+    cur_b[1] = R.b[1];
   };
   auto compute = [&](int bi) __attribute__((always_inline)) {
 #pragma unroll
     for (int jb = 0; jb < GB; ++jb) {
       const int gl = bi * GB + jb;  // group index within this workgroup's range
       if (gl >= ng) break;
-      bf16x8 a[4];
+      bf16x8 av[4];
       if (a_live) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int unit = (BITS == 4) ? gl * 8 + half * 4 + i : gl * 8 + (i >> 1) * 4 + half * 2 + (i & 1);
-          a[i] = __builtin_bit_cast(bf16x8, xl[l32 * kXUnits + unit]);
+          av[i] = __builtin_bit_cast(bf16x8, xl[l32 * kXUnits + unit]);
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = bf16x8{};
+        for (int i = 0; i < 4; ++i) av[i] = bf16x8{};
       }
       u32x4 wv0, wv1;
       if (BITS == 4) {
@@ -275,7 +389,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
         wv0 = tw[tslot(l32, 4 * jb + half)];
         wv1 = tw[tslot(l32, 4 * jb + 2 + half)];
       }
-      const uint32_t sbv = sbrow[gl];
       f32x16 d = {};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -286,10 +399,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
           const u32x4 wh = (i >> 1) ? wv1 : wv0;
           bv = (i & 1) ? unpack8(wh[2], wh[3]) : unpack8(wh[0], wh[1]);
         }
-        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bv, d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv, d, 0, 0, 0);
       }
-      const float s = bf16_bits_to_f32(sbv & 0xFFFFu);
-      const float bb = bf16_bits_to_f32(sbv >> 16);
+      const uint32_t sw = cur_s[jb >> 1], bw = cur_b[jb >> 1];
+      const float s = __uint_as_float((jb & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
+      const float bb = __uint_as_float((jb & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
       const float c = (BITS == 4) ? __builtin_fmaf(-128.f, s, bb) : bb;
 #pragma unroll
       for (int r = 0; r < kUseful; ++r) {
@@ -311,18 +425,73 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   // ------------------------------------------------------------------ epilogue
   const int n = n0 + wave * kTileN + l32;
   const bool n_ok = n < N;
+  const int n_cb = (N + kColsWG - 1) / kColsWG;
+  uint16_t* yb = reinterpret_cast<uint16_t*>(a.y);
   auto store = [&](int m, int col, float v) __attribute__((always_inline)) {
-    if (y_f32)
-      reinterpret_cast<float*>(y)[(size_t)m * ldy + col] = v;
+    if (a.y_f32)
+      reinterpret_cast<float*>(a.y)[(size_t)m * a.ldy + col] = v;
     else
-      reinterpret_cast<uint16_t*>(y)[(size_t)m * ldy + col] = f32_to_bf16_rne(v);
+      yb[(size_t)m * a.ldy + col] = f32_to_bf16_rne(v);
   };
-  if (splits == 1) {
-    if (n_ok) {
+  // Residual: y = bf16(r + bf16(v)); returns the stored value as float.
+  auto residual = [&](int m, int col, float v) __attribute__((always_inline)) -> float {
+    const float h = round_bf16(bf16_bits_to_f32(a.res[(size_t)m * a.ldr + col]) + round_bf16(v));
+    yb[(size_t)m * a.ldy + col] = f32_to_bf16_rne(h);
+    return h;
+  };
+  auto swiglu = [&](float g, float u) __attribute__((always_inline)) -> uint16_t {
+    const float gb = round_bf16(g);
+    return f32_to_bf16_rne(gb / (1.f + expf(-gb)) * round_bf16(u));
+  };
+
+  if (a.splits == 1) {
+    if constexpr (EPI == kEpiStore) {
+      if (n_ok) {
+#pragma unroll
+        for (int r = 0; r < kUseful; ++r) {
+          const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+          if (m < M) store(m, n, acc[r]);
+        }
+      }
+    } else if constexpr (EPI == kEpiResidual) {
+      float sq[kUseful];
 #pragma unroll
       for (int r = 0; r < kUseful; ++r) {
         const int m = 8 * (r >> 2) + 4 * half + (r & 3);
-        if (m < M) store(m, n, acc[r]);
+        sq[r] = 0.f;
+        if (n_ok && m < M) {
+          const float h = residual(m, n, acc[r]);
+          sq[r] = h * h;
+        }
+      }
+      if (a.y_ss) {
+        // Sum over the wave's 32 columns (lanes of one half), then over the waves.
+#pragma unroll
+        for (int r = 0; r < kUseful; ++r) {
+#pragma unroll
+          for (int off = 16; off > 0; off >>= 1) sq[r] += __shfl_xor(sq[r], off);
+          if (l32 == 0) red[wave][8 * (r >> 2) + 4 * half + (r & 3)] = sq[r];
+        }
+        __syncthreads();
+        if (tid < M) a.y_ss[(size_t)tid * n_cb + cb] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+      }
+    } else {
+      // SwiGLU: waves 2, 3 hold the up rows of the gate rows of waves 0, 1.
+      float* upl = reinterpret_cast<float*>(&tl[0][0]);  // 16 x 64 floats; the block buffers are free now
+      __syncthreads();
+      if (wave >= 2) {
+#pragma unroll
+        for (int r = 0; r < kUseful; ++r)
+          upl[(8 * (r >> 2) + 4 * half + (r & 3)) * 64 + (wave - 2) * 32 + l32] = acc[r];
+      }
+      __syncthreads();
+      const int col = cb * 64 + wave * 32 + l32;
+      if (wave < 2 && col < N / 2) {
+#pragma unroll
+        for (int r = 0; r < kUseful; ++r) {
+          const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+          if (m < M) yb[(size_t)m * a.ldy + col] = swiglu(acc[r], upl[m * 64 + wave * 32 + l32]);
+        }
       }
     }
     return;
@@ -334,7 +503,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   // counter increment is issued. No store or load of this exchange goes through
   // a possibly stale cache line, so no L2 writeback or invalidation is needed
   // (which would evict the weight lines other waves are still streaming).
-  float* part = partial + (size_t)split * M * N;
+  float* part = a.partial + (size_t)split * M * N;
   if (n_ok) {
 #pragma unroll
     for (int r = 0; r < kUseful; ++r) {
@@ -345,33 +514,201 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0)
-    s_last = __hip_atomic_fetch_add(&counters[cb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
+    s_last = __hip_atomic_fetch_add(&a.counters[cb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.splits - 1;
   __syncthreads();
   if (!s_last) return;
-  for (int t = tid; t < M * kColsWG; t += kThreads) {
-    const int m = t / kColsWG;
-    const int col = cb * kColsWG + t % kColsWG;
-    if (col >= N) continue;
-    float v = 0.f;
-    for (int sp = 0; sp < splits; ++sp)
-      v += __hip_atomic_load(&partial[((size_t)sp * M + m) * N + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    store(m, col, v);
+  // Sum the partials in split order, 4 splits x kVPT loads in flight per thread.
+  // Thread t, value i covers element t + i * 256 of the block's [M][128] (store,
+  // residual) or of its [M][64] gate/up column pairs (SwiGLU).
+  constexpr int kCols = EPI == kEpiSwiGLU ? kColsWG / 2 : kColsWG;
+  constexpr int kVPT = MT * kCols / kThreads;
+  constexpr int kPair = EPI == kEpiSwiGLU ? 2 : 1;
+  float v[kVPT][kPair];
+  size_t idx[kVPT];
+  bool ok[kVPT];
+#pragma unroll
+  for (int i = 0; i < kVPT; ++i) {
+    const int t = tid + i * kThreads;
+    const int m = t / kCols;
+    const int col = cb * kColsWG + t % kCols;
+    ok[i] = m < M && col < N;
+    idx[i] = (size_t)m * N + col;
+#pragma unroll
+    for (int h = 0; h < kPair; ++h) v[i][h] = 0.f;
   }
-  if (tid == 0) __hip_atomic_store(&counters[cb], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const size_t sstride = (size_t)M * N;
+  for (int sp = 0; sp < a.splits; sp += 4) {
+    float pv[4][kVPT][kPair];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int i = 0; i < kVPT; ++i) {
+#pragma unroll
+        for (int h = 0; h < kPair; ++h)
+          pv[u][i][h] = (ok[i] && sp + u < a.splits)
+                            ? __hip_atomic_load(&a.partial[(sp + u) * sstride + idx[i] + h * 64], __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT)
+                            : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int i = 0; i < kVPT; ++i) {
+#pragma unroll
+        for (int h = 0; h < kPair; ++h) v[i][h] += pv[u][i][h];
+      }
+    }
+  }
+  if constexpr (EPI == kEpiStore) {
+#pragma unroll
+    for (int i = 0; i < kVPT; ++i) {
+      const int t = tid + i * kThreads;
+      if (ok[i]) store(t / kCols, cb * kColsWG + t % kCols, v[i][0]);
+    }
+  } else if constexpr (EPI == kEpiResidual) {
+    // Threads 0-127 of value i hold row 2i, threads 128-255 row 2i+1: each
+    // wave sums half a row, then the two halves are added.
+#pragma unroll
+    for (int i = 0; i < kVPT; ++i) {
+      const int t = tid + i * kThreads;
+      float sq = 0.f;
+      if (ok[i]) {
+        const float h = residual(t / kCols, cb * kColsWG + t % kCols, v[i][0]);
+        sq = h * h;
+      }
+      if (a.y_ss) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+        if (lane == 0) red[wave & 1][2 * i + (wave >> 1)] = sq;
+      }
+    }
+    if (a.y_ss) {
+      __syncthreads();
+      if (tid < M) a.y_ss[(size_t)tid * n_cb + cb] = red[0][tid] + red[1][tid];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kVPT; ++i) {
+      const int t = tid + i * kThreads;
+      const int col = cb * (kColsWG / 2) + t % kCols;
+      if (ok[i] && col < N / 2) yb[(size_t)(t / kCols) * a.ldy + col] = swiglu(v[i][0], v[i][1]);
+    }
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[cb], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Tiled layout from the row-major one. Workgroup (tile t, block kb), thread u:
+// 16 bytes of codes of row 32t + u/8, chunk u%8; threads 0-31 also write the
+// scale|bias record of row 32t + u. Rows past N and groups past K are zero.
+template <int BITS>
+__global__ __launch_bounds__(256) void qmm_pack_kernel(const uint8_t* __restrict__ wq,
+                                                       const uint16_t* __restrict__ scales,
+                                                       const uint16_t* __restrict__ biases, int N, int K,
+                                                       uint8_t* __restrict__ out) {
+  constexpr int GB = BlockCfg<BITS>::GB;
+  const int t = blockIdx.x;
+  const int kb = blockIdx.y;
+  const int KB = gridDim.y;
+  const int G = K / 64;
+  const size_t row_bytes = (size_t)K * BITS / 8;
+  const int u = threadIdx.x;
+  const int r = u >> 3, c = u & 7;
+  const int n = 32 * t + r;
+  uint8_t* blk = out + ((size_t)t * KB + kb) * BlockCfg<BITS>::BYTES;
+  const size_t src = (size_t)kb * kRowBytes + c * 16;
+  u32x4 w = {0u, 0u, 0u, 0u};
+  if (n < N && src < row_bytes) w = *reinterpret_cast<const u32x4*>(wq + (size_t)n * row_bytes + src);
+  *reinterpret_cast<u32x4*>(blk + (size_t)r * kRowBytes + c * 16) = w;
+  if (u < 32) {
+    const int nr = 32 * t + u;
+    uint32_t sv[4] = {0u, 0u, 0u, 0u}, bv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      const int g = kb * GB + j;
+      if (nr < N && g < G) {
+        sv[j] = scales[(size_t)nr * G + g];
+        bv[j] = biases[(size_t)nr * G + g];
+      }
+    }
+    if constexpr (BITS == 4) {
+      u32x4 sb;
+      sb[0] = sv[0] | (sv[1] << 16);
+      sb[1] = sv[2] | (sv[3] << 16);
+      sb[2] = bv[0] | (bv[1] << 16);
+      sb[3] = bv[2] | (bv[3] << 16);
+      *reinterpret_cast<u32x4*>(blk + 32 * kRowBytes + u * 16) = sb;
+    } else {
+      uint2 sb;
+      sb.x = sv[0] | (sv[1] << 16);
+      sb.y = bv[0] | (bv[1] << 16);
+      *reinterpret_cast<uint2*>(blk + 32 * kRowBytes + u * 8) = sb;
+    }
+  }
+}
+
+// Per-row sums of squares of a bf16 matrix per 128-column block (the layout the
+// residual epilogue writes), for the first RMSNorm of a chain.
+__global__ __launch_bounds__(128) void row_sumsq_kernel(const uint16_t* __restrict__ x, int64_t ldx, int N,
+                                                        float* __restrict__ out) {
+  __shared__ float r2[2];
+  const int cb = blockIdx.x, m = blockIdx.y;
+  const int n_cb = gridDim.x;
+  const int col = cb * kColsWG + threadIdx.x;
+  float v = 0.f;
+  if (col < N) {
+    v = bf16_bits_to_f32(x[(size_t)m * ldx + col]);
+    v = v * v;
+  }
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) r2[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) out[(size_t)m * n_cb + cb] = r2[0] + r2[1];
 }
 
 }  // namespace
 
-QmmPlan qmm_plan(int bits, int M, int N, int K) {
+size_t qmm_pack_bytes(int bits, int N, int K) {
+  const int GB = bits == 4 ? BlockCfg<4>::GB : BlockCfg<8>::GB;
+  const size_t blk = bits == 4 ? BlockCfg<4>::BYTES : BlockCfg<8>::BYTES;
+  const size_t tiles = (size_t)(N + 31) / 32;
+  const size_t kbs = (size_t)(K / 64 + GB - 1) / GB;
+  return tiles * kbs * blk;
+}
+
+hipError_t qmm_pack(const void* wq, const void* scales, const void* biases, int bits, int N, int K, void* out,
+                    hipStream_t stream) {
+  const int GB = bits == 4 ? BlockCfg<4>::GB : BlockCfg<8>::GB;
+  dim3 grid((N + 31) / 32, (K / 64 + GB - 1) / GB);
+  auto* w = reinterpret_cast<const uint8_t*>(wq);
+  auto* s = reinterpret_cast<const uint16_t*>(scales);
+  auto* b = reinterpret_cast<const uint16_t*>(biases);
+  auto* o = reinterpret_cast<uint8_t*>(out);
+  if (bits == 4)
+    hipLaunchKernelGGL(qmm_pack_kernel<4>, grid, dim3(256), 0, stream, w, s, b, N, K, o);
+  else
+    hipLaunchKernelGGL(qmm_pack_kernel<8>, grid, dim3(256), 0, stream, w, s, b, N, K, o);
+  return hipGetLastError();
+}
+
+hipError_t row_sumsq(const void* x, int64_t ldx, int M, int N, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(row_sumsq_kernel, dim3((N + kColsWG - 1) / kColsWG, M), dim3(128), 0, stream,
+                     reinterpret_cast<const uint16_t*>(x), ldx, N, out);
+  return hipGetLastError();
+}
+
+int qmm_sumsq_parts(int N) { return (N + kColsWG - 1) / kColsWG; }
+
+QmmPlan qmm_plan(int bits, int M, int N, int K, bool tiled) {
   QmmPlan p{};
   p.mt = M <= 8 ? 8 : 16;
   p.cols_per_wg = kColsWG;
   p.n_blocks = (N + kColsWG - 1) / kColsWG;
-  const int G = K / 64;
   const int GB = bits == 4 ? 4 : 2;
+  const int G = tiled ? (K / 64 + GB - 1) / GB * GB : K / 64;
   // Enough workgroups for about two per compute unit, and at most kCG groups
   // per workgroup (one LDS chunk of x). Split boundaries fall on multiples of 4
-  // groups (the scale/bias preload unit).
+  // groups (the scale/bias vector unit and the tiled block).
   int s = (2 * kNumCU + p.n_blocks - 1) / p.n_blocks;
   const int s_lds = (G + kCG - 1) / kCG;
   s = s < s_lds ? s_lds : s;
@@ -380,45 +717,82 @@ QmmPlan qmm_plan(int bits, int M, int N, int K) {
   gps = (gps + 2) / 4 * 4;  // nearest multiple of 4
   if (gps < 4) gps = 4;
   if (gps > kCG) gps = kCG;
-  (void)GB;
-  (void)kMaxCounters;  // n_blocks <= kMaxCounters is guaranteed by the N <= 2^20 limit of the ABI
   p.groups_per_split = gps;
   p.splits = (G + gps - 1) / gps;
+  // n_blocks <= kCounterBytes / 4 follows from the N <= 2^20 limit of the ABI.
   p.counter_bytes = p.splits > 1 ? kCounterBytes : 0;
   p.partial_bytes = p.splits > 1 ? align_up((size_t)p.splits * M * N * sizeof(float), 256) : 0;
   return p;
 }
 
-hipError_t qmm_launch(const QmmPlan& plan, const void* x, int64_t ldx, const void* wq,
-                      const void* scales, const void* biases, int bits, int M, int N, int K,
-                      void* y, int64_t ldy, int y_f32, void* workspace, hipStream_t stream) {
-  int* counters = reinterpret_cast<int*>(workspace);
-  float* partial = plan.splits > 1
-                       ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.counter_bytes)
-                       : nullptr;
+hipError_t qmm_launch(const QmmPlan& plan, const QmmCall& c, hipStream_t stream) {
+  QmmArgs a{};
+  a.x = reinterpret_cast<const uint16_t*>(c.x);
+  a.ldx = c.ldx;
+  a.x_ss = c.x_ss;
+  a.ss_parts = c.ss_parts;
+  a.eps = c.eps;
+  a.wq = reinterpret_cast<const uint8_t*>(c.wq);
+  a.scales = reinterpret_cast<const uint16_t*>(c.scales);
+  a.biases = reinterpret_cast<const uint16_t*>(c.biases);
+  a.M = c.M;
+  a.N = c.N;
+  a.K = c.K;
+  a.splits = plan.splits;
+  a.groups_per_split = plan.groups_per_split;
+  a.y = c.y;
+  a.ldy = c.ldy;
+  a.y_f32 = c.y_f32;
+  a.res = reinterpret_cast<const uint16_t*>(c.res);
+  a.ldr = c.ldr;
+  a.y_ss = c.y_ss;
+  a.counters = reinterpret_cast<int*>(c.workspace);
+  a.partial = plan.splits > 1
+                  ? reinterpret_cast<float*>(reinterpret_cast<char*>(c.workspace) + plan.counter_bytes)
+                  : nullptr;
   dim3 grid(plan.n_blocks, plan.splits);
   dim3 block(kThreads);
-  auto* xp = reinterpret_cast<const uint16_t*>(x);
-  auto* wp = reinterpret_cast<const uint8_t*>(wq);
-  auto* sp = reinterpret_cast<const uint16_t*>(scales);
-  auto* bp = reinterpret_cast<const uint16_t*>(biases);
-  // Vector (8-byte) scale/bias loads need 4-group alignment of every row and
-  // split start; otherwise 2-byte loads.
-  const int G = K / 64;
-  const bool vec = (G % 4 == 0) && (plan.groups_per_split % 4 == 0) &&
-                   (reinterpret_cast<uintptr_t>(scales) % 8 == 0) && (reinterpret_cast<uintptr_t>(biases) % 8 == 0);
-#define VQ_QMM_LAUNCH(B, MTV, V)                                                                     \
-  hipLaunchKernelGGL((qmm_kernel<B, MTV, V>), grid, block, 0, stream, xp, ldx, wp, sp, bp, M, N, K, \
-                     plan.splits, plan.groups_per_split, y, ldy, y_f32, partial, counters)
-#define VQ_QMM_MT(B, V) \
-  if (plan.mt == 8) VQ_QMM_LAUNCH(B, 8, V); else VQ_QMM_LAUNCH(B, 16, V);
-  if (bits == 4) {
-    if (vec) { VQ_QMM_MT(4, true) } else { VQ_QMM_MT(4, false) }
-  } else {
-    if (vec) { VQ_QMM_MT(8, true) } else { VQ_QMM_MT(8, false) }
+  const int G = c.K / 64;
+  int layout = kLayoutTiled;
+  if (!c.tiled) {
+    // Vector (8-byte) scale/bias loads need 4-group alignment of every row and
+    // split start; otherwise 2-byte loads.
+    const bool vec = (G % 4 == 0) && (plan.groups_per_split % 4 == 0) &&
+                     (reinterpret_cast<uintptr_t>(c.scales) % 8 == 0) &&
+                     (reinterpret_cast<uintptr_t>(c.biases) % 8 == 0);
+    layout = vec ? kLayoutRow : kLayoutRowScalar;
   }
-#undef VQ_QMM_MT
-#undef VQ_QMM_LAUNCH
+  const bool norm = c.x_ss != nullptr;
+#define VQ_K(B, MT, L, E, NRM) hipLaunchKernelGGL((qmm_kernel<B, MT, L, E, NRM>), grid, block, 0, stream, a)
+#define VQ_EPI_NORM(B, MT)                                         \
+  switch (c.epilogue * 2 + (norm ? 1 : 0)) {                       \
+    case 0: VQ_K(B, MT, kLayoutTiled, kEpiStore, false); break;    \
+    case 1: VQ_K(B, MT, kLayoutTiled, kEpiStore, true); break;     \
+    case 2: VQ_K(B, MT, kLayoutTiled, kEpiResidual, false); break; \
+    case 3: VQ_K(B, MT, kLayoutTiled, kEpiResidual, true); break;  \
+    case 4: VQ_K(B, MT, kLayoutTiled, kEpiSwiGLU, false); break;   \
+    default: VQ_K(B, MT, kLayoutTiled, kEpiSwiGLU, true); break;   \
+  }
+#define VQ_BITS(B)                                                \
+  if (layout == kLayoutRow) {                                     \
+    if (plan.mt == 8) VQ_K(B, 8, kLayoutRow, kEpiStore, false);   \
+    else VQ_K(B, 16, kLayoutRow, kEpiStore, false);               \
+  } else if (layout == kLayoutRowScalar) {                        \
+    if (plan.mt == 8) VQ_K(B, 8, kLayoutRowScalar, kEpiStore, false); \
+    else VQ_K(B, 16, kLayoutRowScalar, kEpiStore, false);         \
+  } else if (plan.mt == 8) {                                      \
+    VQ_EPI_NORM(B, 8)                                             \
+  } else {                                                        \
+    VQ_EPI_NORM(B, 16)                                            \
+  }
+  if (c.bits == 4) {
+    VQ_BITS(4)
+  } else {
+    VQ_BITS(8)
+  }
+#undef VQ_BITS
+#undef VQ_EPI_NORM
+#undef VQ_K
   return hipGetLastError();
 }
 

@@ -104,7 +104,7 @@ const char* vq_version(void) { return "0.1.0"; }
 // ------------------------------------------------------------------ QMM
 size_t vq_skinny_qmm_workspace(int bits, int group_size, int M, int N, int K) {
   if (!qmm_shape_ok(bits, group_size, M, N, K)) return 0;
-  const vq::QmmPlan p = vq::qmm_plan(bits, M, N, K);
+  const vq::QmmPlan p = vq::qmm_plan(bits, M, N, K, false);
   return p.counter_bytes + p.partial_bytes;
 }
 
@@ -125,13 +125,128 @@ int vq_skinny_qmm(const void* x, int64_t ldx, const void* wq, const void* scales
     return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: x and wq must be 16-byte aligned");
   if (!aligned(scales, 2) || !aligned(biases, 2) || !aligned(y, y_dtype == VQ_F32 ? 4 : 2))
     return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: misaligned scales, biases or y");
-  const vq::QmmPlan plan = vq::qmm_plan(bits, M, N, K);
+  const vq::QmmPlan plan = vq::qmm_plan(bits, M, N, K, false);
   int rc = check_workspace(workspace, workspace_bytes, plan.counter_bytes + plan.partial_bytes);
   if (rc) return rc;
   if ((rc = check_device())) return rc;
-  hipError_t e = vq::qmm_launch(plan, x, ldx, wq, scales, biases, bits, M, N, K, y, ldy, y_dtype == VQ_F32,
-                                workspace, reinterpret_cast<hipStream_t>(stream));
+  vq::QmmCall c{};
+  c.x = x;
+  c.ldx = ldx;
+  c.wq = wq;
+  c.scales = scales;
+  c.biases = biases;
+  c.tiled = false;
+  c.bits = bits;
+  c.M = M;
+  c.N = N;
+  c.K = K;
+  c.epilogue = vq::kEpiStore;
+  c.y = y;
+  c.ldy = ldy;
+  c.y_f32 = y_dtype == VQ_F32;
+  c.workspace = workspace;
+  hipError_t e = vq::qmm_launch(plan, c, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_skinny_qmm launch");
+}
+
+size_t vq_qmm_pack_bytes(int bits, int group_size, int N, int K) {
+  if (!qmm_shape_ok(bits, group_size, 1, N, K)) return 0;
+  return vq::qmm_pack_bytes(bits, N, K);
+}
+
+int vq_qmm_pack(const void* wq, const void* scales, const void* biases, int bits, int group_size, int N, int K,
+                void* packed, size_t packed_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!wq || !scales || !biases || !packed) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_pack: NULL pointer");
+  if (!qmm_shape_ok(bits, group_size, 1, N, K))
+    return fail(VQ_ERR_INVALID_ARG, "vq_qmm_pack: unsupported bits=%d group_size=%d N=%d K=%d", bits, group_size, N, K);
+  if (!aligned(wq, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(biases, 2))
+    return fail(VQ_ERR_INVALID_ARG, "vq_qmm_pack: wq and packed must be 16-byte aligned");
+  const size_t need = vq::qmm_pack_bytes(bits, N, K);
+  if (packed_bytes < need) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_pack: packed has %zu bytes, %zu needed", packed_bytes, need);
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = vq::qmm_pack(wq, scales, biases, bits, N, K, packed, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_qmm_pack launch");
+}
+
+size_t vq_qmm_packed_workspace(int bits, int group_size, int M, int N, int K) {
+  if (!qmm_shape_ok(bits, group_size, M, N, K)) return 0;
+  const vq::QmmPlan p = vq::qmm_plan(bits, M, N, K, true);
+  return p.counter_bytes + p.partial_bytes;
+}
+
+int vq_sumsq_parts(int N) { return N >= 1 ? vq::qmm_sumsq_parts(N) : 0; }
+
+int vq_qmm_packed(const void* x, int64_t ldx, const float* x_sumsq, int x_sumsq_parts, float eps, const void* packed,
+                  int bits, int group_size, int M, int N, int K, int epilogue, const void* residual, int64_t ldr,
+                  void* y, int64_t ldy, int y_dtype, float* y_sumsq, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  g_err[0] = 0;
+  if (!x || !packed || !y) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: NULL data pointer");
+  if (!qmm_shape_ok(bits, group_size, M, N, K))
+    return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: unsupported bits=%d group_size=%d M=%d N=%d K=%d", bits,
+                group_size, M, N, K);
+  if (ldx < K || ldx % 8 != 0) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: ldx must be >= K and a multiple of 8");
+  if (!aligned(x, 16) || !aligned(packed, 16))
+    return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: x and packed must be 16-byte aligned");
+  if (x_sumsq) {
+    if (x_sumsq_parts < 1 || x_sumsq_parts > 256)
+      return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: x_sumsq_parts must be in [1, 256] (got %d)", x_sumsq_parts);
+    if (!(eps >= 0.f) || !isfinite(eps)) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: eps must be finite and >= 0");
+    if (!aligned(x_sumsq, 4)) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: misaligned x_sumsq");
+  }
+  if (y_sumsq && epilogue != VQ_EPI_RESIDUAL)
+    return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: y_sumsq is produced by the residual epilogue only");
+  if (y_sumsq && !aligned(y_sumsq, 4)) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: misaligned y_sumsq");
+  switch (epilogue) {
+    case VQ_EPI_STORE:
+      if (y_dtype != VQ_BF16 && y_dtype != VQ_F32) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: bad y_dtype %d", y_dtype);
+      if (ldy < N) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: ldy must be >= N");
+      break;
+    case VQ_EPI_RESIDUAL:
+      if (y_dtype != VQ_BF16) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: the residual epilogue writes bf16");
+      if (!residual) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: residual is NULL");
+      if (ldy < N || ldr < N) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: ldy and ldr must be >= N");
+      if (residual == y && ldr != ldy)
+        return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: an in-place residual needs ldr == ldy");
+      if (!aligned(residual, 2)) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: misaligned residual");
+      break;
+    case VQ_EPI_SWIGLU:
+      if (y_dtype != VQ_BF16) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: the SwiGLU epilogue writes bf16");
+      if (N % 128 != 0) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: SwiGLU needs N a multiple of 128 (got %d)", N);
+      if (ldy < N / 2) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: ldy must be >= N / 2");
+      break;
+    default:
+      return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: unknown epilogue %d", epilogue);
+  }
+  if (!aligned(y, y_dtype == VQ_F32 ? 4 : 2)) return fail(VQ_ERR_INVALID_ARG, "vq_qmm_packed: misaligned y");
+  const vq::QmmPlan plan = vq::qmm_plan(bits, M, N, K, true);
+  int rc = check_workspace(workspace, workspace_bytes, plan.counter_bytes + plan.partial_bytes);
+  if (rc) return rc;
+  if ((rc = check_device())) return rc;
+  vq::QmmCall c{};
+  c.x = x;
+  c.ldx = ldx;
+  c.x_ss = x_sumsq;
+  c.ss_parts = x_sumsq ? x_sumsq_parts : 0;
+  c.eps = eps;
+  c.wq = packed;
+  c.tiled = true;
+  c.bits = bits;
+  c.M = M;
+  c.N = N;
+  c.K = K;
+  c.epilogue = epilogue;
+  c.res = residual;
+  c.ldr = ldr;
+  c.y = y;
+  c.ldy = ldy;
+  c.y_f32 = y_dtype == VQ_F32;
+  c.y_ss = y_sumsq;
+  c.workspace = workspace;
+  hipError_t e = vq::qmm_launch(plan, c, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_qmm_packed launch");
 }
 
 // ------------------------------------------------------------ attention
@@ -216,6 +331,16 @@ int vq_rmsnorm_bf16(const void* x, int64_t ldx, void* y, int64_t ldy, int M, int
   if (rc) return rc;
   hipError_t e = vq::glue_rmsnorm(x, ldx, y, ldy, M, N, eps, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_rmsnorm_bf16 launch");
+}
+
+int vq_row_sumsq_bf16(const void* x, int64_t ldx, int M, int N, float* out, void* stream) {
+  g_err[0] = 0;
+  if (!x || !out || M < 1 || M > 65535 || N < 1 || N > (1 << 20) || ldx < N || !aligned(x, 2) || !aligned(out, 4))
+    return fail(VQ_ERR_INVALID_ARG, "vq_row_sumsq_bf16: invalid arguments");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = vq::row_sumsq(x, ldx, M, N, out, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_row_sumsq_bf16 launch");
 }
 
 int vq_add_bf16(const void* a, const void* b, void* y, int64_t n, void* stream) {

@@ -24,10 +24,38 @@ struct QmmPlan {
   size_t counter_bytes;  // zeroed completion counters at the start of the workspace
   size_t partial_bytes;  // float32 partial sums [splits][M][N]
 };
-QmmPlan qmm_plan(int bits, int M, int N, int K);
-hipError_t qmm_launch(const QmmPlan& plan, const void* x, int64_t ldx, const void* wq,
-                      const void* scales, const void* biases, int bits, int M, int N, int K,
-                      void* y, int64_t ldy, int y_f32, void* workspace, hipStream_t stream);
+
+enum { kEpiStore = 0, kEpiResidual = 1, kEpiSwiGLU = 2 };
+
+// One validated QMM call (row-major or tiled weights, any epilogue).
+struct QmmCall {
+  const void* x;
+  int64_t ldx;
+  const float* x_ss;  // nullable: RMSNorm prologue from per-row sums of squares [M][ss_parts]
+  int ss_parts;
+  float eps;
+  const void* wq;     // row-major codes, or the tiled pack (then scales / biases unused)
+  const void* scales;
+  const void* biases;
+  bool tiled;
+  int bits, M, N, K;
+  int epilogue;
+  const void* res;    // residual epilogue
+  int64_t ldr;
+  void* y;
+  int64_t ldy;
+  int y_f32;
+  float* y_ss;        // residual epilogue: per-row sums of squares per 128 columns (nullable)
+  void* workspace;
+};
+
+QmmPlan qmm_plan(int bits, int M, int N, int K, bool tiled);
+hipError_t qmm_launch(const QmmPlan& plan, const QmmCall& call, hipStream_t stream);
+size_t qmm_pack_bytes(int bits, int N, int K);
+hipError_t qmm_pack(const void* wq, const void* scales, const void* biases, int bits, int N, int K, void* out,
+                    hipStream_t stream);
+hipError_t row_sumsq(const void* x, int64_t ldx, int M, int N, float* out, hipStream_t stream);
+int qmm_sumsq_parts(int N);
 
 // ----------------------------------------------------------- attention
 struct AttnPlan {

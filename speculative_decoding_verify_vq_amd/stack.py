@@ -4,20 +4,21 @@ The verify pass of MTP speculative decoding runs the last committed token and
 the K drafted tokens (M = K + 1 rows) through one forward pass, then accepts or
 rejects the drafts exactly (page "The fastest way to run local LLMs on a Mac",
 sections "Why native MTP doubles decode" and "Why exact acceptance matters").
-Per layer:
+Per layer, with h the bf16 residual stream and S its per-row sums of squares
+(per 128 columns):
 
-    a   = rmsnorm(h)
-    qkv = skinny_qmm(a, W_qkv)                      fused q | k | v
+    qkv = qmm(rms(h), W_qkv)                         RMSNorm fused into the staging of x
     attention layers: append k, v at positions ctx .. ctx+M-1, then
           c = multirow_attn(q, K cache, V cache, T = ctx + M)
     other layers (their recurrent state is out of scope): c = q
-    h  += skinny_qmm(c, W_o)
-    gu  = skinny_qmm(rmsnorm(h), W_gate_up)         fused gate | up
-    h  += skinny_qmm(silu(gate) * up, W_down)
+    h, S = h + qmm(c, W_o)                           residual epilogue, writes S
+    act  = swiglu(qmm(rms(h), W_gate_up))            gate|up rows interleaved per 64 outputs
+    h, S = h + qmm(act, W_down)
 
-then float32 logits = skinny_qmm(rmsnorm(h), W_lm) feed spec_accept in logits
-mode together with the draft logits. Every launch goes to one stream, so the
-whole step can be captured once into a HIP graph and replayed.
+then float32 logits = qmm(rms(h), W_lm) feed spec_accept in logits mode together
+with the draft logits. Weights are held in the tiled pack of vq_qmm_pack. Every
+launch goes to one stream, so the whole step can be captured once into a HIP
+graph and replayed.
 """
 from __future__ import annotations
 
@@ -52,6 +53,7 @@ class StackConfig:
     top_k: int = 0
     top_p: float = 0.95
     group_size: int = 64
+    eps: float = 1e-6
 
     def is_attn(self, layer: int) -> bool:
         return layer % self.attn_every == self.attn_every - 1
@@ -77,21 +79,27 @@ class StackConfig:
 
 @dataclass
 class QPack:
-    """One quantized weight matrix W[N, K] in the library's packed layout."""
-    wq: torch.Tensor       # int32 words, N * K * bits / 32
-    scales: torch.Tensor   # bf16 [N, K / group_size]
-    biases: torch.Tensor   # bf16 [N, K / group_size]
+    """One quantized weight matrix W[N, K] in the tiled pack of vq_qmm_pack."""
+    packed: torch.Tensor   # uint8, vq.qmm_pack_bytes(bits, N, K) bytes
     N: int
     K: int
     bits: int
+    group_size: int = 64
 
     def nbytes(self) -> int:
-        return self.wq.numel() * 4 + self.scales.numel() * 2 + self.biases.numel() * 2
+        """Algorithmic bytes of the weight: codes + one bf16 scale and bias per group."""
+        return self.N * self.K * self.bits // 8 + 4 * self.N * (self.K // self.group_size)
+
+    @staticmethod
+    def from_rows(wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int, N: int, K: int,
+                  group_size: int = 64) -> "QPack":
+        """Packs a row-major weight (int32 code words, bf16 scales and biases [N, K / gs])."""
+        return QPack(vq.qmm_pack(wq, scales, biases, bits, N, K, group_size), N, K, bits, group_size)
 
 
 @dataclass
 class StackWeights:
-    layers: list = field(default_factory=list)   # per layer: dict name -> QPack
+    layers: list = field(default_factory=list)   # per layer: dict name -> QPack ("gate_up" rows interleaved)
     lm_head: QPack | None = None
     k_cache: list = field(default_factory=list)  # per attention layer: bf16 [Hkv, T_cap, D]
     v_cache: list = field(default_factory=list)
@@ -110,18 +118,16 @@ class DenseVerifyStack:
         M = cfg.M
         bf = torch.bfloat16
         self.h = torch.empty((M, cfg.hidden), dtype=bf, device=dev)
-        self.a = torch.empty((M, cfg.hidden), dtype=bf, device=dev)
+        self.ss = torch.empty((M, vq.sumsq_parts(cfg.hidden)), dtype=torch.float32, device=dev)
         self.qkv = torch.empty((M, cfg.qkv_width), dtype=bf, device=dev)
         self.ctx_out = torch.empty((M, cfg.q_width), dtype=bf, device=dev)
-        self.proj = torch.empty((M, cfg.hidden), dtype=bf, device=dev)
-        self.gu = torch.empty((M, 2 * cfg.inter), dtype=bf, device=dev)
         self.act = torch.empty((M, cfg.inter), dtype=bf, device=dev)
         self.logits = torch.empty((1, M, cfg.vocab), dtype=torch.float32, device=dev)
         self.probs = torch.empty((1, 2 * M - 1, cfg.vocab), dtype=torch.float32, device=dev)
         self.tokens = torch.empty((1, M), dtype=torch.int32, device=dev)
         self.n_acc = torch.empty((1,), dtype=torch.int32, device=dev)
         sh = cfg.shapes()
-        qmm_ws = max(vq.qmm_workspace_bytes(b, M, N, K)
+        qmm_ws = max(vq.qmm_packed_workspace_bytes(b, M, N, K)
                      for name, (N, K) in sh.items()
                      for b in ([cfg.lm_bits] if name == "lm_head" else [cfg.bits]))
         T = cfg.ctx + M
@@ -137,37 +143,35 @@ class DenseVerifyStack:
         off = (-buf.data_ptr()) % 256
         return buf[off:]
 
-    def _qmm(self, x, pack: QPack, out):
-        vq.skinny_qmm(x, pack.wq, pack.scales, pack.biases, pack.bits, pack.N, pack.K, self.cfg.group_size,
-                      out=out, workspace=self._wsv("qmm"))
+    def _qmm(self, x, pack: QPack, out, *, norm: bool = False, epilogue: int = vq.VQ_EPI_STORE, y_sumsq=None):
+        vq.qmm_packed(x, pack.packed, pack.bits, pack.N, pack.K, group_size=pack.group_size,
+                      x_sumsq=self.ss if norm else None, eps=self.cfg.eps, epilogue=epilogue,
+                      residual=self.h if epilogue == vq.VQ_EPI_RESIDUAL else None, out=out, y_sumsq=y_sumsq,
+                      workspace=self._wsv("qmm"))
 
     def forward_hidden(self, h_in: torch.Tensor) -> torch.Tensor:
-        """Runs the layers on h_in [M, hidden] (bf16); returns the final hidden rows."""
+        """Runs the layers on h_in [M, hidden] (bf16); returns the final hidden rows
+        (their sums of squares are left in self.ss for the final RMSNorm)."""
         cfg = self.cfg
         self.h.copy_(h_in)
+        vq.row_sumsq(self.h, out=self.ss)
         ai = 0
         for li, lay in enumerate(self.w.layers):
-            vq.rmsnorm(self.h, out=self.a)
-            self._qmm(self.a, lay["qkv"], self.qkv)
+            self._qmm(self.h, lay["qkv"], self.qkv, norm=True)
             q = self.qkv[:, : cfg.q_width]
             if cfg.is_attn(li):
                 kc, vc = self.w.k_cache[ai], self.w.v_cache[ai]
                 ai += 1
                 vq.kv_append(self.qkv, cfg.q_width, cfg.q_width + cfg.Hkv * cfg.D, kc, vc, cfg.ctx)
-                qv = q.view(cfg.M, cfg.Hq, cfg.D) if q.is_contiguous() else q.as_strided(
-                    (cfg.M, cfg.Hq, cfg.D), (self.qkv.stride(0), cfg.D, 1))
+                qv = q.as_strided((cfg.M, cfg.Hq, cfg.D), (self.qkv.stride(0), cfg.D, 1))
                 ov = self.ctx_out.view(cfg.M, cfg.Hq, cfg.D)
                 vq.multirow_attn(qv, kc, vc, cfg.ctx + cfg.M, cfg.D ** -0.5, out=ov, workspace=self._wsv("attn"))
                 c = self.ctx_out
             else:
                 c = q
-            self._qmm(c, lay["o"], self.proj)
-            vq.add_(self.h, self.proj)
-            vq.rmsnorm(self.h, out=self.a)
-            self._qmm(self.a, lay["gate_up"], self.gu)
-            vq.silu_mul(self.gu, out=self.act)
-            self._qmm(self.act, lay["down"], self.proj)
-            vq.add_(self.h, self.proj)
+            self._qmm(c, lay["o"], self.h, epilogue=vq.VQ_EPI_RESIDUAL, y_sumsq=self.ss)
+            self._qmm(self.h, lay["gate_up"], self.act, norm=True, epilogue=vq.VQ_EPI_SWIGLU)
+            self._qmm(self.act, lay["down"], self.h, epilogue=vq.VQ_EPI_RESIDUAL, y_sumsq=self.ss)
         return self.h
 
     def step(self, h_in, draft_logits, drafts, uniforms):
@@ -178,8 +182,7 @@ class DenseVerifyStack:
         """
         cfg = self.cfg
         self.forward_hidden(h_in)
-        vq.rmsnorm(self.h, out=self.a)
-        self._qmm(self.a, self.w.lm_head, self.logits[0])
+        self._qmm(self.h, self.w.lm_head, self.logits[0], norm=True)
         vq.spec_accept(self.logits, draft_logits, drafts, uniforms, logits=True, temperature=cfg.temperature,
                        top_k=cfg.top_k, top_p=cfg.top_p, probs_out=self.probs, out_tokens=self.tokens,
                        out_n=self.n_acc, workspace=self._wsv("accept"))
@@ -187,7 +190,7 @@ class DenseVerifyStack:
 
     def bytes_per_step(self) -> dict:
         """Algorithmic HBM bytes of one step: weights once, KV (K and V) once per
-        attention layer, and the logits/probability rows of the acceptance step."""
+        attention layer, and the logit rows of the acceptance step."""
         cfg = self.cfg
         T = cfg.ctx + cfg.M
         kv = cfg.n_attn * 4 * cfg.Hkv * T * cfg.D

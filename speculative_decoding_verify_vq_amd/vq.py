@@ -22,6 +22,7 @@ lib = ctypes.CDLL(LIB_PATH)
 VQ_OK, VQ_ERR_INVALID_ARG, VQ_ERR_HIP, VQ_ERR_UNSUPPORTED_DEVICE = 0, 1, 2, 3
 VQ_BF16, VQ_F32 = 0, 1
 VQ_PROBS, VQ_LOGITS = 0, 1
+VQ_EPI_STORE, VQ_EPI_RESIDUAL, VQ_EPI_SWIGLU = 0, 1, 2
 
 _c = ctypes
 _P, _I, _I64, _F, _SZ = _c.c_void_p, _c.c_int, _c.c_int64, _c.c_float, _c.c_size_t
@@ -38,6 +39,13 @@ _proto("vq_last_error", _c.c_char_p, [])
 _proto("vq_version", _c.c_char_p, [])
 _proto("vq_skinny_qmm_workspace", _SZ, [_I, _I, _I, _I, _I])
 _proto("vq_skinny_qmm", _I, [_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I64, _I, _P, _SZ, _P])
+_proto("vq_qmm_pack_bytes", _SZ, [_I, _I, _I, _I])
+_proto("vq_qmm_pack", _I, [_P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P])
+_proto("vq_sumsq_parts", _I, [_I])
+_proto("vq_qmm_packed_workspace", _SZ, [_I, _I, _I, _I, _I])
+_proto("vq_qmm_packed", _I, [_P, _I64, _P, _I, _F, _P, _I, _I, _I, _I, _I, _I, _P, _I64, _P, _I64, _I, _P, _P, _SZ,
+                             _P])
+_proto("vq_row_sumsq_bf16", _I, [_P, _I64, _I, _I, _P, _P])
 _proto("vq_multirow_attn_workspace", _SZ, [_I, _I, _I, _I, _I])
 _proto("vq_multirow_attn", _I, [_P, _I64, _P, _P, _I64, _I, _I, _I, _I, _I, _F, _P, _I64, _P, _SZ, _P])
 _proto("vq_spec_accept_workspace", _SZ, [_I, _I, _I, _I, _I64, _I64])
@@ -143,6 +151,65 @@ def skinny_qmm(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: 
                            group_size, M, N, K, out.data_ptr(), out.stride(0), y_dtype, _ptr(ws), wsz,
                            _stream(stream))
     _check("vq_skinny_qmm", rc)
+    return out
+
+
+def qmm_pack_bytes(bits: int, N: int, K: int, group_size: int = 64) -> int:
+    return int(lib.vq_qmm_pack_bytes(bits, group_size, N, K))
+
+
+def qmm_pack(wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int, N: int, K: int,
+             group_size: int = 64, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The tiled pack of a row-major weight (uint8 device tensor; see vq_qmm_pack in include/vq.h)."""
+    nbytes = qmm_pack_bytes(bits, N, K, group_size)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=wq.device)
+    rc = lib.vq_qmm_pack(wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), bits, group_size, N, K,
+                         out.data_ptr(), out.numel() * out.element_size(), _stream(stream))
+    _check("vq_qmm_pack", rc)
+    return out
+
+
+def sumsq_parts(N: int) -> int:
+    return int(lib.vq_sumsq_parts(N))
+
+
+def qmm_packed_workspace_bytes(bits: int, M: int, N: int, K: int, group_size: int = 64) -> int:
+    return int(lib.vq_qmm_packed_workspace(bits, group_size, M, N, K))
+
+
+def qmm_packed(x: torch.Tensor, packed: torch.Tensor, bits: int, N: int, K: int, *, group_size: int = 64,
+               x_sumsq: torch.Tensor | None = None, eps: float = 1e-6, epilogue: int = VQ_EPI_STORE,
+               residual: torch.Tensor | None = None, out: torch.Tensor | None = None,
+               out_dtype: torch.dtype = torch.bfloat16, y_sumsq: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """QMM on a tiled pack with the fused RMSNorm prologue and store / residual /
+    SwiGLU epilogues (see vq_qmm_packed in include/vq.h). x_sumsq, y_sumsq are
+    float32 [M, sumsq_parts(.)] tensors."""
+    M = x.shape[0]
+    n_out = N // 2 if epilogue == VQ_EPI_SWIGLU else N
+    if out is None:
+        out = torch.empty((M, n_out), dtype=out_dtype, device=x.device)
+    y_dtype = VQ_F32 if out.dtype == torch.float32 else VQ_BF16
+    need = qmm_packed_workspace_bytes(bits, M, N, K, group_size)
+    ws = _ws(need, x.device, workspace, "qmm_packed")
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    parts = 0 if x_sumsq is None else x_sumsq.shape[-1]
+    rc = lib.vq_qmm_packed(x.data_ptr(), x.stride(0), _ptr(x_sumsq), parts, eps, packed.data_ptr(), bits,
+                           group_size, M, N, K, epilogue, _ptr(residual),
+                           0 if residual is None else residual.stride(0), out.data_ptr(), out.stride(0), y_dtype,
+                           _ptr(y_sumsq), _ptr(ws), wsz, _stream(stream))
+    _check("vq_qmm_packed", rc)
+    return out
+
+
+def row_sumsq(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """float32 [M, ceil(N / 128)] sums of squares of x [M, N] per 128 columns (see include/vq_glue.h)."""
+    M, N = x.shape
+    if out is None:
+        out = torch.empty((M, sumsq_parts(N)), dtype=torch.float32, device=x.device)
+    rc = lib.vq_row_sumsq_bf16(x.data_ptr(), x.stride(0), M, N, out.data_ptr(), _stream(stream))
+    _check("vq_row_sumsq_bf16", rc)
     return out
 
 

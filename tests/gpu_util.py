@@ -37,3 +37,30 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, what: str = "") -> None:
     err = np.abs(gpu - ref)
     worst = float(err.max())
     assert worst <= tol, f"{what}: max |gpu - oracle| = {worst:.3e} > tol {tol:.3e}"
+
+
+def interleave_gate_up(wg: dict, wu: dict) -> dict:
+    """Rows of [gate; up] regrouped per 64 outputs (gate rows 64c..64c+63, then the
+    matching up rows), the row order the SwiGLU epilogue of vq_qmm_packed expects."""
+    I, K, bits = wg["N"], wg["K"], wg["bits"]
+    G = K // 64
+    out = {}
+    for key, width in (("wq", K * bits // 32), ("scales", G), ("biases", G)):
+        g = np.asarray(wg[key]).reshape(I, width)
+        u = np.asarray(wu[key]).reshape(I, width)
+        blocks = [np.concatenate([g[64 * c: 64 * c + 64], u[64 * c: 64 * c + 64]]) for c in range(I // 64)]
+        out[key] = np.ascontiguousarray(np.concatenate(blocks))
+    out.update(N=2 * I, K=K, bits=bits, group_size=64)
+    return out
+
+
+def stack_gate_up(wg: dict, wu: dict) -> dict:
+    """The [gate; up] matrix of the oracle composition (gate rows first)."""
+    I, K, bits = wg["N"], wg["K"], wg["bits"]
+    G = K // 64
+    out = {}
+    for key, width in (("wq", K * bits // 32), ("scales", G), ("biases", G)):
+        out[key] = np.ascontiguousarray(np.concatenate([np.asarray(wg[key]).reshape(I, width),
+                                                        np.asarray(wu[key]).reshape(I, width)]))
+    out.update(N=2 * I, K=K, bits=bits, group_size=64)
+    return out

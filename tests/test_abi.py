@@ -111,3 +111,50 @@ def test_workspace_queries_are_pure(vqmod):
     assert vq.attn_workspace_bytes(4, 2, 2, 64, 256) >= 0
     assert vq.accept_workspace_bytes(1, 3, 1000, 0, 0, 0) > 0
     assert vq.accept_workspace_bytes(1, 3, 1000, 1, 0, 0) > vq.accept_workspace_bytes(1, 3, 1000, 0, 0, 0)
+
+
+def _packed(vq, **kw):
+    a = dict(x=A16, ldx=1024, ss=None, parts=0, eps=1e-6, pk=A16, bits=4, gs=64, M=4, N=512, K=1024, epi=0,
+             r=None, ldr=0, y=A16, ldy=512, yd=0, yss=None, ws=A16, wsz=1 << 30)
+    a.update(kw)
+    return vq.lib.vq_qmm_packed(a["x"], a["ldx"], a["ss"], a["parts"], a["eps"], a["pk"], a["bits"], a["gs"],
+                                a["M"], a["N"], a["K"], a["epi"], a["r"], a["ldr"], a["y"], a["ldy"], a["yd"],
+                                a["yss"], a["ws"], a["wsz"], None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(x=None), dict(pk=None), dict(y=None), dict(bits=2), dict(gs=128), dict(M=0), dict(M=17), dict(K=100),
+    dict(ldx=1020), dict(x=A16 + 8), dict(pk=A16 + 8), dict(ss=A16, parts=0), dict(ss=A16, parts=257),
+    dict(ss=A16, parts=4, eps=-1.0), dict(ss=A16, parts=4, eps=float("nan")), dict(ss=A16 + 2, parts=4),
+    dict(epi=3), dict(epi=-1), dict(yd=5), dict(ldy=100), dict(yss=A16),
+    dict(epi=1), dict(epi=1, r=A16, ldr=100), dict(epi=1, r=A16, ldr=512, yd=1), dict(epi=1, r=A16, ldr=1024),
+    dict(epi=1, r=A16 + 1, ldr=512), dict(epi=1, r=A16, ldr=512, yss=A16 + 2),
+    dict(epi=2, N=500), dict(epi=2, ldy=100), dict(epi=2, yd=1), dict(epi=2, yss=A16),
+    dict(ws=None, N=64, K=8192), dict(wsz=16, N=64, K=8192),
+])
+def test_packed_rejects(vqmod, bad):
+    assert _packed(vqmod, **bad) == vqmod.VQ_ERR_INVALID_ARG
+    assert vqmod.last_error()
+
+
+@pytest.mark.parametrize("bad", [
+    dict(wq=None), dict(out=None), dict(bits=5), dict(gs=32), dict(K=70), dict(N=0), dict(nbytes=16),
+    dict(wq=A16 + 4), dict(out=A16 + 8),
+])
+def test_pack_rejects(vqmod, bad):
+    a = dict(wq=A16, s=A16, b=A16, bits=4, gs=64, N=512, K=1024, out=A16, nbytes=1 << 30)
+    a.update(bad)
+    rc = vqmod.lib.vq_qmm_pack(a["wq"], a["s"], a["b"], a["bits"], a["gs"], a["N"], a["K"], a["out"], a["nbytes"],
+                               None)
+    assert rc == vqmod.VQ_ERR_INVALID_ARG
+
+
+def test_pack_sizes(vqmod):
+    vq = vqmod
+    # 4-bit: 32-row tiles x 256-input blocks of 4608 bytes; 8-bit: 128-input blocks of 4352 bytes
+    assert vq.qmm_pack_bytes(4, 512, 1024) == 16 * 4 * 4608
+    assert vq.qmm_pack_bytes(4, 500, 1088) == 16 * 5 * 4608      # ragged N and K are zero-padded
+    assert vq.qmm_pack_bytes(8, 512, 1024) == 16 * 8 * 4352
+    assert vq.qmm_pack_bytes(4, 512, 100) == 0
+    assert vq.sumsq_parts(5120) == 40 and vq.sumsq_parts(129) == 2
+    assert vq.qmm_packed_workspace_bytes(4, 4, 8192, 5120) > 0

@@ -1,0 +1,82 @@
+"""The dense verify step composed from the library's kernels (fused RMSNorm,
+residual and SwiGLU around the packed QMM, KV append, multi-row attention,
+float32 lm_head, exact acceptance in logits mode) against the oracle
+composition of the same reduced stack."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.accept as oacc
+import oracle.stack as ostack
+from speculative_decoding_verify_vq_amd.stack import DenseVerifyStack, QPack, StackConfig, StackWeights
+from synth import accept_logits, attn_inputs, qmm_activations, qmm_weights, uniforms24
+from tests.gpu_util import (assert_close, bf16_tensor, f32_tensor, i32_tensor, interleave_gate_up, stack_gate_up,
+                            to_f64, words_tensor)
+
+pytestmark = pytest.mark.gpu
+
+
+def _pack(w):
+    return QPack.from_rows(words_tensor(w["wq"]), bf16_tensor(w["scales"]), bf16_tensor(w["biases"]), w["bits"],
+                           w["N"], w["K"])
+
+
+@pytest.mark.parametrize("bits,M,layers", [(4, 4, 4), (8, 8, 2), (4, 1, 2), (4, 16, 2)])
+def test_stack_step_matches_oracle(vq, bits, M, layers):
+    cfg = StackConfig(layers=layers, hidden=512, inter=1024, Hq=4, Hkv=2, D=64, vocab=1000, bits=bits, lm_bits=bits,
+                      attn_every=2, ctx=64, M=M, temperature=0.8, top_k=0, top_p=0.9)
+    sh = cfg.shapes()
+    T_cap = cfg.ctx + M + 4
+    gpu_w, ora_w = StackWeights(), []
+    for li in range(layers):
+        lw, lo = {}, {}
+        for j, name in enumerate(("qkv", "o", "down")):
+            N, K = sh[name]
+            w = qmm_weights(30, N, K, bits, layer=10 * li + j)
+            lw[name], lo[name] = _pack(w), w
+        wg = qmm_weights(30, cfg.inter, cfg.hidden, bits, layer=10 * li + 7)
+        wu = qmm_weights(30, cfg.inter, cfg.hidden, bits, layer=10 * li + 8)
+        lw["gate_up"], lo["gate_up"] = _pack(interleave_gate_up(wg, wu)), stack_gate_up(wg, wu)
+        gpu_w.layers.append(lw)
+        ora_w.append(lo)
+    wl = qmm_weights(30, cfg.vocab, cfg.hidden, bits, layer=999)
+    gpu_w.lm_head = _pack(wl)
+    kv = []
+    for a in range(cfg.n_attn):
+        _, k, v = attn_inputs(30, M, cfg.Hq, cfg.Hkv, cfg.D, T_cap, extra=a)
+        gpu_w.k_cache.append(bf16_tensor(k))
+        gpu_w.v_cache.append(bf16_tensor(v))
+        kv.append({"k": to_f64(bf16_tensor(k)), "v": to_f64(bf16_tensor(v))})
+    hb = qmm_activations(30, M, cfg.hidden)
+    K = M - 1
+    _, ql = accept_logits(30, max(K, 1), cfg.vocab)
+    ql = ql[:K]
+    drafts = np.array([[int(np.argmax(ql[i])) for i in range(K)]], dtype=np.int32).reshape(1, K)
+    us = uniforms24(30, (1, K + 1))
+
+    st = DenseVerifyStack(cfg, gpu_w)
+    toks, n = st.step(bf16_tensor(hb), f32_tensor(ql[None]).reshape(1, K, cfg.vocab), i32_tensor(drafts),
+                      f32_tensor(us))
+    torch.cuda.synchronize()
+
+    # oracle composition on the same weights and caches
+    h = to_f64(bf16_tensor(hb))
+    ai = 0
+    for li in range(layers):
+        attn = cfg.is_attn(li)
+        h = ostack.layer_forward(h, ora_w[li], attn, kv[ai] if attn else None, cfg.ctx, cfg.Hq, cfg.Hkv, cfg.D,
+                                 cfg.inter)
+        ai += int(attn)
+    assert_close(to_f64(st.h), h, "final hidden rows")
+    for a in range(cfg.n_attn):
+        rows = slice(cfg.ctx, cfg.ctx + M)
+        assert_close(to_f64(gpu_w.k_cache[a][:, rows]), kv[a]["k"][:, rows], f"appended keys {a}")
+        assert_close(to_f64(gpu_w.v_cache[a][:, rows]), kv[a]["v"][:, rows], f"appended values {a}")
+    logits = ostack.lm_head_logits(h, wl)
+    assert_close(to_f64(st.logits[0]), logits, "lm_head logits")
+    # exact acceptance on the device's own probabilities
+    probs = st.probs[0].cpu().numpy()
+    P, Q = probs[: K + 1], probs[K + 1:]
+    assert_close(P.astype(np.float64), oacc.softmax_f64(st.logits[0].cpu().numpy(), cfg.temperature), "probs")
+    rt, rn = oacc.spec_accept(P, Q, list(drafts[0]), us[0], cfg.top_k, cfg.top_p)
+    assert list(toks[0].cpu().numpy()) == rt and int(n[0]) == rn
