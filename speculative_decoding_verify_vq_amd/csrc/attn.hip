@@ -11,7 +11,7 @@
 // byte is read from HBM once per call.
 //
 // Per 32-key tile:
-//   * the tile is loaded with coalesced 16-byte loads into registers one tile
+//   * the tile is loaded with coalesced 16-byte loads into registers two tiles
 //     ahead, then written to LDS row-major;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q rows
 //     from LDS); in the output layout each lane holds 16 keys of one query row,
@@ -97,24 +97,37 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
 
   const uint16_t* kh = kc + (size_t)kvh * kv_head_stride;
   const uint16_t* vh = vc + (size_t)kvh * kv_head_stride;
-  uint4 kr[C::PER_THREAD], vr[C::PER_THREAD];
-  auto fetch = [&](int t0) {
+  // Two K/V tiles in flight (register sets 0 and 1). The loads are issued
+  // unconditionally (key clamped into the range, values past it masked later),
+  // so the wait counts the compiler derives stay exact.
+  struct KV {
+    u32x4 k[C::PER_THREAD], v[C::PER_THREAD];
+  };
+  KV r0, r1;
+  auto fetch = [&](KV& r, int t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < C::PER_THREAD; ++e) {
       const int u = tid + e * kThreads;
-      kr[e] = make_uint4(0, 0, 0, 0);
-      vr[e] = make_uint4(0, 0, 0, 0);
-      if (u < C::UNITS) {
-        const int key = t0 + u / (D / 8);
-        const int dc = u % (D / 8);
-        if (key < j1) {
-          kr[e] = *reinterpret_cast<const uint4*>(kh + (size_t)key * D + dc * 8);
-          vr[e] = *reinterpret_cast<const uint4*>(vh + (size_t)key * D + dc * 8);
-        }
-      }
+      const int key = min(t0 + u / (D / 8), j1 - 1);
+      const int dc = u % (D / 8);
+      r.k[e] = *reinterpret_cast<const u32x4*>(kh + (size_t)key * D + dc * 8);
+      r.v[e] = *reinterpret_cast<const u32x4*>(vh + (size_t)key * D + dc * 8);
     }
   };
-  if (j0 < j1) fetch(j0);
+  auto stage = [&](const KV& r) __attribute__((always_inline)) {
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < C::PER_THREAD; ++e) {
+      const int u = tid + e * kThreads;
+      const int key = u / (D / 8);
+      const int dc = u % (D / 8);
+      *reinterpret_cast<u32x4*>(&k_lds[key * C::LD + dc * 8]) = r.k[e];
+      *reinterpret_cast<u32x4*>(&v_lds[key * C::LD + dc * 8]) = r.v[e];
+    }
+    __syncthreads();
+  };
+  if (j0 < j1) fetch(r0, j0);
+  if (j0 + kTileKeys < j1) fetch(r1, j0 + kTileKeys);
 
   const int rt = wave / C::DS;
   const int dpart = wave % C::DS;
@@ -129,21 +142,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
 #pragma unroll
   for (int t = 0; t < C::DT; ++t) o[t] = f32x16{};
 
-  for (int t0 = j0; t0 < j1; t0 += kTileKeys) {
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < C::PER_THREAD; ++e) {
-      const int u = tid + e * kThreads;
-      if (u < C::UNITS) {
-        const int key = u / (D / 8);
-        const int dc = u % (D / 8);
-        *reinterpret_cast<uint4*>(&k_lds[key * C::LD + dc * 8]) = kr[e];
-        *reinterpret_cast<uint4*>(&v_lds[key * C::LD + dc * 8]) = vr[e];
-      }
-    }
-    __syncthreads();
-    if (t0 + kTileKeys < j1) fetch(t0 + kTileKeys);
-    if (!active) continue;
+  auto tile = [&](int t0) __attribute__((always_inline)) {
+    if (!active) return;
 
     // S^T[key][row] = sum_d K[key][d] Q[row][d]
     f32x16 s = {};
@@ -207,6 +207,17 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
         const bf16x8 a = __builtin_bit_cast(bf16x8, aw);
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, c ? pb1 : pb0, o[t], 0, 0, 0);
       }
+    }
+  };
+  static_assert(C::UNITS % kThreads == 0, "every thread moves whole 16-byte units of a tile");
+  for (int t0 = j0; t0 < j1; t0 += 2 * kTileKeys) {
+    stage(r0);
+    if (t0 + 2 * kTileKeys < j1) fetch(r0, t0 + 2 * kTileKeys);
+    tile(t0);
+    if (t0 + kTileKeys < j1) {
+      stage(r1);
+      if (t0 + 3 * kTileKeys < j1) fetch(r1, t0 + 3 * kTileKeys);
+      tile(t0 + kTileKeys);
     }
   }
 
@@ -340,10 +351,10 @@ AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T) {
   AttnPlan p{};
   p.rows = M * (Hq / Hkv);
   p.row_tiles = (p.rows + 31) / 32;
-  // Up to two workgroups per compute unit, at least 256 keys per range.
+  // About two workgroups per compute unit, at least 128 keys per range.
   const int tiles = (T + kTileKeys - 1) / kTileKeys;
   int s = (2 * kNumCU + Hkv - 1) / Hkv;
-  int max_s = (tiles + 7) / 8;
+  int max_s = (tiles + 3) / 4;
   s = s > max_s ? max_s : s;
   s = s < 1 ? 1 : s;
   const int tiles_per = (tiles + s - 1) / s;

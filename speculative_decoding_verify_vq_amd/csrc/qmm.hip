@@ -295,8 +295,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
         }
       }
     }
-    // The first code blocks go out after the x loads, so that waiting for
-    // those (in-order counter) leaves the code blocks in flight.
+    // x is waited for before the first code blocks go out: issued together, its
+    // few lines would queue behind the burst of code requests of every
+    // workgroup at the start of the kernel.
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int i = 0; i < kInFlight; ++i) issue(R[i], i);
     if constexpr (NORM) {
@@ -517,12 +519,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     s_last = __hip_atomic_fetch_add(&a.counters[cb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.splits - 1;
   __syncthreads();
   if (!s_last) return;
-  // Sum the partials in split order, 4 splits x kVPT loads in flight per thread.
-  // Thread t, value i covers element t + i * 256 of the block's [M][128] (store,
-  // residual) or of its [M][64] gate/up column pairs (SwiGLU).
+  // Sum the partials in split order, kBatch splits x kVPT x kPair loads in
+  // flight per thread (32 or fewer). Thread t, value i covers element t + i * 256
+  // of the block's [M][128] (store, residual) or of its [M][64] gate/up column
+  // pairs (SwiGLU).
   constexpr int kCols = EPI == kEpiSwiGLU ? kColsWG / 2 : kColsWG;
   constexpr int kVPT = MT * kCols / kThreads;
   constexpr int kPair = EPI == kEpiSwiGLU ? 2 : 1;
+  constexpr int kBatch = 32 / (kVPT * kPair);
   float v[kVPT][kPair];
   size_t idx[kVPT];
   bool ok[kVPT];
@@ -537,10 +541,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     for (int h = 0; h < kPair; ++h) v[i][h] = 0.f;
   }
   const size_t sstride = (size_t)M * N;
-  for (int sp = 0; sp < a.splits; sp += 4) {
-    float pv[4][kVPT][kPair];
+  for (int sp = 0; sp < a.splits; sp += kBatch) {
+    float pv[kBatch][kVPT][kPair];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
 #pragma unroll
       for (int i = 0; i < kVPT; ++i) {
 #pragma unroll
@@ -552,7 +556,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
 #pragma unroll
       for (int i = 0; i < kVPT; ++i) {
 #pragma unroll
