@@ -194,6 +194,21 @@ int vq_multirow_attn(const void* q, int64_t q_row_stride, const void* k_cache,
                      int D, int T, float scale, void* out, int64_t out_row_stride,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same attention with the append of the M verify rows fused in: the rows
+ * k_new[m, h*D .. (h+1)*D) and v_new[m, ...] (m < M, KV head h, rows
+ * new_row_stride elements apart, >= Hkv * D and a multiple of 8, 16-byte
+ * aligned) become cache positions T-M+m of KV head h — the append-only cache
+ * of the full-attention layers (page "The fastest way to run local LLMs on a
+ * Mac", section "Why token 1,000 is faster than token 100,000") — and the
+ * attention over the T keys uses them. The caches are written (rows T-M ..
+ * T-1 only); everything else is as vq_multirow_attn, with the same
+ * workspace. k_new and v_new must not overlap the caches. */
+int vq_multirow_attn_append(const void* q, int64_t q_row_stride, const void* k_new,
+                            const void* v_new, int64_t new_row_stride, void* k_cache,
+                            void* v_cache, int64_t kv_head_stride, int M, int Hq, int Hkv,
+                            int D, int T, float scale, void* out, int64_t out_row_stride,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Exact speculative acceptance
  *

@@ -62,10 +62,10 @@ struct AttnCfg {
 
 template <int D, int RT>
 __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
-    const uint16_t* __restrict__ q, int64_t q_rs, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, int64_t kv_head_stride, int M, int Hq, int Hkv, int T, float scale_log2,
-    int keys_per_split, int splits, uint16_t* __restrict__ out, int64_t out_rs, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    const uint16_t* __restrict__ q, int64_t q_rs, const uint16_t* kc, const uint16_t* vc, int64_t kv_head_stride,
+    int M, int Hq, int Hkv, int T, float scale_log2, int keys_per_split, int splits, uint16_t* __restrict__ out,
+    int64_t out_rs, float* __restrict__ part_o, float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, int64_t new_rs, uint16_t* kc_w, uint16_t* vc_w) {
   using C = AttnCfg<D, RT>;
   __shared__ uint16_t q_lds[RT * 32 * C::LD];
   __shared__ uint16_t k_lds[kTileKeys * C::LD];
@@ -110,8 +110,14 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
       const int u = tid + e * kThreads;
       const int key = min(t0 + u / (D / 8), j1 - 1);
       const int dc = u % (D / 8);
-      r.k[e] = *reinterpret_cast<const u32x4*>(kh + (size_t)key * D + dc * 8);
-      r.v[e] = *reinterpret_cast<const u32x4*>(vh + (size_t)key * D + dc * 8);
+      const uint16_t* ks = kh + (size_t)key * D;
+      const uint16_t* vs = vh + (size_t)key * D;
+      if (k_new && key >= T - M) {  // a row being appended: read it from its source
+        ks = k_new + (size_t)(key - (T - M)) * new_rs + (size_t)kvh * D;
+        vs = v_new + (size_t)(key - (T - M)) * new_rs + (size_t)kvh * D;
+      }
+      r.k[e] = *reinterpret_cast<const u32x4*>(ks + dc * 8);
+      r.v[e] = *reinterpret_cast<const u32x4*>(vs + dc * 8);
     }
   };
   auto stage = [&](const KV& r) __attribute__((always_inline)) {
@@ -126,6 +132,19 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     }
     __syncthreads();
   };
+  // Append: the rows T-M .. T-1 that fall in this key range are copied from
+  // their source into the caches (every row is in exactly one range).
+  if (k_new) {
+    const int a0 = max(j0, T - M), a1 = j1;
+    for (int u = tid; u < (a1 - a0) * (D / 8); u += kThreads) {
+      const int key = a0 + u / (D / 8);
+      const int dc = u % (D / 8);
+      const size_t src = (size_t)(key - (T - M)) * new_rs + (size_t)kvh * D + dc * 8;
+      const size_t dst = (size_t)kvh * kv_head_stride + (size_t)key * D + dc * 8;
+      *reinterpret_cast<u32x4*>(kc_w + dst) = *reinterpret_cast<const u32x4*>(k_new + src);
+      *reinterpret_cast<u32x4*>(vc_w + dst) = *reinterpret_cast<const u32x4*>(v_new + src);
+    }
+  }
   if (j0 < j1) fetch(r0, j0);
   if (j0 + kTileKeys < j1) fetch(r1, j0 + kTileKeys);
 
@@ -367,7 +386,13 @@ AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T) {
 
 hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const void* k, const void* v,
                        int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T, float scale,
-                       void* out, int64_t out_rs, void* workspace, hipStream_t stream) {
+                       void* out, int64_t out_rs, void* workspace, hipStream_t stream, const void* k_new,
+                       const void* v_new, int64_t new_rs) {
+  auto* kn = reinterpret_cast<const uint16_t*>(k_new);
+  auto* vn = reinterpret_cast<const uint16_t*>(v_new);
+  // With an append the caches are written (rows T-M .. T-1) as well as read.
+  auto* kw = k_new ? const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(k)) : nullptr;
+  auto* vw = k_new ? const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(v)) : nullptr;
   float* part_o = reinterpret_cast<float*>(workspace);
   float* part_ml = plan.splits > 1
                        ? part_o + (size_t)plan.splits * Hkv * plan.rows * D
@@ -381,7 +406,7 @@ hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const 
 #define VQ_ATTN(DV, RTV)                                                                        \
   hipLaunchKernelGGL((attn_partial_kernel<DV, RTV>), grid, dim3(kThreads), 0, stream, qp, q_rs, kp, vp, \
                      kv_head_stride, M, Hq, Hkv, T, sl2, plan.keys_per_split, plan.splits, op,         \
-                     out_rs, part_o, part_ml)
+                     out_rs, part_o, part_ml, kn, vn, new_rs, kw, vw)
 #define VQ_ATTN_RT(DV)                         \
   switch (plan.row_tiles) {                    \
     case 1: VQ_ATTN(DV, 1); break;             \

@@ -540,6 +540,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
     for (int h = 0; h < kPair; ++h) v[i][h] = 0.f;
   }
+  // The residual rows go out with the first batch of partial loads.
+  uint32_t rv[EPI == kEpiResidual ? kVPT : 1];
+  if constexpr (EPI == kEpiResidual) {
+#pragma unroll
+    for (int i = 0; i < kVPT; ++i) {
+      const int t = tid + i * kThreads;
+      rv[i] = ok[i] ? a.res[(size_t)(t / kCols) * a.ldr + cb * kColsWG + t % kCols] : 0u;
+    }
+  }
   const size_t sstride = (size_t)M * N;
   for (int sp = 0; sp < a.splits; sp += kBatch) {
     float pv[kBatch][kVPT][kPair];
@@ -578,7 +587,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
       const int t = tid + i * kThreads;
       float sq = 0.f;
       if (ok[i]) {
-        const float h = residual(t / kCols, cb * kColsWG + t % kCols, v[i][0]);
+        const int col = cb * kColsWG + t % kCols;
+        const float h = round_bf16(bf16_bits_to_f32(rv[i]) + round_bf16(v[i][0]));
+        yb[(size_t)(t / kCols) * a.ldy + col] = f32_to_bf16_rne(h);
         sq = h * h;
       }
       if (a.y_ss) {

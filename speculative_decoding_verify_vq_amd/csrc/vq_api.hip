@@ -282,6 +282,39 @@ int vq_multirow_attn(const void* q, int64_t q_row_stride, const void* k_cache, c
   return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_multirow_attn launch");
 }
 
+int vq_multirow_attn_append(const void* q, int64_t q_row_stride, const void* k_new, const void* v_new,
+                            int64_t new_row_stride, void* k_cache, void* v_cache, int64_t kv_head_stride, int M,
+                            int Hq, int Hkv, int D, int T, float scale, void* out, int64_t out_row_stride,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!k_new || !v_new) return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: NULL k_new or v_new");
+  if (new_row_stride < (int64_t)Hkv * D || new_row_stride % 8 != 0)
+    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: new_row_stride must be >= Hkv*D and a multiple of 8");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: k_new and v_new must be 16-byte aligned");
+  if (!q || !k_cache || !v_cache || !out)
+    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: NULL data pointer");
+  if (!attn_shape_ok(M, Hq, Hkv, D, T))
+    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: unsupported shape M=%d Hq=%d Hkv=%d D=%d T=%d", M, Hq,
+                Hkv, D, T);
+  if (kv_head_stride < (int64_t)T * D || kv_head_stride % 8 != 0)
+    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: kv_head_stride must be >= T*D and a multiple of 8");
+  if (q_row_stride < (int64_t)Hq * D || q_row_stride % 8 != 0 || out_row_stride < (int64_t)Hq * D ||
+      out_row_stride % 8 != 0)
+    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: row strides must be >= Hq*D and multiples of 8");
+  if (!isfinite(scale)) return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: scale must be finite");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: q, caches and out must be 16-byte aligned");
+  const vq::AttnPlan plan = vq::attn_plan(M, Hq, Hkv, D, T);
+  int rc = check_workspace(workspace, workspace_bytes, plan.partial_bytes);
+  if (rc) return rc;
+  if ((rc = check_device())) return rc;
+  hipError_t e = vq::attn_launch(plan, q, q_row_stride, k_cache, v_cache, kv_head_stride, M, Hq, Hkv, D, T, scale,
+                                 out, out_row_stride, workspace, reinterpret_cast<hipStream_t>(stream), k_new, v_new,
+                                 new_row_stride);
+  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_multirow_attn_append launch");
+}
+
 // ----------------------------------------------------------- acceptance
 size_t vq_spec_accept_workspace(int B, int K, int V, int input_kind, int64_t p_batch_stride,
                                 int64_t q_batch_stride) {

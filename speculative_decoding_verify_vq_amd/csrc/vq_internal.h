@@ -66,9 +66,13 @@ struct AttnPlan {
   size_t partial_bytes;
 };
 AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T);
+// k_new / v_new (nullable): the M rows appended at positions T-M .. T-1, rows
+// new_rs elements apart, KV head h at offset h*D; they are written into the
+// caches and read from their source by the attention itself.
 hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const void* k, const void* v,
                        int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T, float scale,
-                       void* out, int64_t out_rs, void* workspace, hipStream_t stream);
+                       void* out, int64_t out_rs, void* workspace, hipStream_t stream,
+                       const void* k_new = nullptr, const void* v_new = nullptr, int64_t new_rs = 0);
 
 // ---------------------------------------------------------- acceptance
 struct AcceptPlan {

@@ -8,8 +8,8 @@ Per layer, with h the bf16 residual stream and S its per-row sums of squares
 (per 128 columns):
 
     qkv = qmm(rms(h), W_qkv)                         RMSNorm fused into the staging of x
-    attention layers: append k, v at positions ctx .. ctx+M-1, then
-          c = multirow_attn(q, K cache, V cache, T = ctx + M)
+    attention layers: c = multirow_attn(q, K cache, V cache, T = ctx + M), which
+          appends k, v at positions ctx .. ctx+M-1 itself
     other layers (their recurrent state is out of scope): c = q
     h, S = h + qmm(c, W_o)                           residual epilogue, writes S
     act  = swiglu(qmm(rms(h), W_gate_up))            gate|up rows interleaved per 64 outputs
@@ -162,10 +162,12 @@ class DenseVerifyStack:
             if cfg.is_attn(li):
                 kc, vc = self.w.k_cache[ai], self.w.v_cache[ai]
                 ai += 1
-                vq.kv_append(self.qkv, cfg.q_width, cfg.q_width + cfg.Hkv * cfg.D, kc, vc, cfg.ctx)
                 qv = q.as_strided((cfg.M, cfg.Hq, cfg.D), (self.qkv.stride(0), cfg.D, 1))
                 ov = self.ctx_out.view(cfg.M, cfg.Hq, cfg.D)
-                vq.multirow_attn(qv, kc, vc, cfg.ctx + cfg.M, cfg.D ** -0.5, out=ov, workspace=self._wsv("attn"))
+                k_new = self.qkv[:, cfg.q_width: cfg.q_width + cfg.Hkv * cfg.D]
+                v_new = self.qkv[:, cfg.q_width + cfg.Hkv * cfg.D:]
+                vq.multirow_attn(qv, kc, vc, cfg.ctx + cfg.M, cfg.D ** -0.5, out=ov, workspace=self._wsv("attn"),
+                                 k_new=k_new, v_new=v_new)
                 c = self.ctx_out
             else:
                 c = q

@@ -158,3 +158,17 @@ def test_pack_sizes(vqmod):
     assert vq.qmm_pack_bytes(4, 512, 100) == 0
     assert vq.sumsq_parts(5120) == 40 and vq.sumsq_parts(129) == 2
     assert vq.qmm_packed_workspace_bytes(4, 4, 8192, 5120) > 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(kn=None), dict(vn=None), dict(nrs=100), dict(nrs=132), dict(kn=A16 + 8), dict(q=None), dict(T=3),
+    dict(hs=256 * 64 - 8), dict(scale=float("nan")), dict(ws=None, T=100000),
+])
+def test_attn_append_rejects(vqmod, bad):
+    a = dict(q=A16, qrs=128, kn=A16, vn=A16, nrs=128, k=A16, v=A16, hs=256 * 64, M=4, Hq=2, Hkv=2, D=64, T=256,
+             scale=0.125, out=A16, ors=128, ws=A16, wsz=1 << 30)
+    a.update(bad)
+    rc = vqmod.lib.vq_multirow_attn_append(a["q"], a["qrs"], a["kn"], a["vn"], a["nrs"], a["k"], a["v"], a["hs"],
+                                           a["M"], a["Hq"], a["Hkv"], a["D"], a["T"], a["scale"], a["out"],
+                                           a["ors"], a["ws"], a["wsz"], None)
+    assert rc == vqmod.VQ_ERR_INVALID_ARG

@@ -57,3 +57,41 @@ def test_deterministic(vq):
     a = _run(vq, q, k, v, 8200, 1 / 16)
     for _ in range(2):
         assert np.array_equal(a, _run(vq, q, k, v, 8200, 1 / 16))
+
+
+@pytest.mark.parametrize("M,Hq,Hkv,D,T,T_cap", [
+    (4, 2, 2, 64, 256, 260),       # config 0 with the append
+    (8, 4, 2, 64, 1026, 1030),     # the appended rows straddle two key ranges
+    (16, 16, 2, 128, 16, 20),      # T == M: every key is appended
+    (4, 24, 4, 256, 4100, 4100),   # 27B heads
+])
+def test_append_fused(vq, M, Hq, Hkv, D, T, T_cap):
+    """vq_multirow_attn_append: the M new rows (taken from a fused q|k|v-like row
+    layout) land at cache positions T-M .. T-1 and the output equals the
+    attention over the appended cache, bit for bit with the separate append."""
+    q, k, v = attn_inputs(22, M, Hq, Hkv, D, T_cap, extra=T)
+    rng = np.random.default_rng(T)
+    new = rng.standard_normal((M, 2 * Hkv * D + 16)).astype(np.float32)
+    from tests.gpu_util import dev
+    import oracle.stack as ostack
+    new_bits = ostack.to_bf16_bits(new.astype(np.float64))
+    src = bf16_tensor(new_bits)
+    k_new, v_new = src[:, : Hkv * D], src[:, Hkv * D: 2 * Hkv * D]
+    # fused
+    kc, vc = bf16_tensor(k), bf16_tensor(v)
+    out = vq.multirow_attn(bf16_tensor(q), kc, vc, T, 1 / math.sqrt(D), k_new=k_new, v_new=v_new)
+    # separate append then attention
+    kc2, vc2 = bf16_tensor(k), bf16_tensor(v)
+    vq.kv_append(src, 0, Hkv * D, kc2, vc2, T - M)
+    out2 = vq.multirow_attn(bf16_tensor(q), kc2, vc2, T, 1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    assert torch.equal(kc, kc2) and torch.equal(vc, vc2)
+    assert torch.equal(out, out2)
+    # oracle on the appended cache
+    ka, va = k.copy(), v.copy()
+    ka[:, T - M: T] = new_bits[:, : Hkv * D].reshape(M, Hkv, D).transpose(1, 0, 2)
+    va[:, T - M: T] = new_bits[:, Hkv * D: 2 * Hkv * D].reshape(M, Hkv, D).transpose(1, 0, 2)
+    ref = oa.multirow_attention(q, ka, va, M, Hq, Hkv, D, T, T_cap, 1 / math.sqrt(D))
+    assert_close(to_f64(out), ref, "append fused vs oracle")
+    # rows past T untouched
+    assert torch.equal(kc[:, T:], bf16_tensor(k)[:, T:])
