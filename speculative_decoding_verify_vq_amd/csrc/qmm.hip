@@ -32,7 +32,7 @@
 //     of 128.0 gives the exact bf16 value 128 + q, two per 32-bit word, and the
 //     constant 128 is removed per group through the group sums of x. 8-bit:
 //     v_cvt_f32_ubyte + a byte permute gives the exact bf16 q.
-//   * x (zero-padded to MT = 8 or 16 rows) is staged in LDS once per workgroup,
+//   * x (zero-padded to MT = 4, 8 or 16 rows) is staged in LDS once per workgroup,
 //     in the element order of the unpack, with its per-group sums. Optionally it
 //     is RMS-normalised on the way in (x * 1/sqrt(mean(x^2) + eps), rounded to
 //     bf16), from per-row sums of squares that the producer of x wrote.
@@ -158,7 +158,9 @@ template <int BITS, int MT, int LAYOUT, int EPI, bool NORM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void qmm_kernel(const QmmArgs a) {
   constexpr int GB = BlockCfg<BITS>::GB;
   constexpr int kInFlight = BlockCfg<BITS>::IN_FLIGHT;
-  constexpr int kUseful = MT / 2;  // accumulator registers that hold rows < MT
+  // Accumulator registers that hold rows < MT: with the 32x32 output layout,
+  // register r of lane half h holds row 8*(r/4) + 4*h + r%4.
+  constexpr int kUseful = MT <= 8 ? 4 : 8;
 
   __shared__ u32x4 xl[MT * kXUnits];
   __shared__ float xsum[kCG][16];
@@ -520,13 +522,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   __syncthreads();
   if (!s_last) return;
   // Sum the partials in split order, kBatch splits x kVPT x kPair loads in
-  // flight per thread (32 or fewer). Thread t, value i covers element t + i * 256
+  // flight per thread (36 or fewer). Thread t, value i covers element t + i * 256
   // of the block's [M][128] (store, residual) or of its [M][64] gate/up column
   // pairs (SwiGLU).
   constexpr int kCols = EPI == kEpiSwiGLU ? kColsWG / 2 : kColsWG;
   constexpr int kVPT = MT * kCols / kThreads;
   constexpr int kPair = EPI == kEpiSwiGLU ? 2 : 1;
-  constexpr int kBatch = 32 / (kVPT * kPair);
+  constexpr int kBatch = 36 / (kVPT * kPair);
   float v[kVPT][kPair];
   size_t idx[kVPT];
   bool ok[kVPT];
@@ -716,7 +718,7 @@ int qmm_sumsq_parts(int N) { return (N + kColsWG - 1) / kColsWG; }
 
 QmmPlan qmm_plan(int bits, int M, int N, int K, bool tiled) {
   QmmPlan p{};
-  p.mt = M <= 8 ? 8 : 16;
+  p.mt = M <= 4 ? 4 : M <= 8 ? 8 : 16;
   p.cols_per_wg = kColsWG;
   p.n_blocks = (N + kColsWG - 1) / kColsWG;
   const int GB = bits == 4 ? 4 : 2;
@@ -788,17 +790,21 @@ hipError_t qmm_launch(const QmmPlan& plan, const QmmCall& c, hipStream_t stream)
     case 4: VQ_K(B, MT, kLayoutTiled, kEpiSwiGLU, false); break;   \
     default: VQ_K(B, MT, kLayoutTiled, kEpiSwiGLU, true); break;   \
   }
-#define VQ_BITS(B)                                                \
-  if (layout == kLayoutRow) {                                     \
-    if (plan.mt == 8) VQ_K(B, 8, kLayoutRow, kEpiStore, false);   \
-    else VQ_K(B, 16, kLayoutRow, kEpiStore, false);               \
-  } else if (layout == kLayoutRowScalar) {                        \
-    if (plan.mt == 8) VQ_K(B, 8, kLayoutRowScalar, kEpiStore, false); \
-    else VQ_K(B, 16, kLayoutRowScalar, kEpiStore, false);         \
-  } else if (plan.mt == 8) {                                      \
-    VQ_EPI_NORM(B, 8)                                             \
-  } else {                                                        \
-    VQ_EPI_NORM(B, 16)                                            \
+#define VQ_BITS(B)                                                      \
+  if (layout == kLayoutRow) {                                           \
+    if (plan.mt == 4) VQ_K(B, 4, kLayoutRow, kEpiStore, false);         \
+    else if (plan.mt == 8) VQ_K(B, 8, kLayoutRow, kEpiStore, false);    \
+    else VQ_K(B, 16, kLayoutRow, kEpiStore, false);                     \
+  } else if (layout == kLayoutRowScalar) {                              \
+    if (plan.mt == 4) VQ_K(B, 4, kLayoutRowScalar, kEpiStore, false);   \
+    else if (plan.mt == 8) VQ_K(B, 8, kLayoutRowScalar, kEpiStore, false); \
+    else VQ_K(B, 16, kLayoutRowScalar, kEpiStore, false);               \
+  } else if (plan.mt == 4) {                                            \
+    VQ_EPI_NORM(B, 4)                                                   \
+  } else if (plan.mt == 8) {                                            \
+    VQ_EPI_NORM(B, 8)                                                   \
+  } else {                                                              \
+    VQ_EPI_NORM(B, 16)                                                  \
   }
   if (c.bits == 4) {
     VQ_BITS(4)

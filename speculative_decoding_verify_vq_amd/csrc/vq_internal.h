@@ -16,7 +16,7 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- skinny QMM
 struct QmmPlan {
-  int mt;          // padded row count of the kernel variant (8 or 16)
+  int mt;          // padded row count of the kernel variant (4, 8 or 16)
   int cols_per_wg; // output columns per workgroup
   int n_blocks;    // column blocks
   int splits;      // K splits (workgroups per column block)
