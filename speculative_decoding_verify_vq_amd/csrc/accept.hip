@@ -63,24 +63,34 @@ __device__ __forceinline__ u64 key_of(float v, int x, int V) {
   return ((u64)b << 20) | (u64)(V - 1 - x);
 }
 
-// Apply f(x, v) to every element of a row; thread t takes x = t + i*blockDim
-// (coalesced), kUnroll loads issued before any is used.
+// Apply f(x, v) to every element of a row. The body of the row is read as
+// float4 (a scalar head up to 16-byte alignment and a scalar tail around it);
+// thread t takes float4 units t + i*blockDim (coalesced), kUnroll units in
+// flight before any is used.
 template <typename F>
 __device__ __forceinline__ void for_row(const float* __restrict__ row, int V, F&& f) {
   const int nt = blockDim.x;
-  for (int base = threadIdx.x; base < V; base += nt * kUnroll) {
-    float v[kUnroll];
+  const int head = min(V, (int)(((16u - (uint32_t)(reinterpret_cast<uintptr_t>(row) & 15u)) & 15u) >> 2));
+  for (int x = threadIdx.x; x < head; x += nt) f(x, row[x]);
+  const float4* body = reinterpret_cast<const float4*>(row + head);
+  const int nb = (V - head) >> 2;
+  for (int base = threadIdx.x; base < nb; base += nt * kUnroll) {
+    float4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = body[min(base + u * nt, nb - 1)];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int x = base + u * nt;
-      v[u] = x < V ? row[x] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int x = base + u * nt;
-      if (x < V) f(x, v[u]);
+      const int i = base + u * nt;
+      if (i < nb) {
+        const int x = head + 4 * i;
+        f(x, v[u].x);
+        f(x + 1, v[u].y);
+        f(x + 2, v[u].z);
+        f(x + 3, v[u].w);
+      }
     }
   }
+  for (int x = head + 4 * nb + threadIdx.x; x < V; x += nt) f(x, row[x]);
 }
 
 // --------------------------------------------------------------- block scans
@@ -404,22 +414,37 @@ __device__ int draw_token(const DrawRow& d, uint32_t mu, u128* scan, u128* wsum,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NW = kEntryThreads / 64;
   const int V = d.V;
-  const int chunk = (V + NW - 1) / NW;
+  const int chunk = ((V + NW - 1) / NW + 3) & ~3;  // multiple of 4: chunk starts stay 16-byte aligned
   const int c0 = min(V, wave * chunk), c1 = min(V, c0 + chunk);
   u128 local = 0;
-  for (int base = c0 + lane; base < c1; base += 64 * 4) {
-    float pv[4], qv[4];
+  {
+    // Scalar up to a multiple of 4 elements from the chunk start when the rows
+    // are not 16-byte aligned there; float4 otherwise, 4 units per lane in flight.
+    const bool vec = ((reinterpret_cast<uintptr_t>(d.P + c0) | (d.Q ? reinterpret_cast<uintptr_t>(d.Q + c0) : 0)) & 15) == 0;
+    const int nv = vec ? (c1 - c0) >> 2 : 0;
+    const float4* P4 = reinterpret_cast<const float4*>(d.P + c0);
+    const float4* Q4 = reinterpret_cast<const float4*>(d.Q ? d.Q + c0 : d.P + c0);
+    for (int base = lane; base < nv; base += 64 * 4) {
+      float4 pv[4], qv[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = base + 64 * u;
-      pv[u] = x < c1 ? d.P[x] : 0.f;
-      qv[u] = (x < c1 && d.Q) ? d.Q[x] : 0.f;
-    }
+      for (int u = 0; u < 4; ++u) {
+        const int i = min(base + 64 * u, nv - 1);
+        pv[u] = P4[i];
+        qv[u] = Q4[i];
+      }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = base + 64 * u;
-      if (x < c1) local += d.w(x, pv[u], qv[u]);
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + 64 * u;
+        if (i < nv) {
+          const int x = c0 + 4 * i;
+          local += d.w(x, pv[u].x, qv[u].x);
+          local += d.w(x + 1, pv[u].y, qv[u].y);
+          local += d.w(x + 2, pv[u].z, qv[u].z);
+          local += d.w(x + 3, pv[u].w, qv[u].w);
+        }
+      }
     }
+    for (int x = c0 + 4 * nv + lane; x < c1; x += 64) local += d.w(x, d.P[x], d.Q ? d.Q[x] : 0.f);
   }
   // wave total
 #pragma unroll
