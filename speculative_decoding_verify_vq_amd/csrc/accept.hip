@@ -166,6 +166,37 @@ struct SelectLds {
   int flag;
 };
 
+// ------------------------------------------- state of the chunked pipeline
+constexpr int kChunk = 8192;
+constexpr int kCT = 256;           // threads of the chunk kernels
+constexpr int kCandCap = 16384;    // keys gathered per row
+constexpr int kTopShift = 38;      // the histogram bin of a key is key >> 38 (12 bits)
+constexpr int kCandBits = 8;       // digit width of the selects over gathered keys
+
+struct RowState {
+  u64 total;         // mass of the row
+  u64 above;         // weight of the keys above the candidate bin
+  u64 thr;           // weight the select must reach
+  uint32_t bad;      // an invalid probability was seen
+  uint32_t cand_n;   // keys gathered
+  int bin;           // candidate bin
+  int phase;         // 0 top-k select, 1 top-p select, 3 left to the rows kernel
+  int pending;       // a compact + resolve is due
+  int pad;
+};
+
+// Clears a row's histogram and select state: the first kernel of every call
+// (the workspace layout depends on the shapes, so nothing is assumed zero).
+__global__ __launch_bounds__(256) void rows_clear_kernel(RowState* __restrict__ st, uint32_t* __restrict__ hcnt,
+                                                         u64* __restrict__ hmass) {
+  const int r = blockIdx.x;
+  for (int b = threadIdx.x; b < kBins; b += blockDim.x) {
+    hcnt[(int64_t)r * kBins + b] = 0u;
+    hmass[(int64_t)r * kBins + b] = 0ull;
+  }
+  if (threadIdx.x == 0) st[r] = RowState{};
+}
+
 // Walking the row in order (key descending) among elements with key >= lo,
 // find the first element at which the running weight reaches `thr` (weight 1 for
 // count, the mass for by_mass). For the mass walk thr is derived from the
@@ -282,7 +313,7 @@ __device__ void radix_select(const float* __restrict__ row, int V, u64 lo, bool 
 __global__ __launch_bounds__(kRowThreads) void accept_rows_kernel(
     const float* __restrict__ p, const float* __restrict__ q, int input_kind, int64_t p_stride,
     int64_t q_stride, int K, int V, float t_scale, int top_k, uint32_t tp, float* __restrict__ probs,
-    RowMeta* __restrict__ meta) {
+    RowMeta* __restrict__ meta, RowState* __restrict__ gate, uint32_t* __restrict__ hcnt, u64* __restrict__ hmass) {
   __shared__ SelectLds s;
   __shared__ float red[kRowThreads / 64];
   __shared__ int bad;
@@ -290,6 +321,10 @@ __global__ __launch_bounds__(kRowThreads) void accept_rows_kernel(
   const int e = blockIdx.y;
   const int nrows = 2 * K + 1;
   const int tid = threadIdx.x;
+  // After the chunked pipeline only the rows it left over (crossing bin too
+  // crowded to gather) are done here.
+  const int ri = e * nrows + r;
+  if (gate && gate[ri].phase != 3) return;
   const float* src = (r <= K) ? p + (int64_t)e * p_stride + (int64_t)r * V
                               : q + (int64_t)e * q_stride + (int64_t)(r - K - 1) * V;
   const float* row = src;
@@ -554,6 +589,643 @@ __global__ __launch_bounds__(kEntryThreads) void accept_entry_kernel(
   if (tid == 0) out_n[b] = j;
 }
 
+// ----------------------------------------------------------- chunked pipeline
+// The rows and the draw spread over the whole chip: every row is cut into
+// chunks of kChunk elements, one 256-thread workgroup per (chunk, row).
+//   stats    (logits) per-chunk running max and sum of exp2
+//   hist     probabilities (written in logits mode), validity, the row's mass,
+//            and the 4096-bin histogram (count, mass) of the top 12 key bits,
+//            merged into a per-row histogram with global atomics
+//   find     (one workgroup per row) the bin where the first select crosses;
+//            rows without truncation, invalid rows or an empty select finish
+//   compact  the keys of that bin gathered per row (at most kCandCap)
+//   resolve  (one workgroup per row) radix select over the gathered keys; a
+//            top-p walk after top-k that crosses in a higher bin asks for a
+//            second compact + resolve
+// A row whose crossing bin holds more than kCandCap keys is left to the
+// single-workgroup rows kernel above. Every count is an integer, so the
+// result does not depend on how the work is split.
+// f(x, v) for x in [x0, x1): scalar head to 16-byte alignment, float4 body with
+// kUnroll units per thread in flight, scalar tail.
+template <typename F>
+__device__ __forceinline__ void for_range(const float* __restrict__ row, int x0, int x1, F&& f) {
+  const int nt = blockDim.x;
+  const int lead = (int)(((16u - (uint32_t)(reinterpret_cast<uintptr_t>(row + x0) & 15u)) & 15u) >> 2);
+  const int head = min(x1 - x0, lead);
+  for (int i = threadIdx.x; i < head; i += nt) f(x0 + i, row[x0 + i]);
+  const int b0 = x0 + head;
+  const float4* body = reinterpret_cast<const float4*>(row + b0);
+  const int nb = (x1 - b0) >> 2;
+  for (int base = threadIdx.x; base < nb; base += nt * kUnroll) {
+    float4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = body[min(base + u * nt, nb - 1)];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = base + u * nt;
+      if (i < nb) {
+        const int x = b0 + 4 * i;
+        f(x, v[u].x);
+        f(x + 1, v[u].y);
+        f(x + 2, v[u].z);
+        f(x + 3, v[u].w);
+      }
+    }
+  }
+  for (int x = b0 + 4 * nb + threadIdx.x; x < x1; x += nt) f(x, row[x]);
+}
+
+__device__ __forceinline__ const float* row_ptr(const float* p, const float* q, int64_t ps, int64_t qs, int K,
+                                                int V, int r) {
+  const int nrows = 2 * K + 1;
+  const int e = r / nrows, rr = r % nrows;
+  return rr <= K ? p + (int64_t)e * ps + (int64_t)rr * V : q + (int64_t)e * qs + (int64_t)(rr - K - 1) * V;
+}
+
+template <typename T>
+__device__ T wg_sum(T v, T* lds /* blockDim/64 entries */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int off = 32; off > 0; off >>= 1) {
+    if constexpr (sizeof(T) == 8) {
+      const uint32_t lo = __shfl_xor((uint32_t)v, off), hi = __shfl_xor((uint32_t)((u64)v >> 32), off);
+      v += (T)(((u64)hi << 32) | lo);
+    } else {
+      v += __shfl_xor(v, off);
+    }
+  }
+  __syncthreads();
+  if (lane == 0) lds[wave] = v;
+  __syncthreads();
+  T t = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += lds[w];
+  return t;
+}
+
+__global__ __launch_bounds__(kCT) void rows_stats_kernel(const float* __restrict__ p, const float* __restrict__ q,
+                                                         int64_t ps, int64_t qs, int K, int V, int C, float t_scale,
+                                                         float2* __restrict__ stats) {
+  __shared__ float red[kCT / 64];
+  const int c = blockIdx.x % C, r = blockIdx.x / C;
+  const float* src = row_ptr(p, q, ps, qs, K, V, r);
+  const int x0 = c * kChunk, x1 = min(V, x0 + kChunk);
+  float mx = -INFINITY, sm = 0.f;
+  for_range(src, x0, x1, [&](int, float v) {
+    const float a = v * t_scale;
+    if (a > mx) {
+      sm = sm * exp2f(mx - a) + 1.f;
+      mx = a;
+    } else if (a > -INFINITY) {
+      sm += exp2f(a - mx);
+    }
+  });
+  const float cmx = block_reduce_max(mx, red);
+  const float part = (mx == -INFINITY) ? 0.f : sm * exp2f(mx - cmx);
+  const float csum = block_reduce_sum(part, red);
+  if (threadIdx.x == 0) stats[(int64_t)r * C + c] = make_float2(cmx, csum);
+}
+
+__global__ __launch_bounds__(kCT) void rows_hist_kernel(
+    const float* __restrict__ p, const float* __restrict__ q, int input_kind, int64_t ps, int64_t qs, int K, int V,
+    int C, float t_scale, int use_hist, float* __restrict__ probs, const float2* __restrict__ stats,
+    RowState* __restrict__ st, uint32_t* __restrict__ hcnt, u64* __restrict__ hmass) {
+  __shared__ uint32_t cnt[kBins];
+  __shared__ u64 mas[kBins];
+  __shared__ u64 red64[kCT / 64];
+  __shared__ float sg[2];
+  __shared__ int s_bad;
+  const int c = blockIdx.x % C, r = blockIdx.x / C;
+  const int tid = threadIdx.x;
+  const int x0 = c * kChunk, x1 = min(V, x0 + kChunk);
+  const float* src = row_ptr(p, q, ps, qs, K, V, r);
+  float* dst = probs + (int64_t)r * V;
+  if (tid == 0) {
+    s_bad = 0;
+    if (input_kind == 1) {
+      // The row's max and sum from the chunk statistics, in chunk order: every
+      // workgroup of the row gets the same values.
+      float gmx = -INFINITY;
+      for (int i = 0; i < C; ++i) gmx = fmaxf(gmx, stats[(int64_t)r * C + i].x);
+      float gs = 0.f;
+      for (int i = 0; i < C; ++i) {
+        const float2 s2 = stats[(int64_t)r * C + i];
+        gs += (s2.x == -INFINITY) ? 0.f : s2.y * exp2f(s2.x - gmx);
+      }
+      sg[0] = gmx;
+      sg[1] = 1.f / gs;
+    }
+  }
+  if (use_hist) {
+    for (int b = tid; b < kBins; b += kCT) {
+      cnt[b] = 0u;
+      mas[b] = 0ull;
+    }
+  }
+  __syncthreads();
+  const float gmx = sg[0], inv = sg[1];
+  u64 msum = 0;
+  int bad = 0;
+  auto visit = [&](int x, float pv) {
+    if (!prob_ok(pv)) {
+      bad = 1;
+      return;
+    }
+    const u64 m = mass_of(pv);
+    msum += m;
+    if (use_hist) {
+      const int bin = (int)(key_of(pv, x, V) >> kTopShift);
+      atomicAdd(&cnt[bin], 1u);
+      if (m) atomicAdd(&mas[bin], m);
+    }
+  };
+  if (input_kind == 1) {
+    for_range(src, x0, x1, [&](int x, float v) {
+      const float pv = exp2f(v * t_scale - gmx) * inv;
+      dst[x] = pv;
+      visit(x, pv);
+    });
+  } else {
+    for_range(src, x0, x1, visit);
+  }
+  if (bad) s_bad = 1;
+  const u64 tot = wg_sum<u64>(msum, red64);  // barriers inside
+  if (tid == 0) {
+    if (s_bad) atomicOr(&st[r].bad, 1u);
+    if (tot) atomicAdd(&st[r].total, tot);
+  }
+  if (use_hist) {
+    for (int b = tid; b < kBins; b += kCT) {
+      if (cnt[b]) atomicAdd(&hcnt[(int64_t)r * kBins + b], cnt[b]);
+      if (mas[b]) atomicAdd(&hmass[(int64_t)r * kBins + b], mas[b]);
+    }
+  }
+}
+
+// Walks the row histogram from the top bin down (bins > `below` only when
+// below >= 0): the bin where the running weight (count or mass) first reaches
+// thr, the weight above it and its count. Returns -1 if thr is not reached.
+struct Crossing {
+  int bin;
+  u64 above;
+  uint32_t count;
+};
+
+__device__ Crossing find_bin(const uint32_t* hc, const u64* hm, bool by_mass, u64 thr, int below, u64* scan,
+                             Crossing* out) {
+  const int tid = threadIdx.x;  // 1024 threads, 4 bins each, descending
+  u64 w[4];
+  uint32_t cc[4];
+  u64 lsum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = kBins - 1 - (4 * tid + i);
+    const bool in = b > below;
+    cc[i] = in ? hc[b] : 0u;
+    w[i] = in ? (by_mass ? hm[b] : (u64)cc[i]) : 0ull;
+    lsum += w[i];
+  }
+  u64 tot;
+  const u64 excl = block_excl_scan<u64, kRowThreads>(lsum, scan, tot);
+  if (tid == 0) *out = Crossing{-1, 0, 0};
+  __syncthreads();
+  if (excl < thr && thr <= excl + lsum) {
+    u64 run = excl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (run + w[i] >= thr) {
+        *out = Crossing{kBins - 1 - (4 * tid + i), run, cc[i]};
+        break;
+      }
+      run += w[i];
+    }
+  }
+  __syncthreads();
+  const Crossing res = *out;
+  __syncthreads();
+  return res;
+}
+
+__global__ __launch_bounds__(kRowThreads) void rows_find_kernel(int V, int top_k, uint32_t tp,
+                                                                RowState* __restrict__ st,
+                                                                uint32_t* __restrict__ hcnt,
+                                                                u64* __restrict__ hmass, RowMeta* __restrict__ meta) {
+  __shared__ u64 scan[kRowThreads / 64 + 1];
+  __shared__ Crossing cr;
+  const int r = blockIdx.x;
+  const RowState s0 = st[r];
+  const bool use_k = top_k > 0 && top_k < V;
+  const bool use_p = tp < (1u << 24);
+  RowMeta out{};
+  if (s0.bad || (!use_k && !use_p)) {
+    out.z = s0.bad ? 0ull : s0.total;
+    out.status = (s0.bad || s0.total == 0) ? 1 : 0;
+    __syncthreads();
+    if (threadIdx.x == 0) meta[r] = out;
+    return;
+  }
+  u64 thr = (u64)top_k;
+  if (!use_k) thr = (u64)(((u128)tp * s0.total + ((u128)1 << 24) - 1) >> 24);
+  const Crossing c = find_bin(hcnt + (int64_t)r * kBins, hmass + (int64_t)r * kBins, !use_k, thr, -1, scan, &cr);
+  if (thr == 0 || c.bin < 0) {  // nothing to keep
+    out.status = 1;
+    if (threadIdx.x == 0) meta[r] = out;
+    return;
+  }
+  if (threadIdx.x == 0) {
+    RowState s = s0;
+    s.bin = c.bin;
+    s.above = c.above;
+    s.thr = thr;
+    s.cand_n = 0;
+    if (c.count > (uint32_t)kCandCap) {
+      s.phase = 3;
+      s.pending = 0;
+    } else {
+      s.phase = use_k ? 0 : 1;
+      s.pending = 1;
+    }
+    st[r] = s;
+  }
+}
+
+__global__ __launch_bounds__(kCT) void rows_compact_kernel(const float* __restrict__ p, const float* __restrict__ q,
+                                                           int input_kind, int64_t ps, int64_t qs, int K, int V,
+                                                           int C, const float* __restrict__ probs,
+                                                           RowState* __restrict__ st, u64* __restrict__ cand) {
+  __shared__ uint32_t n_lds, w_lds, base;
+  const int c = blockIdx.x % C, r = blockIdx.x / C;
+  if (!st[r].pending) return;
+  const int bin = st[r].bin;
+  const float* row = input_kind == 1 ? probs + (int64_t)r * V : row_ptr(p, q, ps, qs, K, V, r);
+  const int x0 = c * kChunk, x1 = min(V, x0 + kChunk);
+  if (threadIdx.x == 0) {
+    n_lds = 0u;
+    w_lds = 0u;
+  }
+  __syncthreads();
+  // Count this chunk's keys of the bin, reserve their slots, then write them.
+  uint32_t mine = 0;
+  for_range(row, x0, x1, [&](int x, float v) { mine += (int)(key_of(v, x, V) >> kTopShift) == bin; });
+  if (mine) atomicAdd(&n_lds, mine);
+  __syncthreads();
+  const uint32_t n = n_lds;
+  if (n == 0) return;
+  if (threadIdx.x == 0) base = atomicAdd(&st[r].cand_n, n);
+  __syncthreads();
+  u64* dst = cand + (int64_t)r * kCandCap + base;
+  for_range(row, x0, x1, [&](int x, float v) {
+    const u64 key = key_of(v, x, V);
+    if ((int)(key >> kTopShift) == bin) dst[atomicAdd(&w_lds, 1u)] = key;
+  });
+}
+
+__device__ __forceinline__ float key_value(u64 key) { return __uint_as_float((uint32_t)(key >> 20)); }
+
+// Radix select over gathered keys that share the top 12 bits (key >> 38 ==
+// prefix): the first key, walking down from the largest, at which the running
+// weight (count or mass; only keys >= lo count) reaches thr, given the weight
+// `above` of everything above the bin. 8-bit digits from bit 30 down (the last
+// one 6 bits); a level whose crossing digit holds one key ends the walk.
+struct Sel {
+  u64 key;
+  u64 mass;
+  u64 above;
+};
+
+__device__ Sel select_keys(const u64* __restrict__ keys, int n, u64 prefix, u64 above, u64 thr, bool by_mass, u64 lo,
+                           uint32_t* cnt, u64* mas, u64* scan, Sel* res, int* flag) {
+  const int tid = threadIdx.x;
+  int hi_shift = kTopShift;
+  for (int level = 0; level < 5; ++level) {
+    const int bits = level < 4 ? kCandBits : 6;
+    const int shift = hi_shift - bits;
+    const int nb = 1 << bits;
+    for (int b = tid; b < nb; b += kRowThreads) {
+      cnt[b] = 0u;
+      mas[b] = 0ull;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += kRowThreads) {
+      const u64 key = keys[i];
+      if (key < lo || (key >> hi_shift) != prefix) continue;
+      const int d = (int)((key >> shift) & (u64)(nb - 1));
+      atomicAdd(&cnt[d], 1u);
+      if (by_mass) {
+        const u64 m = mass_of(key_value(key));
+        if (m) atomicAdd(&mas[d], m);
+      }
+    }
+    __syncthreads();
+    // Thread t < nb owns digit nb-1-t (descending).
+    const int d = nb - 1 - tid;
+    const uint32_t cd = (tid < nb) ? cnt[d] : 0u;
+    const u64 wd = (tid < nb) ? (by_mass ? mas[d] : (u64)cd) : 0ull;
+    u64 tot;
+    const u64 excl = above + block_excl_scan<u64, kRowThreads>(wd, scan, tot);
+    if (tid == 0) *flag = 0;
+    __syncthreads();
+    if (tid < nb && excl < thr && thr <= excl + wd) {
+      *res = Sel{(prefix << bits) | (u64)d, cd, excl};  // mass field carries the digit's count here
+      *flag = 1;
+    }
+    __syncthreads();
+    const Sel s = *res;
+    __syncthreads();
+    prefix = s.key;
+    above = s.above;
+    hi_shift = shift;
+    if (s.mass == 1 || level == 4) {
+      // One key left in the crossing digit: it is the answer.
+      for (int i = tid; i < n; i += kRowThreads) {
+        const u64 key = keys[i];
+        if (key >= lo && (key >> hi_shift) == prefix) *res = Sel{key, mass_of(key_value(key)), above};
+      }
+      __syncthreads();
+      const Sel out = *res;
+      __syncthreads();
+      return out;
+    }
+  }
+  return Sel{0, 0, 0};  // not reached
+}
+
+__global__ __launch_bounds__(kRowThreads) void rows_resolve_kernel(int V, int top_k, uint32_t tp,
+                                                                   RowState* __restrict__ st,
+                                                                   uint32_t* __restrict__ hcnt,
+                                                                   u64* __restrict__ hmass,
+                                                                   const u64* __restrict__ cand,
+                                                                   RowMeta* __restrict__ meta) {
+  __shared__ uint32_t cnt[1 << kCandBits];
+  __shared__ u64 mas[1 << kCandBits];
+  __shared__ u64 scan[kRowThreads / 64 + 1];
+  __shared__ u64 red64[kRowThreads / 64];
+  __shared__ Sel res;
+  __shared__ Crossing cr;
+  __shared__ int flag;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const RowState s0 = st[r];
+  if (!s0.pending) return;
+  __syncthreads();
+  const u64* keys = cand + (int64_t)r * kCandCap;
+  const int n = (int)s0.cand_n;
+  const bool use_p = tp < (1u << 24);
+  RowMeta out{};
+  if (s0.phase == 1) {
+    const Sel sel = select_keys(keys, n, (u64)s0.bin, s0.above, s0.thr, true, 0ull, cnt, mas, scan, &res, &flag);
+    out.thresh = sel.key;
+    out.z = sel.above + sel.mass;
+    out.status = out.z == 0 ? 1 : 0;
+    if (tid == 0) {
+      meta[r] = out;
+      st[r].pending = 0;
+    }
+    return;
+  }
+  // Top-k: the top_k-th key, then the kept mass Z_k (bins above + gathered keys >= it).
+  const Sel sk = select_keys(keys, n, (u64)s0.bin, s0.above, s0.thr, false, 0ull, cnt, mas, scan, &res, &flag);
+  const u64 theta = sk.key;
+  u64 m_in = 0;
+  for (int i = tid; i < n; i += kRowThreads)
+    if (keys[i] >= theta) m_in += mass_of(key_value(keys[i]));
+  u64 m_above = 0;
+  for (int b = s0.bin + 1 + tid; b < kBins; b += kRowThreads) m_above += hmass[(int64_t)r * kBins + b];
+  const u64 zk_above = wg_sum<u64>(m_above, red64);
+  const u64 zk = wg_sum<u64>(m_in, red64) + zk_above;
+  if (!use_p || zk == 0) {
+    out.thresh = theta;
+    out.z = zk;
+    out.status = zk == 0 ? 1 : 0;
+    if (tid == 0) {
+      meta[r] = out;
+      st[r].pending = 0;
+    }
+    return;
+  }
+  const u64 thr = (u64)(((u128)tp * zk + ((u128)1 << 24) - 1) >> 24);
+  const Crossing c = find_bin(hcnt + (int64_t)r * kBins, hmass + (int64_t)r * kBins, true, thr, s0.bin, scan, &cr);
+  if (c.bin >= 0) {
+    // The top-p walk crosses in a higher bin: gather it next.
+    if (tid == 0) {
+      RowState s = s0;
+      s.bin = c.bin;
+      s.above = c.above;
+      s.thr = thr;
+      s.cand_n = 0;
+      if (c.count > (uint32_t)kCandCap) {
+        s.phase = 3;
+        s.pending = 0;
+      } else {
+        s.phase = 1;
+        s.pending = 1;
+      }
+      st[r] = s;
+    }
+    return;
+  }
+  // It crosses among the gathered keys kept by top-k.
+  const Sel sp = select_keys(keys, n, (u64)s0.bin, zk_above, thr, true, theta, cnt, mas, scan, &res, &flag);
+  out.thresh = sp.key;
+  out.z = sp.above + sp.mass;
+  out.status = out.z == 0 ? 1 : 0;
+  if (tid == 0) {
+    meta[r] = out;
+    st[r].pending = 0;
+  }
+}
+
+// ------------------------------------------------------- chunked draw (entries)
+// Per (chunk, entry): the accept tests (every workgroup of the entry repeats
+// them: K pairs of loads), then the chunk's sums of the draw weights of the
+// first rejected position j — the residual, or the kept target mass when all K
+// drafts pass — and of the kept target mass of row j (used only if the
+// residual is zero everywhere).
+__device__ int entry_decide(const float* P, const float* Q, const RowMeta* mrow, const int32_t* dr, const float* us,
+                            int K, int V, int* bad_out) {
+  int bad = 0;
+  for (int i = 0; i < 2 * K + 1; ++i) bad |= mrow[i].status;
+  for (int i = 0; i <= K; ++i) bad |= !uniform_ok(us[i]);
+  for (int i = 0; i < K; ++i) bad |= (dr[i] < 0 || dr[i] >= V);
+  int j = K;
+  if (!bad) {
+    for (int i = 0; i < K; ++i) {
+      const int d = dr[i];
+      const RowMeta mp = mrow[i], mq = mrow[K + 1 + i];
+      const u64 a = kept_mass(P + (int64_t)i * V, d, V, mp);
+      const u64 c = kept_mass(Q + (int64_t)i * V, d, V, mq);
+      if (!accept_test(mu_of(us[i]), c, mp.z, a, mq.z)) {
+        j = i;
+        break;
+      }
+    }
+  }
+  *bad_out = bad;
+  return j;
+}
+
+__global__ __launch_bounds__(kCT) void draw_sums_kernel(const float* __restrict__ probs_p,
+                                                        const float* __restrict__ probs_q, int64_t pp_stride,
+                                                        int64_t qq_stride, const RowMeta* __restrict__ meta,
+                                                        int64_t meta_stride, const int32_t* __restrict__ draft,
+                                                        const float* __restrict__ uniforms, int K, int V, int C,
+                                                        u128* __restrict__ esum) {
+  __shared__ u128 scan[kCT / 64 + 1];
+  __shared__ int s_j, s_bad;
+  const int c = blockIdx.x % C, b = blockIdx.x / C;
+  const int tid = threadIdx.x;
+  const RowMeta* mrow = meta + (int64_t)b * meta_stride;
+  const float* P = probs_p + (int64_t)b * pp_stride;
+  const float* Q = probs_q + (int64_t)b * qq_stride;
+  if (tid == 0) s_j = entry_decide(P, Q, mrow, draft + (int64_t)b * K, uniforms + (int64_t)b * (K + 1), K, V, &s_bad);
+  __syncthreads();
+  if (s_bad) return;
+  const int j = s_j;
+  DrawRow d;
+  d.P = P + (int64_t)j * V;
+  d.mp = mrow[j];
+  d.Q = j < K ? Q + (int64_t)j * V : nullptr;
+  d.mq = j < K ? mrow[K + 1 + j] : RowMeta{};
+  d.V = V;
+  const int x0 = c * kChunk, x1 = min(V, x0 + kChunk);
+  u128 wm = 0, wf = 0;
+  if (d.Q) {
+    // P and Q rows side by side: element x of both in the same step.
+    const int lead = (int)(((16u - (uint32_t)(reinterpret_cast<uintptr_t>(d.P + x0) & 15u)) & 15u) >> 2);
+    const bool qal = ((reinterpret_cast<uintptr_t>(d.Q + x0) ^ reinterpret_cast<uintptr_t>(d.P + x0)) & 15u) == 0;
+    const int head = qal ? min(x1 - x0, lead) : x1 - x0;  // unaligned pair: all scalar
+    for (int x = x0 + tid; x < x0 + head; x += kCT) {
+      const float pv = d.P[x];
+      wm += d.w(x, pv, d.Q[x]);
+      wf += kept_mass_v(pv, x, V, d.mp);
+    }
+    const int b0 = x0 + head;
+    const int nb = (x1 - b0) >> 2;
+    const float4* P4 = reinterpret_cast<const float4*>(d.P + b0);
+    const float4* Q4 = reinterpret_cast<const float4*>(d.Q + b0);
+    for (int base = tid; base < nb; base += kCT * 4) {
+      float4 pv[4], qv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = min(base + u * kCT, nb - 1);
+        pv[u] = P4[i];
+        qv[u] = Q4[i];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + u * kCT;
+        if (i < nb) {
+          const int x = b0 + 4 * i;
+          wm += d.w(x, pv[u].x, qv[u].x) + d.w(x + 1, pv[u].y, qv[u].y) + d.w(x + 2, pv[u].z, qv[u].z) +
+                d.w(x + 3, pv[u].w, qv[u].w);
+          wf += (u128)(kept_mass_v(pv[u].x, x, V, d.mp) + kept_mass_v(pv[u].y, x + 1, V, d.mp)) +
+                (u128)(kept_mass_v(pv[u].z, x + 2, V, d.mp) + kept_mass_v(pv[u].w, x + 3, V, d.mp));
+        }
+      }
+    }
+    for (int x = b0 + 4 * nb + tid; x < x1; x += kCT) {
+      const float pv = d.P[x];
+      wm += d.w(x, pv, d.Q[x]);
+      wf += kept_mass_v(pv, x, V, d.mp);
+    }
+  } else {
+    for_range(d.P, x0, x1, [&](int x, float v) { wm += kept_mass_v(v, x, V, d.mp); });
+  }
+  u128 tm, tf;
+  block_excl_scan<u128, kCT>(wm, scan, tm);
+  block_excl_scan<u128, kCT>(wf, scan, tf);
+  if (tid == 0) {
+    esum[((int64_t)b * C + c) * 2] = tm;
+    esum[((int64_t)b * C + c) * 2 + 1] = tf;
+  }
+}
+
+// Per entry: the draw weights' total from the chunk sums (in chunk order), the
+// chunk that holds floor(mu * R / 2^24), and the token inside it (each thread
+// sums 8 consecutive weights; a block scan finds the thread, which walks them).
+__global__ __launch_bounds__(kRowThreads) void draw_pick_kernel(
+    const float* __restrict__ probs_p, const float* __restrict__ probs_q, int64_t pp_stride, int64_t qq_stride,
+    const RowMeta* __restrict__ meta, int64_t meta_stride, const int32_t* __restrict__ draft,
+    const float* __restrict__ uniforms, int K, int V, int C, const u128* __restrict__ esum,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_n) {
+  __shared__ u128 scan[kRowThreads / 64 + 1];
+  __shared__ int s_j, s_bad, s_tok, s_fb, s_c;
+  __shared__ u128 s_before, s_tau;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const RowMeta* mrow = meta + (int64_t)b * meta_stride;
+  const float* P = probs_p + (int64_t)b * pp_stride;
+  const float* Q = probs_q + (int64_t)b * qq_stride;
+  const int32_t* dr = draft + (int64_t)b * K;
+  const float* us = uniforms + (int64_t)b * (K + 1);
+  if (tid == 0) {
+    s_j = entry_decide(P, Q, mrow, dr, us, K, V, &s_bad);
+    s_tok = -1;
+    if (!s_bad) {
+      u128 R = 0;
+      for (int c = 0; c < C; ++c) R += esum[((int64_t)b * C + c) * 2];
+      int fb = 0;
+      if (R == 0) {  // p~_j == q~_j and the draft lay outside both supports: draw from p~_j
+        fb = 1;
+        for (int c = 0; c < C; ++c) R += esum[((int64_t)b * C + c) * 2 + 1];
+      }
+      const u128 tau = scaled_draw(mu_of(us[K]), R);
+      u128 before = 0;
+      int cs = C - 1;
+      for (int c = 0; c < C; ++c) {
+        const u128 w = esum[((int64_t)b * C + c) * 2 + fb];
+        if (before + w > tau) {
+          cs = c;
+          break;
+        }
+        before += w;
+      }
+      s_fb = fb;
+      s_c = cs;
+      s_before = before;
+      s_tau = tau;
+    }
+  }
+  __syncthreads();
+  const int j = s_j;
+  if (s_bad) {
+    for (int i = tid; i <= K; i += kRowThreads) out_tokens[(int64_t)b * (K + 1) + i] = -1;
+    if (tid == 0) out_n[b] = -1;
+    return;
+  }
+  DrawRow d;
+  d.P = P + (int64_t)j * V;
+  d.mp = mrow[j];
+  d.Q = (j < K && !s_fb) ? Q + (int64_t)j * V : nullptr;
+  d.mq = j < K ? mrow[K + 1 + j] : RowMeta{};
+  d.V = V;
+  const int x0 = s_c * kChunk, x1 = min(V, x0 + kChunk);
+  const int per = (x1 - x0 + kRowThreads - 1) / kRowThreads;
+  const int a0 = min(x1, x0 + tid * per), a1 = min(x1, a0 + per);
+  u128 mine = 0;
+  for (int x = a0; x < a1; ++x) mine += d.w(x, d.P[x], d.Q ? d.Q[x] : 0.f);
+  u128 tot;
+  const u128 excl = s_before + block_excl_scan<u128, kRowThreads>(mine, scan, tot);
+  const u128 tau = s_tau;
+  if (excl <= tau && tau < excl + mine) {
+    u128 run = excl;
+    for (int x = a0; x < a1; ++x) {
+      run += d.w(x, d.P[x], d.Q ? d.Q[x] : 0.f);
+      if (run > tau) {
+        s_tok = x;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  const int tok = s_tok;
+  for (int i = tid; i <= K; i += kRowThreads) {
+    int32_t t = -1;
+    if (i < j) t = dr[i];
+    else if (i == j) t = tok;
+    out_tokens[(int64_t)b * (K + 1) + i] = t;
+  }
+  if (tid == 0) out_n[b] = j;
+}
+
 // ------------------------------------------------------------- shared rows
 // Running sums of each position's draw weights: table[j][x] = sum_{t <= x} r_j(t).
 __global__ __launch_bounds__(kEntryThreads) void accept_table_kernel(
@@ -633,15 +1305,36 @@ __global__ __launch_bounds__(256) void accept_trials_kernel(
 
 }  // namespace
 
+// The chunked stages are used while the rows (or entries) alone would leave
+// most of the chip idle.
+constexpr int kChunkedMaxRows = 1024;
+constexpr int kChunkedMaxEntries = 64;
+
 AcceptPlan accept_plan(int B, int K, int V, int input_kind, int64_t p_stride, int64_t q_stride) {
   AcceptPlan p{};
   p.shared = (p_stride == 0 && q_stride == 0);
   p.entries = p.shared ? 1 : B;
   p.rows_per_entry = 2 * K + 1;
-  p.meta_bytes = align_up((size_t)p.entries * p.rows_per_entry * sizeof(RowMeta), 256);
-  p.probs_bytes = input_kind == 1 ? align_up((size_t)p.entries * p.rows_per_entry * V * sizeof(float), 256) : 0;
+  const int64_t R = (int64_t)p.entries * p.rows_per_entry;
+  p.chunks = (V + kChunk - 1) / kChunk;
+  p.chunked = R <= kChunkedMaxRows;
+  p.draw_chunked = !p.shared && B <= kChunkedMaxEntries;
+  p.meta_bytes = align_up((size_t)R * sizeof(RowMeta), 256);
+  p.probs_bytes = input_kind == 1 ? align_up((size_t)R * V * sizeof(float), 256) : 0;
   p.table_bytes = p.shared ? align_up((size_t)(K + 1) * V * sizeof(u128), 256) : 0;
+  if (p.chunked) {
+    p.state_bytes = align_up((size_t)R * sizeof(RowState), 256);
+    p.hist_bytes = align_up((size_t)R * kBins * (sizeof(uint32_t) + sizeof(u64)), 256);
+    p.cand_bytes = align_up((size_t)R * kCandCap * sizeof(u64), 256);
+    p.stats_bytes = input_kind == 1 ? align_up((size_t)R * p.chunks * sizeof(float2), 256) : 0;
+  }
+  if (p.draw_chunked) p.esum_bytes = align_up((size_t)B * p.chunks * 2 * sizeof(u128), 256);
   return p;
+}
+
+size_t accept_workspace_total(const AcceptPlan& p) {
+  return p.meta_bytes + p.probs_bytes + p.table_bytes + p.state_bytes + p.hist_bytes + p.cand_bytes +
+         p.stats_bytes + p.esum_bytes;
 }
 
 hipError_t accept_launch(const AcceptPlan& plan, const float* p, const float* q, int input_kind,
@@ -649,9 +1342,24 @@ hipError_t accept_launch(const AcceptPlan& plan, const float* p, const float* q,
                          const float* uniforms, int B, int K, int V, float temperature, int top_k,
                          float top_p, int32_t* out_tokens, int32_t* out_n, float* probs_out,
                          void* workspace, hipStream_t stream) {
+  // Workspace: per-row results, select state, histograms (cleared by the first
+  // kernel of the call), gathered keys, chunk statistics, draw sums,
+  // probabilities, shared-mode tables.
   char* ws = reinterpret_cast<char*>(workspace);
   RowMeta* meta = reinterpret_cast<RowMeta*>(ws);
   ws += plan.meta_bytes;
+  RowState* st = reinterpret_cast<RowState*>(ws);
+  ws += plan.state_bytes;
+  uint32_t* hcnt = reinterpret_cast<uint32_t*>(ws);
+  const int64_t R = (int64_t)plan.entries * plan.rows_per_entry;
+  u64* hmass = reinterpret_cast<u64*>(ws + align_up((size_t)R * kBins * sizeof(uint32_t), 16));
+  ws += plan.hist_bytes;
+  u64* cand = reinterpret_cast<u64*>(ws);
+  ws += plan.cand_bytes;
+  float2* stats = reinterpret_cast<float2*>(ws);
+  ws += plan.stats_bytes;
+  u128* esum = reinterpret_cast<u128*>(ws);
+  ws += plan.esum_bytes;
   float* probs = nullptr;
   if (input_kind == 1) {
     probs = probs_out ? probs_out : reinterpret_cast<float*>(ws);
@@ -663,10 +1371,47 @@ hipError_t accept_launch(const AcceptPlan& plan, const float* p, const float* q,
   if (tp < 1) tp = 1;
   if (tp > (1u << 24)) tp = 1u << 24;
   if (q == nullptr) q = p;  // K == 0: no draft rows are read
-  hipLaunchKernelGGL(accept_rows_kernel, dim3(plan.rows_per_entry, plan.entries), dim3(kRowThreads), 0,
-                     stream, p, q, input_kind, p_stride, q_stride, K, V, t_scale, top_k, tp, probs, meta);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const bool use_k = top_k > 0 && top_k < V;
+  const bool use_p = tp < (1u << 24);
+  const int C = plan.chunks;
+  hipError_t e;
+  if (plan.chunked) {
+    const unsigned cg = (unsigned)(C * R);
+    hipLaunchKernelGGL(rows_clear_kernel, dim3((unsigned)R), dim3(256), 0, stream, st, hcnt, hmass);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (input_kind == 1) {
+      hipLaunchKernelGGL(rows_stats_kernel, dim3(cg), dim3(kCT), 0, stream, p, q, p_stride, q_stride, K, V, C,
+                         t_scale, stats);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(rows_hist_kernel, dim3(cg), dim3(kCT), 0, stream, p, q, input_kind, p_stride, q_stride, K, V,
+                       C, t_scale, (int)(use_k || use_p), probs, stats, st, hcnt, hmass);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(rows_find_kernel, dim3((unsigned)R), dim3(kRowThreads), 0, stream, V, top_k, tp, st, hcnt,
+                       hmass, meta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (use_k || use_p) {
+      const int rounds = (use_k && use_p) ? 2 : 1;
+      for (int round = 0; round < rounds; ++round) {
+        hipLaunchKernelGGL(rows_compact_kernel, dim3(cg), dim3(kCT), 0, stream, p, q, input_kind, p_stride, q_stride,
+                           K, V, C, probs, st, cand);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(rows_resolve_kernel, dim3((unsigned)R), dim3(kRowThreads), 0, stream, V, top_k, tp, st,
+                           hcnt, hmass, cand, meta);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      // Rows whose crossing bin was too crowded to gather.
+      hipLaunchKernelGGL(accept_rows_kernel, dim3(plan.rows_per_entry, plan.entries), dim3(kRowThreads), 0, stream,
+                         p, q, input_kind, p_stride, q_stride, K, V, t_scale, top_k, tp, probs, meta, st, hcnt,
+                         hmass);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  } else {
+    hipLaunchKernelGGL(accept_rows_kernel, dim3(plan.rows_per_entry, plan.entries), dim3(kRowThreads), 0, stream, p,
+                       q, input_kind, p_stride, q_stride, K, V, t_scale, top_k, tp, probs, meta, nullptr, nullptr,
+                       nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   // Rows to read from now on: the probabilities (computed or given).
   const float* PP;
   const float* QQ;
@@ -684,13 +1429,19 @@ hipError_t accept_launch(const AcceptPlan& plan, const float* p, const float* q,
   if (plan.shared) {
     hipLaunchKernelGGL(accept_table_kernel, dim3(K + 1), dim3(kEntryThreads), 0, stream, PP, QQ, meta, K, V,
                        table);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(accept_trials_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, PP, QQ, meta, table,
                        draft, uniforms, B, K, V, out_tokens, out_n);
     return hipGetLastError();
   }
-  if (input_kind == 1) pps = qqs = (int64_t)plan.rows_per_entry * V;
+  if (plan.draw_chunked) {
+    hipLaunchKernelGGL(draw_sums_kernel, dim3((unsigned)(C * B)), dim3(kCT), 0, stream, PP, QQ, pps, qqs, meta,
+                       (int64_t)plan.rows_per_entry, draft, uniforms, K, V, C, esum);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(draw_pick_kernel, dim3(B), dim3(kRowThreads), 0, stream, PP, QQ, pps, qqs, meta,
+                       (int64_t)plan.rows_per_entry, draft, uniforms, K, V, C, esum, out_tokens, out_n);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(accept_entry_kernel, dim3(B), dim3(kEntryThreads), 0, stream, PP, QQ, pps, qqs, meta,
                      (int64_t)plan.rows_per_entry, draft, uniforms, K, V, out_tokens, out_n);
   return hipGetLastError();

@@ -320,7 +320,7 @@ size_t vq_spec_accept_workspace(int B, int K, int V, int input_kind, int64_t p_b
                                 int64_t q_batch_stride) {
   if (!accept_shape_ok(B, K, V, input_kind, p_batch_stride, q_batch_stride)) return 0;
   const vq::AcceptPlan p = vq::accept_plan(B, K, V, input_kind, p_batch_stride, q_batch_stride);
-  return p.meta_bytes + p.probs_bytes + p.table_bytes;
+  return vq::accept_workspace_total(p);
 }
 
 int vq_spec_accept(const float* p, const float* q, int input_kind, int64_t p_batch_stride, int64_t q_batch_stride,
@@ -345,7 +345,7 @@ int vq_spec_accept(const float* p, const float* q, int input_kind, int64_t p_bat
       !aligned(out_tokens, 4) || !aligned(out_n_accepted, 4) || (probs_out && !aligned(probs_out, 4)))
     return fail(VQ_ERR_INVALID_ARG, "vq_spec_accept: misaligned pointer");
   const vq::AcceptPlan plan = vq::accept_plan(B, K, V, input_kind, p_batch_stride, q_batch_stride);
-  int rc = check_workspace(workspace, workspace_bytes, plan.meta_bytes + plan.probs_bytes + plan.table_bytes);
+  int rc = check_workspace(workspace, workspace_bytes, vq::accept_workspace_total(plan));
   if (rc) return rc;
   if ((rc = check_device())) return rc;
   hipError_t e = vq::accept_launch(plan, p, q, input_kind, p_batch_stride, q_batch_stride, draft, uniforms, B, K, V,

@@ -82,8 +82,18 @@ struct AcceptPlan {
   size_t meta_bytes;  // per-row results of truncation
   size_t probs_bytes; // float32 probabilities (logits mode without probs_out)
   size_t table_bytes; // shared mode: 128-bit running sums [K+1][V]
+  // Chunked pipeline (few rows): rows and draws cut into chunks over the whole chip.
+  bool chunked;        // rows stage chunked
+  bool draw_chunked;   // draw stage chunked
+  int chunks;          // chunks per row
+  size_t state_bytes;  // per-row select state
+  size_t hist_bytes;   // per-row 4096-bin histograms, counts and masses
+  size_t cand_bytes;   // per-row gathered keys
+  size_t stats_bytes;  // logits mode: per-chunk max and sum
+  size_t esum_bytes;   // per-(entry, chunk) sums of the draw weights
 };
 AcceptPlan accept_plan(int B, int K, int V, int input_kind, int64_t p_stride, int64_t q_stride);
+size_t accept_workspace_total(const AcceptPlan& plan);
 hipError_t accept_launch(const AcceptPlan& plan, const float* p, const float* q, int input_kind,
                          int64_t p_stride, int64_t q_stride, const int32_t* draft,
                          const float* uniforms, int B, int K, int V, float temperature, int top_k,

@@ -137,3 +137,26 @@ def test_logits_mode(vq, V, T, top_k, top_p):
     assert np.all(err <= 1e-4 * ref + 1e-12), float((err / (ref + 1e-30)).max())
     toks, n = toks.cpu().numpy().astype(np.int64), n.cpu().numpy().astype(np.int64)
     pins_accept.check_distribution(tr["sr"], toks, n, K, V)
+
+
+@pytest.mark.parametrize("top_k,top_p", [(20, 0.95), (0, 0.95), (0, 1.0)])
+def test_many_entries_per_row_path(vq, top_k, top_p):
+    """Enough verifies that every row gets its own workgroup (no chunked stages)."""
+    P, Q, D, U = _entries(0, 160, 3, 500, 1.0, top_k, top_p, corr=0.5)
+    got = _gpu(vq, P, Q, D, U, top_k=top_k, top_p=top_p)
+    ref = _oracle(P, Q, D, U, top_k, top_p)
+    assert np.array_equal(got[1], ref[1]) and np.array_equal(got[0], ref[0])
+
+
+@pytest.mark.parametrize("top_k,top_p", [(0, 0.9), (30000, 0.9), (0, 1.0), (100, 1.0)])
+def test_crowded_rows(vq, top_k, top_p):
+    """Uniform target rows put every key in one histogram bin: more keys than the
+    chunked selects gather, so those rows take the single-workgroup path."""
+    K, V = 2, 40000
+    P, Q, D, U = _entries(5, 4, K, V, 1.0, top_k, top_p)
+    P[0, :, :] = oacc.probs_f32(np.zeros((K + 1, V), np.float32), 1.0)
+    P[2, 1, :] = P[0, 1, :]
+    Q[3, 0, :] = oacc.probs_f32(np.zeros((1, V), np.float32), 1.0)[0]
+    got = _gpu(vq, P, Q, D, U, top_k=top_k, top_p=top_p)
+    ref = _oracle(P, Q, D, U, top_k, top_p)
+    assert np.array_equal(got[1], ref[1]) and np.array_equal(got[0], ref[0])
