@@ -209,6 +209,24 @@ int vq_multirow_attn_append(const void* q, int64_t q_row_stride, const void* k_n
                             int D, int T, float scale, void* out, int64_t out_row_stride,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Tree verify (page "Speculative decoding and MTP on Apple silicon", Facts:
+ * tree verify runs the full-attention layers with tree-attention masks). The
+ * M rows are the nodes of a draft tree at cache positions T-M .. T-1 (node i at
+ * T-M+i); row i sees every committed position j < T-M and the drafted
+ * position T-M+t iff t == i or bit t of tree_mask[i] is set — its ancestors.
+ * Bits at or above M are ignored. tree_mask: device uint32 [M], 4-byte
+ * aligned, read by the call (it may change between graph replays). A chain
+ * (tree_mask[i] = 2^(i+1) - 1) gives vq_multirow_attn's causal result.
+ * k_new and v_new are both NULL (the caches already hold the M rows; they are
+ * then only read) or both given (the append of vq_multirow_attn_append, with
+ * its rules). Everything else is as vq_multirow_attn, with the same workspace. */
+int vq_multirow_attn_tree(const void* q, int64_t q_row_stride, const void* k_new,
+                          const void* v_new, int64_t new_row_stride, void* k_cache,
+                          void* v_cache, int64_t kv_head_stride, int M, int Hq, int Hkv,
+                          int D, int T, float scale, const uint32_t* tree_mask, void* out,
+                          int64_t out_row_stride, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* ------------------------------------------------------------------------
  * Exact speculative acceptance
  *

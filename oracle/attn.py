@@ -68,6 +68,50 @@ def multirow_attention(q, k_cache, v_cache, M: int, Hq: int, Hkv: int, D: int, T
     return res
 
 
+# ------------------------------------------------------------------ tree verify
+# Tree verify (page "Speculative decoding and MTP on Apple silicon", Facts: the
+# full-attention layers of a tree verify run with tree-attention masks): the M
+# verify rows are the nodes of a draft tree instead of a chain. Readings where
+# the page is silent:
+#   * the nodes occupy the last M of the T valid positions, node i at T - M + i;
+#   * node i sees every committed position (j < T - M) and node t iff bit t of
+#     mask[i] is set — its ancestors; a node always sees itself, and bits at or
+#     above M are ignored;
+#   * the chain mask (bits 0..i for node i) is the causal case above.
+
+def visible_keys(M: int, T: int, mask, m: int) -> np.ndarray:
+    """Key indices row m sees, in increasing order."""
+    bits = int(mask[m]) | (1 << m)
+    return np.array(list(range(T - M)) + [T - M + t for t in range(M) if (bits >> t) & 1], dtype=np.int64)
+
+
+def tree_attention_weights(q, k_cache, M: int, Hq: int, Hkv: int, D: int, T: int, T_cap: int,
+                           scale: float, mask, m: int, h: int) -> np.ndarray:
+    """float64 softmax weights w[j] (length T, zero where not visible) of row m, head h."""
+    G = Hq // Hkv
+    Q = bf16_to_f64(q).reshape(M, Hq, D)
+    Kc = _kv(k_cache, Hkv, T_cap, D, T)
+    idx = visible_keys(M, T, mask, m)
+    s = scale * (Kc[h // G, idx, :] @ Q[m, h, :])
+    e = np.exp(s - s.max())
+    w = np.zeros(T)
+    w[idx] = e / e.sum()
+    return w
+
+
+def tree_attention(q, k_cache, v_cache, M: int, Hq: int, Hkv: int, D: int, T: int, T_cap: int,
+                   scale: float, mask, pairs=None) -> np.ndarray:
+    """float64 output o[M, Hq, D] of tree verify (or the listed (m, h) rows only)."""
+    Vc = _kv(v_cache, Hkv, T_cap, D, T)
+    G = Hq // Hkv
+    todo = [(m, h) for m in range(M) for h in range(Hq)] if pairs is None else list(pairs)
+    res = np.empty((len(todo), D))
+    for i, (m, h) in enumerate(todo):
+        w = tree_attention_weights(q, k_cache, M, Hq, Hkv, D, T, T_cap, scale, mask, m, h)
+        res[i] = w @ Vc[h // G]
+    return res.reshape(M, Hq, D) if pairs is None else res
+
+
 def algorithmic_bytes(M: int, Hq: int, Hkv: int, D: int, T: int) -> int:
     """K and V rows read once per KV head, plus Q in and O out (bf16)."""
     return 4 * Hkv * T * D + 4 * M * Hq * D

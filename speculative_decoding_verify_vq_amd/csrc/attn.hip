@@ -24,6 +24,13 @@
 // same S tile, which costs MFMA time the memory-bound kernel has to spare).
 // With several key ranges per head, unnormalised partial O and the (max, sum)
 // statistics go to the workspace and a combine kernel merges them.
+//
+// Tree verify (page "Speculative decoding and MTP on Apple silicon", Facts:
+// tree-attention masks on the full-attention layers): with a mask, row i sees
+// the committed keys j < T-M and the drafted key T-M+t iff t == i or bit t of
+// mask[i] is set (bits at or above M are ignored); without one, bits 0..i
+// (causal). Each lane keeps its row's bits, so the mask costs one compare per
+// score.
 #include <math.h>
 
 #include "vq_internal.h"
@@ -65,7 +72,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     const uint16_t* __restrict__ q, int64_t q_rs, const uint16_t* kc, const uint16_t* vc, int64_t kv_head_stride,
     int M, int Hq, int Hkv, int T, float scale_log2, int keys_per_split, int splits, uint16_t* __restrict__ out,
     int64_t out_rs, float* __restrict__ part_o, float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
-    const uint16_t* __restrict__ v_new, int64_t new_rs, uint16_t* kc_w, uint16_t* vc_w) {
+    const uint16_t* __restrict__ v_new, int64_t new_rs, uint16_t* kc_w, uint16_t* vc_w,
+    const uint32_t* __restrict__ tree) {
   using C = AttnCfg<D, RT>;
   __shared__ uint16_t q_lds[RT * 32 * C::LD];
   __shared__ uint16_t k_lds[kTileKeys * C::LD];
@@ -154,7 +162,9 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
   const int row = rt * 32 + l32;             // this lane's query row (softmax owner)
   const bool row_ok = row < rows;
   const int mpos = row_ok ? row / G : 0;
-  const int limit = row_ok ? T - M + mpos : T - 1;  // last visible key of the row
+  // Drafted keys T-M+t this lane's row sees: bit t (the row itself always).
+  const uint32_t seen = (tree ? tree[mpos] : (0xFFFFFFFFu >> (31 - mpos))) | (1u << mpos);
+  const int t_new = T - M;  // first drafted key
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[C::DT];
@@ -177,7 +187,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = t0 + 8 * (r >> 2) + 4 * kq + (r & 3);
-      const float v = (j < j1 && j <= limit) ? s[r] * scale_log2 : -INFINITY;
+      const bool vis = j < j1 && (j < t_new || ((seen >> (j - t_new)) & 1u));
+      const float v = vis ? s[r] * scale_log2 : -INFINITY;
       s[r] = v;
       mx = fmaxf(mx, v);
     }
@@ -387,7 +398,7 @@ AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T) {
 hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const void* k, const void* v,
                        int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T, float scale,
                        void* out, int64_t out_rs, void* workspace, hipStream_t stream, const void* k_new,
-                       const void* v_new, int64_t new_rs) {
+                       const void* v_new, int64_t new_rs, const uint32_t* tree) {
   auto* kn = reinterpret_cast<const uint16_t*>(k_new);
   auto* vn = reinterpret_cast<const uint16_t*>(v_new);
   // With an append the caches are written (rows T-M .. T-1) as well as read.
@@ -406,7 +417,7 @@ hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const 
 #define VQ_ATTN(DV, RTV)                                                                        \
   hipLaunchKernelGGL((attn_partial_kernel<DV, RTV>), grid, dim3(kThreads), 0, stream, qp, q_rs, kp, vp, \
                      kv_head_stride, M, Hq, Hkv, T, sl2, plan.keys_per_split, plan.splits, op,         \
-                     out_rs, part_o, part_ml, kn, vn, new_rs, kw, vw)
+                     out_rs, part_o, part_ml, kn, vn, new_rs, kw, vw, tree)
 #define VQ_ATTN_RT(DV)                         \
   switch (plan.row_tiles) {                    \
     case 1: VQ_ATTN(DV, 1); break;             \

@@ -255,31 +255,64 @@ size_t vq_multirow_attn_workspace(int M, int Hq, int Hkv, int D, int T) {
   return vq::attn_plan(M, Hq, Hkv, D, T).partial_bytes;
 }
 
-int vq_multirow_attn(const void* q, int64_t q_row_stride, const void* k_cache, const void* v_cache,
-                     int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T, float scale, void* out,
-                     int64_t out_row_stride, void* workspace, size_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
-  if (!q || !k_cache || !v_cache || !out) return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn: NULL data pointer");
+namespace {
+
+// Checks shared by the attention entry points; `who` names the call.
+int attn_checks(const char* who, const void* q, int64_t q_row_stride, const void* k_cache, const void* v_cache,
+                int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T, float scale, const void* out,
+                int64_t out_row_stride) {
+  if (!q || !k_cache || !v_cache || !out) return fail(VQ_ERR_INVALID_ARG, "%s: NULL data pointer", who);
   if (!attn_shape_ok(M, Hq, Hkv, D, T))
     return fail(VQ_ERR_INVALID_ARG,
-                "vq_multirow_attn: unsupported shape M=%d Hq=%d Hkv=%d D=%d T=%d (M in [1,16], Hq %% Hkv == 0, "
+                "%s: unsupported shape M=%d Hq=%d Hkv=%d D=%d T=%d (M in [1,16], Hq %% Hkv == 0, "
                 "M*Hq/Hkv <= 128, D in {64,128,256}, T >= M)",
-                M, Hq, Hkv, D, T);
+                who, M, Hq, Hkv, D, T);
   if (kv_head_stride < (int64_t)T * D || kv_head_stride % 8 != 0)
-    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn: kv_head_stride must be >= T*D and a multiple of 8");
+    return fail(VQ_ERR_INVALID_ARG, "%s: kv_head_stride must be >= T*D and a multiple of 8", who);
   if (q_row_stride < (int64_t)Hq * D || q_row_stride % 8 != 0 || out_row_stride < (int64_t)Hq * D ||
       out_row_stride % 8 != 0)
-    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn: row strides must be >= Hq*D and multiples of 8");
-  if (!isfinite(scale)) return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn: scale must be finite");
+    return fail(VQ_ERR_INVALID_ARG, "%s: row strides must be >= Hq*D and multiples of 8", who);
+  if (!isfinite(scale)) return fail(VQ_ERR_INVALID_ARG, "%s: scale must be finite", who);
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
-    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn: q, caches and out must be 16-byte aligned");
+    return fail(VQ_ERR_INVALID_ARG, "%s: q, caches and out must be 16-byte aligned", who);
+  return VQ_OK;
+}
+
+int append_checks(const char* who, const void* k_new, const void* v_new, int64_t new_row_stride, int Hkv, int D) {
+  if (!k_new || !v_new) return fail(VQ_ERR_INVALID_ARG, "%s: NULL k_new or v_new", who);
+  if (new_row_stride < (int64_t)Hkv * D || new_row_stride % 8 != 0)
+    return fail(VQ_ERR_INVALID_ARG, "%s: new_row_stride must be >= Hkv*D and a multiple of 8", who);
+  if (!aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(VQ_ERR_INVALID_ARG, "%s: k_new and v_new must be 16-byte aligned", who);
+  return VQ_OK;
+}
+
+int attn_run(const char* who, const void* q, int64_t q_row_stride, const void* k_new, const void* v_new,
+             int64_t new_row_stride, const void* k_cache, const void* v_cache, int64_t kv_head_stride, int M, int Hq,
+             int Hkv, int D, int T, float scale, const uint32_t* tree_mask, void* out, int64_t out_row_stride,
+             void* workspace, size_t workspace_bytes, void* stream) {
   const vq::AttnPlan plan = vq::attn_plan(M, Hq, Hkv, D, T);
   int rc = check_workspace(workspace, workspace_bytes, plan.partial_bytes);
   if (rc) return rc;
   if ((rc = check_device())) return rc;
   hipError_t e = vq::attn_launch(plan, q, q_row_stride, k_cache, v_cache, kv_head_stride, M, Hq, Hkv, D, T, scale,
-                                 out, out_row_stride, workspace, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_multirow_attn launch");
+                                 out, out_row_stride, workspace, reinterpret_cast<hipStream_t>(stream), k_new, v_new,
+                                 new_row_stride, tree_mask);
+  return e == hipSuccess ? VQ_OK : hip_fail(e, who);
+}
+
+}  // namespace
+
+int vq_multirow_attn(const void* q, int64_t q_row_stride, const void* k_cache, const void* v_cache,
+                     int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T, float scale, void* out,
+                     int64_t out_row_stride, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "vq_multirow_attn";
+  int rc = attn_checks(who, q, q_row_stride, k_cache, v_cache, kv_head_stride, M, Hq, Hkv, D, T, scale, out,
+                       out_row_stride);
+  if (rc) return rc;
+  return attn_run(who, q, q_row_stride, nullptr, nullptr, 0, k_cache, v_cache, kv_head_stride, M, Hq, Hkv, D, T,
+                  scale, nullptr, out, out_row_stride, workspace, workspace_bytes, stream);
 }
 
 int vq_multirow_attn_append(const void* q, int64_t q_row_stride, const void* k_new, const void* v_new,
@@ -287,32 +320,32 @@ int vq_multirow_attn_append(const void* q, int64_t q_row_stride, const void* k_n
                             int Hq, int Hkv, int D, int T, float scale, void* out, int64_t out_row_stride,
                             void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  if (!k_new || !v_new) return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: NULL k_new or v_new");
-  if (new_row_stride < (int64_t)Hkv * D || new_row_stride % 8 != 0)
-    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: new_row_stride must be >= Hkv*D and a multiple of 8");
-  if (!aligned(k_new, 16) || !aligned(v_new, 16))
-    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: k_new and v_new must be 16-byte aligned");
-  if (!q || !k_cache || !v_cache || !out)
-    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: NULL data pointer");
-  if (!attn_shape_ok(M, Hq, Hkv, D, T))
-    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: unsupported shape M=%d Hq=%d Hkv=%d D=%d T=%d", M, Hq,
-                Hkv, D, T);
-  if (kv_head_stride < (int64_t)T * D || kv_head_stride % 8 != 0)
-    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: kv_head_stride must be >= T*D and a multiple of 8");
-  if (q_row_stride < (int64_t)Hq * D || q_row_stride % 8 != 0 || out_row_stride < (int64_t)Hq * D ||
-      out_row_stride % 8 != 0)
-    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: row strides must be >= Hq*D and multiples of 8");
-  if (!isfinite(scale)) return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: scale must be finite");
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
-    return fail(VQ_ERR_INVALID_ARG, "vq_multirow_attn_append: q, caches and out must be 16-byte aligned");
-  const vq::AttnPlan plan = vq::attn_plan(M, Hq, Hkv, D, T);
-  int rc = check_workspace(workspace, workspace_bytes, plan.partial_bytes);
+  const char* who = "vq_multirow_attn_append";
+  int rc = append_checks(who, k_new, v_new, new_row_stride, Hkv, D);
+  if (!rc)
+    rc = attn_checks(who, q, q_row_stride, k_cache, v_cache, kv_head_stride, M, Hq, Hkv, D, T, scale, out,
+                     out_row_stride);
   if (rc) return rc;
-  if ((rc = check_device())) return rc;
-  hipError_t e = vq::attn_launch(plan, q, q_row_stride, k_cache, v_cache, kv_head_stride, M, Hq, Hkv, D, T, scale,
-                                 out, out_row_stride, workspace, reinterpret_cast<hipStream_t>(stream), k_new, v_new,
-                                 new_row_stride);
-  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_multirow_attn_append launch");
+  return attn_run(who, q, q_row_stride, k_new, v_new, new_row_stride, k_cache, v_cache, kv_head_stride, M, Hq, Hkv,
+                  D, T, scale, nullptr, out, out_row_stride, workspace, workspace_bytes, stream);
+}
+
+int vq_multirow_attn_tree(const void* q, int64_t q_row_stride, const void* k_new, const void* v_new,
+                          int64_t new_row_stride, void* k_cache, void* v_cache, int64_t kv_head_stride, int M,
+                          int Hq, int Hkv, int D, int T, float scale, const uint32_t* tree_mask, void* out,
+                          int64_t out_row_stride, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "vq_multirow_attn_tree";
+  if (!tree_mask) return fail(VQ_ERR_INVALID_ARG, "%s: tree_mask is NULL", who);
+  if (!aligned(tree_mask, 4)) return fail(VQ_ERR_INVALID_ARG, "%s: misaligned tree_mask", who);
+  int rc = VQ_OK;
+  if (k_new || v_new) rc = append_checks(who, k_new, v_new, new_row_stride, Hkv, D);
+  if (!rc)
+    rc = attn_checks(who, q, q_row_stride, k_cache, v_cache, kv_head_stride, M, Hq, Hkv, D, T, scale, out,
+                     out_row_stride);
+  if (rc) return rc;
+  return attn_run(who, q, q_row_stride, k_new, v_new, new_row_stride, k_cache, v_cache, kv_head_stride, M, Hq, Hkv,
+                  D, T, scale, tree_mask, out, out_row_stride, workspace, workspace_bytes, stream);
 }
 
 // ----------------------------------------------------------- acceptance

@@ -72,7 +72,8 @@ AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T);
 hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const void* k, const void* v,
                        int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T, float scale,
                        void* out, int64_t out_rs, void* workspace, hipStream_t stream,
-                       const void* k_new = nullptr, const void* v_new = nullptr, int64_t new_rs = 0);
+                       const void* k_new = nullptr, const void* v_new = nullptr, int64_t new_rs = 0,
+                       const uint32_t* tree = nullptr);
 
 // ---------------------------------------------------------- acceptance
 struct AcceptPlan {

@@ -50,6 +50,8 @@ _proto("vq_multirow_attn_workspace", _SZ, [_I, _I, _I, _I, _I])
 _proto("vq_multirow_attn", _I, [_P, _I64, _P, _P, _I64, _I, _I, _I, _I, _I, _F, _P, _I64, _P, _SZ, _P])
 _proto("vq_multirow_attn_append", _I, [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I, _I, _I, _I, _I, _F, _P, _I64, _P,
                                        _SZ, _P])
+_proto("vq_multirow_attn_tree", _I, [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _I64, _P,
+                                     _SZ, _P])
 _proto("vq_spec_accept_workspace", _SZ, [_I, _I, _I, _I, _I64, _I64])
 _proto("vq_spec_accept", _I, [_P, _P, _I, _I64, _I64, _P, _P, _I, _I, _I, _F, _I, _F, _P, _P, _P, _P, _SZ, _P])
 _proto("vq_rmsnorm_bf16", _I, [_P, _I64, _P, _I64, _I, _I, _F, _P])
@@ -223,11 +225,13 @@ def attn_workspace_bytes(M: int, Hq: int, Hkv: int, D: int, T: int) -> int:
 def multirow_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, T: int,
                   scale: float | None = None, out: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None, stream=None, k_new: torch.Tensor | None = None,
-                  v_new: torch.Tensor | None = None) -> torch.Tensor:
+                  v_new: torch.Tensor | None = None, tree_mask: torch.Tensor | None = None) -> torch.Tensor:
     """q [M, Hq, D] bf16 (heads of a row contiguous; any row stride); caches
     [Hkv, T_cap, D] bf16 (row-contiguous); returns out [M, Hq, D]. With k_new and
     v_new ([M, >= Hkv*D] rows, same row stride) the M rows are appended at cache
-    positions T-M .. T-1 inside the call (vq_multirow_attn_append)."""
+    positions T-M .. T-1 inside the call (vq_multirow_attn_append). With
+    tree_mask (int32/uint32 device tensor [M] of ancestor bits) the rows are the
+    nodes of a draft tree (vq_multirow_attn_tree)."""
     M, Hq, D = q.shape
     Hkv = k_cache.shape[0]
     if scale is None:
@@ -237,7 +241,16 @@ def multirow_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     need = attn_workspace_bytes(M, Hq, Hkv, D, T)
     ws = _ws(need, q.device, workspace, "attn")
     wsz = 0 if ws is None else ws.numel() * ws.element_size()
-    if k_new is None:
+    if tree_mask is not None:
+        if (k_new is None) != (v_new is None) or (k_new is not None and k_new.stride(0) != v_new.stride(0)):
+            raise ValueError("k_new and v_new go together, with the same row stride")
+        rc = lib.vq_multirow_attn_tree(q.data_ptr(), q.stride(0), _ptr(k_new), _ptr(v_new),
+                                       0 if k_new is None else k_new.stride(0), k_cache.data_ptr(),
+                                       v_cache.data_ptr(), k_cache.stride(0), M, Hq, Hkv, D, T, float(scale),
+                                       tree_mask.data_ptr(), out.data_ptr(), out.stride(0), _ptr(ws), wsz,
+                                       _stream(stream))
+        _check("vq_multirow_attn_tree", rc)
+    elif k_new is None:
         rc = lib.vq_multirow_attn(q.data_ptr(), q.stride(0), k_cache.data_ptr(), v_cache.data_ptr(),
                                   k_cache.stride(0), M, Hq, Hkv, D, T, float(scale), out.data_ptr(), out.stride(0),
                                   _ptr(ws), wsz, _stream(stream))

@@ -19,7 +19,7 @@ import numpy as np
 STREAMS = {
     "W": 1, "S": 2, "B": 3, "X": 4,
     "Q": 5, "K": 6, "V": 7,
-    "plogit": 8, "qlogit": 9, "draft-u": 10, "accept-u": 11,
+    "plogit": 8, "qlogit": 9, "draft-u": 10, "accept-u": 11, "tree": 12,
 }
 
 U_BITS = 24  # uniforms are k * 2**-24, k uniform in [0, 2**24)
@@ -83,6 +83,24 @@ def attn_inputs(config: int, M: int, Hq: int, Hkv: int, D: int, T_cap: int,
     k = bf16_normal(rng(config, "K", seed, extra), (Hkv, T_cap, D))
     v = bf16_normal(rng(config, "V", seed, extra), (Hkv, T_cap, D))
     return q, k, v
+
+
+def tree_masks(config: int, M: int, seed: int = 0, extra: int = 0) -> np.ndarray:
+    """Ancestor masks of a random draft tree of M nodes in topological order:
+    node 0 is the root, node i > 0 hangs under a uniformly drawn earlier node, and
+    mask[i] has bit t set for every node t on the path from the root to i
+    (i included). uint32 [M]."""
+    g = rng(config, "tree", seed, extra)
+    mask = np.zeros(M, dtype=np.uint32)
+    for i in range(M):
+        parent = int(g.integers(0, i)) if i > 0 else -1
+        mask[i] = (int(mask[parent]) if parent >= 0 else 0) | (1 << i)
+    return mask
+
+
+def chain_masks(M: int) -> np.ndarray:
+    """The masks of a chain (node i under node i - 1): bits 0..i."""
+    return np.array([(1 << (i + 1)) - 1 for i in range(M)], dtype=np.uint32)
 
 
 # -------------------------------------------------------------------- acceptance

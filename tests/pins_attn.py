@@ -130,4 +130,105 @@ def pin_causality(mod):
         assert not np.array_equal(out[a["M"] - 1], base[a["M"] - 1])
 
 
-PINS = [pin_rows_sum_to_one, pin_bruteforce, pin_textbook, pin_special_cases, pin_causality]
+# ------------------------------------------------------------------ tree verify
+def tree_bruteforce(q, k, v, M, Hq, Hkv, D, T, T_cap, scale, mask):
+    """Pure-Python loops with math.exp: row i sees keys j < T - M, and key T - M + t
+    when t == i or bit t of mask[i] is set (t < M)."""
+    G = Hq // Hkv
+    out = np.zeros((M, Hq, D))
+    for i in range(M):
+        vis = [j for j in range(T - M)]
+        for t in range(M):
+            if t == i or (int(mask[i]) >> t) & 1:
+                vis.append(T - M + t)
+        for h in range(Hq):
+            kv = h // G
+            s = [scale * sum(_f(q[i, h, d]) * _f(k[kv, j, d]) for d in range(D)) for j in vis]
+            mx = max(s)
+            e = [math.exp(t - mx) for t in s]
+            z = sum(e)
+            for d in range(D):
+                out[i, h, d] = sum(e[n] / z * _f(v[kv, j, d]) for n, j in enumerate(vis))
+    return out
+
+
+def tree_textbook(q, k, v, M, Hq, Hkv, D, T, T_cap, scale, mask):
+    """softmax(scale * Q K^T + tree mask) V, the [M, T] mask built with numpy bit operations."""
+    G = Hq // Hkv
+    wid = lambda a: (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    Q = wid(q).reshape(M, Hq, D).transpose(1, 0, 2)
+    Kr = np.repeat(wid(k).reshape(Hkv, T_cap, D)[:, :T], G, axis=0)
+    Vr = np.repeat(wid(v).reshape(Hkv, T_cap, D)[:, :T], G, axis=0)
+    S = scale * Q @ Kr.transpose(0, 2, 1)
+    bits = (np.asarray(mask, np.uint64)[:, None] >> np.arange(M, dtype=np.uint64)[None, :]) & 1
+    seen = np.concatenate([np.ones((M, T - M), bool), (bits == 1) | np.eye(M, dtype=bool)], axis=1)
+    S = np.where(seen[None], S, -np.inf)
+    S = S - S.max(axis=-1, keepdims=True)
+    W = np.exp(S)
+    W /= W.sum(axis=-1, keepdims=True)
+    return (W @ Vr).transpose(1, 0, 2)
+
+
+def pin_tree_chain_is_causal(mod):
+    """The chain mask is the causal case, value for value."""
+    from synth import chain_masks
+    q, k, v, a = _small(11, M=5, Hq=6, Hkv=2, D=16, T=30, T_cap=32)
+    got = mod.tree_attention(q, k, v, **a, mask=chain_masks(a["M"]))
+    assert np.allclose(got, mod.multirow_attention(q, k, v, **a), rtol=0, atol=1e-15)
+
+
+def pin_tree_bruteforce(mod):
+    from synth import tree_masks
+    for seed, M in ((12, 5), (13, 4)):
+        q, k, v, a = _small(seed, M=M, Hq=4, Hkv=2, D=8, T=12, T_cap=14)
+        mask = tree_masks(seed, M)
+        ref = tree_bruteforce(q, k, v, **a, mask=mask)
+        assert np.allclose(mod.tree_attention(q, k, v, **a, mask=mask), ref, rtol=0, atol=1e-12)
+
+
+def pin_tree_textbook(mod):
+    """Random trees and arbitrary masks (self bit missing, bits at or above M set)."""
+    from synth import tree_masks
+    for seed, shape in ((14, dict(M=8, Hq=12, Hkv=2, D=32, T=90, T_cap=96)),
+                        (15, dict(M=16, Hq=4, Hkv=4, D=16, T=16, T_cap=16))):
+        q, k, v, a = _small(seed, **shape)
+        for mask in (tree_masks(seed, a["M"]), np.array([0, 0xFFFF0001, 5, 2, 0xF0] * 4, np.uint32)[: a["M"]]):
+            ref = tree_textbook(q, k, v, **a, mask=mask)
+            assert np.allclose(mod.tree_attention(q, k, v, **a, mask=mask), ref, rtol=0, atol=1e-12)
+            pairs = [(0, 0), (a["M"] - 1, a["Hq"] - 1)]
+            got = mod.tree_attention(q, k, v, **a, mask=mask, pairs=pairs)
+            assert np.allclose(got, np.stack([ref[m, h] for m, h in pairs]), rtol=0, atol=1e-12)
+
+
+def pin_tree_self_only_is_decode(mod):
+    """A node that sees only itself among the drafted rows is single-row decode
+    attention over the context followed by its own key and value."""
+    q, k, v, a = _small(16, M=4, Hq=4, Hkv=2, D=16, T=24, T_cap=24)
+    M, T = a["M"], a["T"]
+    mask = np.array([1 << i for i in range(M)], np.uint32)
+    got = mod.tree_attention(q, k, v, **a, mask=mask)
+    for i in range(M):
+        keep = list(range(T - M)) + [T - M + i]
+        k1, v1 = k[:, keep], v[:, keep]
+        one = mod.multirow_attention(q[i:i + 1], k1, v1, 1, a["Hq"], a["Hkv"], a["D"], len(keep), len(keep),
+                                     a["scale"])
+        assert np.allclose(got[i], one[0], rtol=0, atol=1e-13)
+
+
+def pin_tree_weights(mod):
+    """Weights sum to one, are zero exactly on the keys the node does not see."""
+    from synth import tree_masks
+    q, k, v, a = _small(17, M=8, Hq=4, Hkv=2, D=16, T=40, T_cap=40)
+    mask = tree_masks(17, a["M"])
+    for m in range(a["M"]):
+        w = mod.tree_attention_weights(q, k, a["M"], a["Hq"], a["Hkv"], a["D"], a["T"], a["T_cap"], a["scale"],
+                                       mask, m, 1)
+        assert abs(w.sum() - 1.0) <= 1e-12
+        seen = [t for t in range(a["M"]) if (int(mask[m]) >> t) & 1]
+        tail = w[a["T"] - a["M"]:]
+        assert np.all(tail[seen] > 0) and np.all(np.delete(tail, seen) == 0) and np.all(w[: a["T"] - a["M"]] > 0)
+
+
+PINS = [pin_rows_sum_to_one, pin_bruteforce, pin_textbook, pin_special_cases, pin_causality,
+        pin_tree_chain_is_causal, pin_tree_bruteforce, pin_tree_textbook, pin_tree_self_only_is_decode,
+        pin_tree_weights]

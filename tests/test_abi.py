@@ -172,3 +172,18 @@ def test_attn_append_rejects(vqmod, bad):
                                            a["M"], a["Hq"], a["Hkv"], a["D"], a["T"], a["scale"], a["out"],
                                            a["ors"], a["ws"], a["wsz"], None)
     assert rc == vqmod.VQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [
+    dict(mask=None), dict(mask=A16 + 2), dict(kn=None), dict(vn=None), dict(nrs=100), dict(q=None), dict(T=3),
+    dict(scale=float("inf")), dict(ws=None, T=100000), dict(M=17),
+])
+def test_attn_tree_rejects(vqmod, bad):
+    a = dict(q=A16, qrs=128, kn=A16, vn=A16, nrs=128, k=A16, v=A16, hs=256 * 64, M=4, Hq=2, Hkv=2, D=64, T=256,
+             scale=0.125, mask=A16, out=A16, ors=128, ws=A16, wsz=1 << 30)
+    a.update(bad)
+    rc = vqmod.lib.vq_multirow_attn_tree(a["q"], a["qrs"], a["kn"], a["vn"], a["nrs"], a["k"], a["v"], a["hs"],
+                                         a["M"], a["Hq"], a["Hkv"], a["D"], a["T"], a["scale"], a["mask"], a["out"],
+                                         a["ors"], a["ws"], a["wsz"], None)
+    assert rc == vqmod.VQ_ERR_INVALID_ARG
+    assert "vq_multirow_attn_tree" in vqmod.last_error()

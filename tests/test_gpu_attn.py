@@ -95,3 +95,91 @@ def test_append_fused(vq, M, Hq, Hkv, D, T, T_cap):
     assert_close(to_f64(out), ref, "append fused vs oracle")
     # rows past T untouched
     assert torch.equal(kc[:, T:], bf16_tensor(k)[:, T:])
+
+
+# ------------------------------------------------------------------ tree verify
+def _tree(vq, q, k, v, T, scale, mask, k_new=None, v_new=None, kc=None, vc=None):
+    from tests.gpu_util import i32_tensor
+    mt = i32_tensor(np.asarray(mask, np.uint32).view(np.int32))
+    kc = bf16_tensor(k) if kc is None else kc
+    vc = bf16_tensor(v) if vc is None else vc
+    out = vq.multirow_attn(bf16_tensor(q), kc, vc, T, scale, tree_mask=mt, k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("M,Hq,Hkv,D,T,T_cap", [
+    (4, 2, 2, 64, 256, 256),       # config 0 heads
+    (8, 12, 2, 64, 300, 300),      # GQA, 48 rows
+    (16, 8, 2, 128, 16, 16),       # T == M: only drafted keys
+    (16, 24, 4, 256, 200, 208),    # 27B heads, 96 rows per KV head
+    (5, 4, 4, 128, 3000, 3000),    # several key ranges, the tree in the last one
+    (1, 8, 8, 64, 70, 70),         # a single node
+])
+def test_tree_random(vq, M, Hq, Hkv, D, T, T_cap):
+    from synth import tree_masks
+    q, k, v = attn_inputs(23, M, Hq, Hkv, D, T_cap, extra=T)
+    mask = tree_masks(23, M, extra=T)
+    scale = 1 / math.sqrt(D)
+    got = to_f64(_tree(vq, q, k, v, T, scale, mask))
+    ref = oa.tree_attention(q, k, v, M, Hq, Hkv, D, T, T_cap, scale, mask)
+    assert_close(got, ref, f"tree M={M} Hq={Hq} Hkv={Hkv} D={D} T={T}")
+
+
+def test_tree_arbitrary_masks(vq):
+    """Masks that are not trees: the self bit missing, bits at or above M, all bits."""
+    M, Hq, Hkv, D, T = 8, 12, 2, 64, 100
+    q, k, v = attn_inputs(24, M, Hq, Hkv, D, T)
+    mask = np.array([0, 0xFFFFFFFF, 0x100, 5, 0xF0, 2, 0xFF, 1 << 31], np.uint32)
+    got = to_f64(_tree(vq, q, k, v, T, 0.125, mask))
+    assert_close(got, oa.tree_attention(q, k, v, M, Hq, Hkv, D, T, T, 0.125, mask), "arbitrary masks")
+
+
+@pytest.mark.parametrize("M,D,T", [(4, 64, 256), (8, 256, 5000), (16, 128, 16)])
+def test_tree_chain_equals_causal(vq, M, D, T):
+    """The chain mask gives the causal call's output bit for bit (same kernel, same
+    arithmetic)."""
+    from synth import chain_masks
+    Hq, Hkv = 8, 2
+    q, k, v = attn_inputs(25, M, Hq, Hkv, D, T, extra=T)
+    scale = 1 / math.sqrt(D)
+    tree = _tree(vq, q, k, v, T, scale, chain_masks(M))
+    causal = vq.multirow_attn(bf16_tensor(q), bf16_tensor(k), bf16_tensor(v), T, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(tree, causal)
+
+
+def test_tree_config2_sampled(vq):
+    """27B heads at 16k + 16 tree nodes: sampled (node, head) pairs against the oracle."""
+    from synth import tree_masks
+    M, Hq, Hkv, D, ctx = 16, 24, 4, 256, 16384
+    T = ctx + M
+    q, k, v = attn_inputs(26, M, Hq, Hkv, D, T)
+    mask = tree_masks(26, M)
+    out = to_f64(_tree(vq, q, k, v, T, 1 / 16, mask))
+    rng = np.random.default_rng(26)
+    pairs = [(m, int(h)) for m in range(M) for h in rng.choice(Hq, 2, replace=False)]
+    ref = oa.tree_attention(q, k, v, M, Hq, Hkv, D, T, T, 1 / 16, mask, pairs=pairs)
+    assert_close(np.stack([out[m, h] for m, h in pairs]), ref, "tree at 16k")
+
+
+def test_tree_with_append(vq):
+    """Tree verify with the append fused in: equals the tree call on a cache appended beforehand."""
+    from synth import tree_masks
+    import oracle.stack as ostack
+    M, Hq, Hkv, D, T = 8, 12, 2, 128, 2050
+    q, k, v = attn_inputs(27, M, Hq, Hkv, D, T + 4, extra=T)
+    mask = tree_masks(27, M)
+    new_bits = ostack.to_bf16_bits(np.random.default_rng(27).standard_normal((M, 2 * Hkv * D)))
+    src = bf16_tensor(new_bits)
+    k_new, v_new = src[:, : Hkv * D], src[:, Hkv * D:]
+    kc, vc = bf16_tensor(k), bf16_tensor(v)
+    out = _tree(vq, q, k, v, T, 0.1, mask, k_new=k_new, v_new=v_new, kc=kc, vc=vc)
+    kc2, vc2 = bf16_tensor(k), bf16_tensor(v)
+    vq.kv_append(src, 0, Hkv * D, kc2, vc2, T - M)
+    out2 = _tree(vq, q, k, v, T, 0.1, mask, kc=kc2, vc=vc2)
+    assert torch.equal(kc, kc2) and torch.equal(vc, vc2) and torch.equal(out, out2)
+    ka, va = k.copy(), v.copy()
+    ka[:, T - M: T] = new_bits[:, : Hkv * D].reshape(M, Hkv, D).transpose(1, 0, 2)
+    va[:, T - M: T] = new_bits[:, Hkv * D:].reshape(M, Hkv, D).transpose(1, 0, 2)
+    assert_close(to_f64(out), oa.tree_attention(q, ka, va, M, Hq, Hkv, D, T, T + 4, 0.1, mask), "tree + append")
