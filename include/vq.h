@@ -227,6 +227,38 @@ int vq_multirow_attn_tree(const void* q, int64_t q_row_stride, const void* k_new
                           int64_t out_row_stride, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* 8-bit KV cache (page "Speculative decoding and MTP on Apple silicon",
+ * Facts: KV-quantized caches are used together with speculative decoding; the
+ * format is not given and this one follows the affine group-64 quantization of
+ * the weights). Per KV head and position, the D values are cut into groups of
+ * 64; group g holds 64 codes q in [0, 255] and one uint32 word whose low half
+ * is the bf16 scale s and whose high half is the bf16 bias b: value = s*q + b.
+ *   k_codes, v_codes  u8 [Hkv, T_cap, D], head stride kv_head_stride (a
+ *                     multiple of D), 16-byte aligned;
+ *   k_sb, v_sb        uint32 [Hkv, T_cap, D/64], 4-byte aligned.
+ * vq_multirow_attn_int8 is vq_multirow_attn (tree_mask NULL) or
+ * vq_multirow_attn_tree without the append (tree_mask given) over the
+ * dequantized caches: scores, softmax and accumulation in float32 on the values
+ * s*q + b rounded to bf16. Workspace: vq_multirow_attn_workspace(). */
+int vq_multirow_attn_int8(const void* q, int64_t q_row_stride, const void* k_codes,
+                          const void* k_sb, const void* v_codes, const void* v_sb,
+                          int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T,
+                          float scale, const uint32_t* tree_mask, void* out,
+                          int64_t out_row_stride, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Quantizes M rows into an 8-bit cache at positions pos .. pos+M-1, the keys
+ * from src[m, k_off + h*D ...] and the values from src[m, v_off + h*D ...] (bf16
+ * rows, stride ld_src elements; the q|k|v projection output). Per group of 64:
+ * mn = min, mx = max, scale = (mx - mn) / 255 and code = rint((x - mn) / scale)
+ * (round half to even), both in correctly rounded float32, clamped to [0, 255];
+ * a constant group gets codes 0 and scale 0; stored scale = bf16(scale) (round
+ * to nearest even), bias = mn. kv_head_stride >= (pos + M) * D, a multiple of
+ * D. No workspace. */
+int vq_kv8_append(const void* src, int64_t ld_src, int k_off, int v_off, void* k_codes,
+                  void* k_sb, void* v_codes, void* v_sb, int64_t kv_head_stride, int M,
+                  int Hkv, int D, int pos, void* stream);
+
 /* ------------------------------------------------------------------------
  * Exact speculative acceptance
  *

@@ -25,6 +25,14 @@
 // With several key ranges per head, unnormalised partial O and the (max, sum)
 // statistics go to the workspace and a combine kernel merges them.
 //
+// 8-bit KV cache (same page, Facts: KV-quantized caches used together with
+// speculation): codes u8 [Hkv, T_cap, D] and one (bf16 scale, bf16 bias) word
+// per 64 codes; a tile is fetched as 16-code units with their word and
+// dequantized (s * q + b, rounded to bf16) while it is written to LDS, so
+// everything after the staging is the bf16 path. The append quantizes rows per
+// group: scale = (max - min) / 255 and code = rint((x - min) / scale), both in
+// correctly rounded float32, bias = min.
+//
 // Tree verify (page "Speculative decoding and MTP on Apple silicon", Facts:
 // tree-attention masks on the full-attention layers): with a mask, row i sees
 // the committed keys j < T-M and the drafted key T-M+t iff t == i or bit t of
@@ -56,25 +64,43 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
 }
 
-template <int D, int RT>
+template <int D, int RT, bool KV8 = false>
 struct AttnCfg {
   static constexpr int DS0 = (RT == 1) ? 4 : (RT == 2) ? 2 : 1;
   static constexpr int DS = DS0 < D / 32 ? DS0 : D / 32;  // head-dim slices per row tile
   static constexpr int DW = D / DS;                         // head dims per wave
   static constexpr int DT = DW / 32;                        // 32-wide d tiles per wave
   static constexpr int LD = D + 8;                          // LDS row stride (elements)
-  static constexpr int UNITS = kTileKeys * D / 8;           // 16-byte units per K (or V) tile
+  static constexpr int UPK = KV8 ? D / 16 : D / 8;         // 16-byte units per key row
+  static constexpr int UNITS = kTileKeys * UPK;             // 16-byte units per K (or V) tile
   static constexpr int PER_THREAD = (UNITS + kThreads - 1) / kThreads;
 };
 
-template <int D, int RT>
+// 16 codes and their (scale, bias) word -> 16 bf16 values s * q + b.
+__device__ __forceinline__ void dequant16(const u32x4 w, uint32_t sb, u32x4& lo, u32x4& hi) {
+  const float s = __uint_as_float(sb << 16);
+  const float b = __uint_as_float(sb & 0xFFFF0000u);
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t word = w[i >> 1];
+    const int sh = 16 * (i & 1);
+    const float f0 = __builtin_fmaf(s, (float)((word >> sh) & 0xFFu), b);
+    const float f1 = __builtin_fmaf(s, (float)((word >> (sh + 8)) & 0xFFu), b);
+    o[i] = pack_bf16x2(f0, f1);
+  }
+  lo = u32x4{o[0], o[1], o[2], o[3]};
+  hi = u32x4{o[4], o[5], o[6], o[7]};
+}
+
+template <int D, int RT, bool KV8>
 __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     const uint16_t* __restrict__ q, int64_t q_rs, const uint16_t* kc, const uint16_t* vc, int64_t kv_head_stride,
     int M, int Hq, int Hkv, int T, float scale_log2, int keys_per_split, int splits, uint16_t* __restrict__ out,
     int64_t out_rs, float* __restrict__ part_o, float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, int64_t new_rs, uint16_t* kc_w, uint16_t* vc_w,
-    const uint32_t* __restrict__ tree) {
-  using C = AttnCfg<D, RT>;
+    const uint32_t* __restrict__ tree, const uint32_t* __restrict__ ksb, const uint32_t* __restrict__ vsb) {
+  using C = AttnCfg<D, RT, KV8>;
   __shared__ uint16_t q_lds[RT * 32 * C::LD];
   __shared__ uint16_t k_lds[kTileKeys * C::LD];
   __shared__ uint16_t v_lds[kTileKeys * C::LD];
@@ -110,11 +136,23 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
   // so the wait counts the compiler derives stay exact.
   struct KV {
     u32x4 k[C::PER_THREAD], v[C::PER_THREAD];
+    uint32_t ks[KV8 ? C::PER_THREAD : 1], vs[KV8 ? C::PER_THREAD : 1];
   };
   KV r0, r1;
   auto fetch = [&](KV& r, int t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < C::PER_THREAD; ++e) {
+      if constexpr (KV8) {
+        const int u = min(tid + e * kThreads, C::UNITS - 1);
+        const int key = min(t0 + u / C::UPK, j1 - 1);
+        const int dc = u % C::UPK;
+        const size_t row = (size_t)kvh * kv_head_stride + (size_t)key * D;  // codes (bytes) before the row
+        r.k[e] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(kc) + row + dc * 16);
+        r.v[e] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(vc) + row + dc * 16);
+        r.ks[e] = ksb[row / 64 + dc / 4];
+        r.vs[e] = vsb[row / 64 + dc / 4];
+        continue;
+      }
       const int u = tid + e * kThreads;
       const int key = min(t0 + u / (D / 8), j1 - 1);
       const int dc = u % (D / 8);
@@ -132,6 +170,21 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < C::PER_THREAD; ++e) {
+      if constexpr (KV8) {
+        const int u = tid + e * kThreads;
+        if (u < C::UNITS) {
+          const int key = u / C::UPK;
+          const int dc = u % C::UPK;
+          u32x4 lo, hi;
+          dequant16(r.k[e], r.ks[e], lo, hi);
+          *reinterpret_cast<u32x4*>(&k_lds[key * C::LD + dc * 16]) = lo;
+          *reinterpret_cast<u32x4*>(&k_lds[key * C::LD + dc * 16 + 8]) = hi;
+          dequant16(r.v[e], r.vs[e], lo, hi);
+          *reinterpret_cast<u32x4*>(&v_lds[key * C::LD + dc * 16]) = lo;
+          *reinterpret_cast<u32x4*>(&v_lds[key * C::LD + dc * 16 + 8]) = hi;
+        }
+        continue;
+      }
       const int u = tid + e * kThreads;
       const int key = u / (D / 8);
       const int dc = u % (D / 8);
@@ -239,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
       }
     }
   };
-  static_assert(C::UNITS % kThreads == 0, "every thread moves whole 16-byte units of a tile");
+  static_assert(KV8 || C::UNITS % kThreads == 0, "every thread moves whole 16-byte units of a tile");
   for (int t0 = j0; t0 < j1; t0 += 2 * kTileKeys) {
     stage(r0);
     if (t0 + 2 * kTileKeys < j1) fetch(r0, t0 + 2 * kTileKeys);
@@ -398,7 +451,8 @@ AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T) {
 hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const void* k, const void* v,
                        int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T, float scale,
                        void* out, int64_t out_rs, void* workspace, hipStream_t stream, const void* k_new,
-                       const void* v_new, int64_t new_rs, const uint32_t* tree) {
+                       const void* v_new, int64_t new_rs, const uint32_t* tree, const uint32_t* k_sb,
+                       const uint32_t* v_sb) {
   auto* kn = reinterpret_cast<const uint16_t*>(k_new);
   auto* vn = reinterpret_cast<const uint16_t*>(v_new);
   // With an append the caches are written (rows T-M .. T-1) as well as read.
@@ -414,10 +468,16 @@ hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const 
   auto* vp = reinterpret_cast<const uint16_t*>(v);
   auto* op = reinterpret_cast<uint16_t*>(out);
   const float sl2 = scale * kLog2e;
-#define VQ_ATTN(DV, RTV)                                                                        \
-  hipLaunchKernelGGL((attn_partial_kernel<DV, RTV>), grid, dim3(kThreads), 0, stream, qp, q_rs, kp, vp, \
-                     kv_head_stride, M, Hq, Hkv, T, sl2, plan.keys_per_split, plan.splits, op,         \
-                     out_rs, part_o, part_ml, kn, vn, new_rs, kw, vw, tree)
+  const bool kv8 = k_sb != nullptr;
+#define VQ_ATTN(DV, RTV)                                                                                     \
+  if (kv8)                                                                                                   \
+    hipLaunchKernelGGL((attn_partial_kernel<DV, RTV, true>), grid, dim3(kThreads), 0, stream, qp, q_rs, kp, vp, \
+                       kv_head_stride, M, Hq, Hkv, T, sl2, plan.keys_per_split, plan.splits, op, out_rs, part_o,  \
+                       part_ml, kn, vn, new_rs, kw, vw, tree, k_sb, v_sb);                                       \
+  else                                                                                                       \
+    hipLaunchKernelGGL((attn_partial_kernel<DV, RTV, false>), grid, dim3(kThreads), 0, stream, qp, q_rs, kp, vp, \
+                       kv_head_stride, M, Hq, Hkv, T, sl2, plan.keys_per_split, plan.splits, op, out_rs, part_o,   \
+                       part_ml, kn, vn, new_rs, kw, vw, tree, nullptr, nullptr)
 #define VQ_ATTN_RT(DV)                         \
   switch (plan.row_tiles) {                    \
     case 1: VQ_ATTN(DV, 1); break;             \
@@ -441,4 +501,49 @@ hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const 
   return hipGetLastError();
 }
 
+
+namespace {
+
+// One wave per (row m, KV head h, group g of 64): the keys, then the values.
+__global__ __launch_bounds__(256) void kv8_append_kernel(const uint16_t* __restrict__ src, int64_t ld, int k_off,
+                                                         int v_off, uint8_t* __restrict__ kq, uint32_t* __restrict__ ks,
+                                                         uint8_t* __restrict__ vq, uint32_t* __restrict__ vs,
+                                                         int64_t hs, int M, int Hkv, int D, int pos) {
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int groups = D / 64;
+  if (w >= M * Hkv * groups) return;
+  const int m = w / (Hkv * groups);
+  const int h = (w / groups) % Hkv;
+  const int g = w % groups;
+  const size_t row = (size_t)h * hs + (size_t)(pos + m) * D;  // codes before the cache row
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const uint16_t* x16 = src + (int64_t)m * ld + (kv ? v_off : k_off) + h * D + g * 64;
+    const float x = __uint_as_float((uint32_t)x16[lane] << 16);
+    float mn = x, mx = x;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      mn = fminf(mn, __shfl_xor(mn, off));
+      mx = fmaxf(mx, __shfl_xor(mx, off));
+    }
+    const float scale = __fdiv_rn(__fsub_rn(mx, mn), 255.f);
+    uint32_t code = 0;
+    if (scale != 0.f) code = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x, mn), scale)), 0.f), 255.f);
+    (kv ? vq : kq)[row + g * 64 + lane] = (uint8_t)code;
+    if (lane == 0) (kv ? vs : ks)[row / 64 + g] = (uint32_t)f32_to_bf16_rne(scale) | ((uint32_t)f32_to_bf16_rne(mn) << 16);
+  }
+}
+
+}  // namespace
+
+hipError_t kv8_append(const void* src, int64_t ld, int k_off, int v_off, void* k_codes, void* k_sb, void* v_codes,
+                      void* v_sb, int64_t hs, int M, int Hkv, int D, int pos, hipStream_t stream) {
+  const int waves = M * Hkv * (D / 64);
+  hipLaunchKernelGGL(kv8_append_kernel, dim3((waves + 3) / 4), dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(src), ld, k_off, v_off, reinterpret_cast<uint8_t*>(k_codes),
+                     reinterpret_cast<uint32_t*>(k_sb), reinterpret_cast<uint8_t*>(v_codes),
+                     reinterpret_cast<uint32_t*>(v_sb), hs, M, Hkv, D, pos);
+  return hipGetLastError();
+}
 }  // namespace vq

@@ -348,6 +348,50 @@ int vq_multirow_attn_tree(const void* q, int64_t q_row_stride, const void* k_new
                   D, T, scale, tree_mask, out, out_row_stride, workspace, workspace_bytes, stream);
 }
 
+int vq_multirow_attn_int8(const void* q, int64_t q_row_stride, const void* k_codes, const void* k_sb,
+                          const void* v_codes, const void* v_sb, int64_t kv_head_stride, int M, int Hq, int Hkv,
+                          int D, int T, float scale, const uint32_t* tree_mask, void* out, int64_t out_row_stride,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "vq_multirow_attn_int8";
+  if (!k_sb || !v_sb) return fail(VQ_ERR_INVALID_ARG, "%s: NULL k_sb or v_sb", who);
+  if (!aligned(k_sb, 4) || !aligned(v_sb, 4) || (tree_mask && !aligned(tree_mask, 4)))
+    return fail(VQ_ERR_INVALID_ARG, "%s: misaligned k_sb, v_sb or tree_mask", who);
+  int rc = attn_checks(who, q, q_row_stride, k_codes, v_codes, kv_head_stride, M, Hq, Hkv, D, T, scale, out,
+                       out_row_stride);
+  if (rc) return rc;
+  if (kv_head_stride % D != 0)
+    return fail(VQ_ERR_INVALID_ARG, "%s: kv_head_stride must be a multiple of D (T_cap * D)", who);
+  const vq::AttnPlan plan = vq::attn_plan(M, Hq, Hkv, D, T);
+  if ((rc = check_workspace(workspace, workspace_bytes, plan.partial_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  hipError_t e = vq::attn_launch(plan, q, q_row_stride, k_codes, v_codes, kv_head_stride, M, Hq, Hkv, D, T, scale,
+                                 out, out_row_stride, workspace, reinterpret_cast<hipStream_t>(stream), nullptr,
+                                 nullptr, 0, tree_mask, reinterpret_cast<const uint32_t*>(k_sb),
+                                 reinterpret_cast<const uint32_t*>(v_sb));
+  return e == hipSuccess ? VQ_OK : hip_fail(e, who);
+}
+
+int vq_kv8_append(const void* src, int64_t ld_src, int k_off, int v_off, void* k_codes, void* k_sb, void* v_codes,
+                  void* v_sb, int64_t kv_head_stride, int M, int Hkv, int D, int pos, void* stream) {
+  g_err[0] = 0;
+  const char* who = "vq_kv8_append";
+  if (!src || !k_codes || !k_sb || !v_codes || !v_sb) return fail(VQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (M < 1 || M > VQ_MAX_ROWS || Hkv < 1 || (D != 64 && D != 128 && D != 256) || pos < 0)
+    return fail(VQ_ERR_INVALID_ARG, "%s: unsupported M=%d Hkv=%d D=%d pos=%d", who, M, Hkv, D, pos);
+  if (k_off < 0 || v_off < 0 || ld_src < (int64_t)(k_off > v_off ? k_off : v_off) + (int64_t)Hkv * D)
+    return fail(VQ_ERR_INVALID_ARG, "%s: k_off, v_off and ld_src must hold Hkv*D values per row", who);
+  if (kv_head_stride < (int64_t)(pos + M) * D || kv_head_stride % D != 0)
+    return fail(VQ_ERR_INVALID_ARG, "%s: kv_head_stride must be a multiple of D and hold pos + M rows", who);
+  if (!aligned(src, 2) || !aligned(k_sb, 4) || !aligned(v_sb, 4))
+    return fail(VQ_ERR_INVALID_ARG, "%s: misaligned src, k_sb or v_sb", who);
+  int rc;
+  if ((rc = check_device())) return rc;
+  hipError_t e = vq::kv8_append(src, ld_src, k_off, v_off, k_codes, k_sb, v_codes, v_sb, kv_head_stride, M, Hkv, D,
+                                pos, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VQ_OK : hip_fail(e, who);
+}
+
 // ----------------------------------------------------------- acceptance
 size_t vq_spec_accept_workspace(int B, int K, int V, int input_kind, int64_t p_batch_stride,
                                 int64_t q_batch_stride) {

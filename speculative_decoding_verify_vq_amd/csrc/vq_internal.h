@@ -73,7 +73,13 @@ hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const 
                        int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T, float scale,
                        void* out, int64_t out_rs, void* workspace, hipStream_t stream,
                        const void* k_new = nullptr, const void* v_new = nullptr, int64_t new_rs = 0,
-                       const uint32_t* tree = nullptr);
+                       const uint32_t* tree = nullptr, const uint32_t* k_sb = nullptr,
+                       const uint32_t* v_sb = nullptr);
+// 8-bit KV cache: quantize M rows of a fused projection output into the caches
+// (codes u8 [Hkv, T_cap, D], one bf16 scale | bf16 bias word per 64 codes) at
+// positions pos .. pos+M-1; hs = head stride of the codes (elements).
+hipError_t kv8_append(const void* src, int64_t ld, int k_off, int v_off, void* k_codes, void* k_sb, void* v_codes,
+                      void* v_sb, int64_t hs, int M, int Hkv, int D, int pos, hipStream_t stream);
 
 // ---------------------------------------------------------- acceptance
 struct AcceptPlan {

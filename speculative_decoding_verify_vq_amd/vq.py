@@ -52,6 +52,9 @@ _proto("vq_multirow_attn_append", _I, [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I,
                                        _SZ, _P])
 _proto("vq_multirow_attn_tree", _I, [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _I64, _P,
                                      _SZ, _P])
+_proto("vq_multirow_attn_int8", _I, [_P, _I64, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _I64, _P, _SZ,
+                                     _P])
+_proto("vq_kv8_append", _I, [_P, _I64, _I, _I, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _P])
 _proto("vq_spec_accept_workspace", _SZ, [_I, _I, _I, _I, _I64, _I64])
 _proto("vq_spec_accept", _I, [_P, _P, _I, _I64, _I64, _P, _P, _I, _I, _I, _F, _I, _F, _P, _P, _P, _P, _SZ, _P])
 _proto("vq_rmsnorm_bf16", _I, [_P, _I64, _P, _I64, _I, _I, _F, _P])
@@ -264,6 +267,38 @@ def multirow_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                          wsz, _stream(stream))
         _check("vq_multirow_attn_append", rc)
     return out
+
+
+def multirow_attn_int8(q: torch.Tensor, k_codes: torch.Tensor, k_sb: torch.Tensor, v_codes: torch.Tensor,
+                       v_sb: torch.Tensor, T: int, scale: float | None = None, out: torch.Tensor | None = None,
+                       tree_mask: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """Attention over an 8-bit KV cache (vq_multirow_attn_int8): codes uint8
+    [Hkv, T_cap, D]; k_sb, v_sb [Hkv, T_cap, D/64] 32-bit words (bf16 scale low,
+    bias high); q [M, Hq, D] bf16; optional tree_mask [M] (32-bit)."""
+    M, Hq, D = q.shape
+    Hkv = k_codes.shape[0]
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    ws = _ws(attn_workspace_bytes(M, Hq, Hkv, D, T), q.device, workspace, "attn")
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = lib.vq_multirow_attn_int8(q.data_ptr(), q.stride(0), k_codes.data_ptr(), k_sb.data_ptr(),
+                                   v_codes.data_ptr(), v_sb.data_ptr(), k_codes.stride(0), M, Hq, Hkv, D, T,
+                                   float(scale), _ptr(tree_mask), out.data_ptr(), out.stride(0), _ptr(ws), wsz,
+                                   _stream(stream))
+    _check("vq_multirow_attn_int8", rc)
+    return out
+
+
+def kv8_append(src: torch.Tensor, k_off: int, v_off: int, k_codes: torch.Tensor, k_sb: torch.Tensor,
+               v_codes: torch.Tensor, v_sb: torch.Tensor, pos: int, stream=None) -> None:
+    """Quantize the M rows of src (bf16 [M, >= ...]) into an 8-bit cache at pos (vq_kv8_append)."""
+    Hkv, _, D = k_codes.shape
+    _check("vq_kv8_append", lib.vq_kv8_append(src.data_ptr(), src.stride(0), k_off, v_off, k_codes.data_ptr(),
+                                              k_sb.data_ptr(), v_codes.data_ptr(), v_sb.data_ptr(),
+                                              k_codes.stride(0), src.shape[0], Hkv, D, pos, _stream(stream)))
 
 
 # ------------------------------------------------------------------ acceptance

@@ -187,3 +187,30 @@ def test_attn_tree_rejects(vqmod, bad):
                                          a["ors"], a["ws"], a["wsz"], None)
     assert rc == vqmod.VQ_ERR_INVALID_ARG
     assert "vq_multirow_attn_tree" in vqmod.last_error()
+
+
+@pytest.mark.parametrize("bad", [
+    dict(ks=None), dict(vs=None), dict(ks=A16 + 2), dict(mask=A16 + 2), dict(kc=None), dict(kc=A16 + 8),
+    dict(hs=256 * 64 + 8), dict(hs=100 * 64), dict(M=0), dict(D=96), dict(ws=None, T=100000),
+])
+def test_attn_int8_rejects(vqmod, bad):
+    a = dict(q=A16, qrs=128, kc=A16, ks=A16, vc=A16, vs=A16, hs=256 * 64, M=4, Hq=2, Hkv=2, D=64, T=256,
+             scale=0.125, mask=None, out=A16, ors=128, ws=A16, wsz=1 << 30)
+    a.update(bad)
+    rc = vqmod.lib.vq_multirow_attn_int8(a["q"], a["qrs"], a["kc"], a["ks"], a["vc"], a["vs"], a["hs"], a["M"],
+                                         a["Hq"], a["Hkv"], a["D"], a["T"], a["scale"], a["mask"], a["out"],
+                                         a["ors"], a["ws"], a["wsz"], None)
+    assert rc == vqmod.VQ_ERR_INVALID_ARG
+    assert "vq_multirow_attn_int8" in vqmod.last_error()
+
+
+@pytest.mark.parametrize("bad", [
+    dict(src=None), dict(kc=None), dict(vs=None), dict(M=0), dict(M=17), dict(D=96), dict(pos=-1),
+    dict(ld=100), dict(hs=256 * 64 + 8), dict(hs=64 * 3), dict(ks=A16 + 2),
+])
+def test_kv8_append_rejects(vqmod, bad):
+    a = dict(src=A16, ld=512, ko=0, vo=128, kc=A16, ks=A16, vc=A16, vs=A16, hs=256 * 64, M=4, Hkv=2, D=64, pos=10)
+    a.update(bad)
+    rc = vqmod.lib.vq_kv8_append(a["src"], a["ld"], a["ko"], a["vo"], a["kc"], a["ks"], a["vc"], a["vs"], a["hs"],
+                                 a["M"], a["Hkv"], a["D"], a["pos"], None)
+    assert rc == vqmod.VQ_ERR_INVALID_ARG
