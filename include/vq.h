@@ -227,6 +227,35 @@ int vq_multirow_attn_tree(const void* q, int64_t q_row_stride, const void* k_new
                           int64_t out_row_stride, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Several sequences in one call (page "Speculative decoding and MTP on Apple
+ * silicon", Facts: the verify window of several streams shares one pass over
+ * the weights; each stream keeps its own cache and length). The rows of all
+ * sequences are stacked in q and out; sequence b (b < B) owns rows
+ * row_start[b] .. row_start[b+1]-1 (M_b rows, 1 <= M_b <= max_rows) and the
+ * first T_b = seq_len[b] positions (M_b <= T_b <= max_T) of its caches
+ * k_cache + b * kv_batch_stride, v_cache + b * kv_batch_stride ([Hkv, T_cap,
+ * D] each, head stride kv_head_stride, kv_batch_stride >= Hkv *
+ * kv_head_stride). Within a sequence everything is as vq_multirow_attn: causal
+ * among its M_b rows, or tree_mask[r] for row r when tree_mask is given
+ * (vq_multirow_attn_tree, the bits relative to the sequence's first row); with
+ * k_new and v_new (rows in the same stacking as q) the M_b rows are appended at
+ * positions T_b - M_b .. T_b - 1 of the sequence's caches.
+ * row_start (int32 [B+1]) and seq_len (int32 [B]) are device arrays read by the
+ * call (they may change between graph replays). Values outside these rules are
+ * clamped into [0, total_rows] and [M_b, max_T]; the outputs are then undefined
+ * but nothing outside the buffers is accessed. B <= VQ_MAX_SEQS. */
+#define VQ_MAX_SEQS 4096
+size_t vq_multirow_attn_batched_workspace(int B, int max_rows, int Hq, int Hkv, int D, int max_T);
+
+int vq_multirow_attn_batched(const void* q, int64_t q_row_stride, const int32_t* row_start,
+                             const int32_t* seq_len, int B, int total_rows, int max_rows,
+                             int max_T, const void* k_new, const void* v_new,
+                             int64_t new_row_stride, void* k_cache, void* v_cache,
+                             int64_t kv_batch_stride, int64_t kv_head_stride, int Hq, int Hkv,
+                             int D, float scale, const uint32_t* tree_mask, void* out,
+                             int64_t out_row_stride, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* 8-bit KV cache (page "Speculative decoding and MTP on Apple silicon",
  * Facts: KV-quantized caches are used together with speculative decoding; the
  * format is not given and this one follows the affine group-64 quantization of

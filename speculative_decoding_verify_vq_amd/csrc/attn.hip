@@ -33,6 +33,13 @@
 // group: scale = (max - min) / 255 and code = rint((x - min) / scale), both in
 // correctly rounded float32, bias = min.
 //
+// Several sequences in one call (same page, Facts: one verify pass for several
+// streams): the grid gains a sequence dimension; sequence b owns query rows
+// row_start[b] .. row_start[b+1]-1 and T_b = seq_len[b] keys of its own cache
+// (batch stride in the cache). The per-sequence values come from device arrays
+// and are clamped into the launch's bounds, so inconsistent arrays can only
+// give wrong outputs, never an access outside the buffers.
+//
 // Tree verify (page "Speculative decoding and MTP on Apple silicon", Facts:
 // tree-attention masks on the full-attention layers): with a mask, row i sees
 // the committed keys j < T-M and the drafted key T-M+t iff t == i or bit t of
@@ -93,14 +100,56 @@ __device__ __forceinline__ void dequant16(const u32x4 w, uint32_t sb, u32x4& lo,
   hi = u32x4{o[4], o[5], o[6], o[7]};
 }
 
+// Rows M and keys T of sequence b, its first query row r0; returns false for an
+// empty sequence. Without batch arrays: the launch's M and T.
+__device__ __forceinline__ bool seq_bounds(const AttnBatch& bt, int b, int M_max, int T_max, int& M, int& T, int& r0) {
+  M = M_max;
+  T = T_max;
+  r0 = 0;
+  if (!bt.row_start) return true;
+  r0 = min(max(bt.row_start[b], 0), bt.total_rows);
+  const int r1 = min(max(bt.row_start[b + 1], r0), bt.total_rows);
+  M = min(r1 - r0, M_max);
+  T = min(max(bt.seq_len[b], M), T_max);
+  return M > 0;
+}
+
 template <int D, int RT, bool KV8>
 __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     const uint16_t* __restrict__ q, int64_t q_rs, const uint16_t* kc, const uint16_t* vc, int64_t kv_head_stride,
-    int M, int Hq, int Hkv, int T, float scale_log2, int keys_per_split, int splits, uint16_t* __restrict__ out,
+    int M_max, int Hq, int Hkv, int T_max, float scale_log2, int keys_per_split, int splits, uint16_t* __restrict__ out,
     int64_t out_rs, float* __restrict__ part_o, float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, int64_t new_rs, uint16_t* kc_w, uint16_t* vc_w,
-    const uint32_t* __restrict__ tree, const uint32_t* __restrict__ ksb, const uint32_t* __restrict__ vsb) {
+    const uint32_t* __restrict__ tree, const uint32_t* __restrict__ ksb, const uint32_t* __restrict__ vsb,
+    const AttnBatch bt, int rows_stride) {
   using C = AttnCfg<D, RT, KV8>;
+  const int b = blockIdx.z;
+  int M, T, row0;
+  if (!seq_bounds(bt, b, M_max, T_max, M, T, row0)) return;
+  {
+    // Sequence b's rows, cache and outputs (cache offsets in elements of the cache's type).
+    const size_t cb = (size_t)b * bt.kv_batch_stride;
+    q += (size_t)row0 * q_rs;
+    out += (size_t)row0 * out_rs;
+    if constexpr (KV8) {
+      kc = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(kc) + cb);
+      vc = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(vc) + cb);
+      ksb += cb / 64;
+      vsb += cb / 64;
+    } else {
+      kc += cb;
+      vc += cb;
+      if (kc_w) {
+        kc_w += cb;
+        vc_w += cb;
+      }
+    }
+    if (k_new) {
+      k_new += (size_t)row0 * new_rs;
+      v_new += (size_t)row0 * new_rs;
+    }
+    if (tree) tree += row0;
+  }
   __shared__ uint16_t q_lds[RT * 32 * C::LD];
   __shared__ uint16_t k_lds[kTileKeys * C::LD];
   __shared__ uint16_t v_lds[kTileKeys * C::LD];
@@ -322,7 +371,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     }
     return;
   }
-  float* po = part_o + (((size_t)split * Hkv + kvh) * rows + row) * D;
+  const size_t prow = (((size_t)split * gridDim.z + b) * Hkv + kvh) * rows_stride + row;
+  float* po = part_o + prow * D;
 #pragma unroll
   for (int t = 0; t < C::DT; ++t) {
 #pragma unroll
@@ -333,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     }
   }
   if (dpart == 0 && kq == 0) {
-    float* pml = part_ml + (((size_t)split * Hkv + kvh) * rows + row) * 2;
+    float* pml = part_ml + prow * 2;
     pml[0] = m_run;
     pml[1] = l_run;
   }
@@ -347,19 +397,24 @@ constexpr int kCombineGroups = 16;
 constexpr int kMaxSplits = 1024;
 
 __global__ __launch_bounds__(256) void attn_combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, int M, int Hq, int Hkv, int D,
-    int splits, uint16_t* __restrict__ out, int64_t out_rs) {
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int M_max, int Hq, int Hkv, int D,
+    int splits, uint16_t* __restrict__ out, int64_t out_rs, const AttnBatch bt, int rows_stride, int T_max) {
   __shared__ float w_lds[kMaxSplits];
   __shared__ float red[256 / 64];
   __shared__ float4 acc_lds[kCombineGroups][16];
   const int row = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int d0 = blockIdx.z * 64;
+  const int nd = D / 64;
+  const int b = blockIdx.z / nd;
+  const int d0 = (blockIdx.z % nd) * 64;
   const int tid = threadIdx.x;
   const int G = Hq / Hkv;
-  const int rows = M * G;
-  const size_t s_stride = (size_t)Hkv * rows;  // partial rows between consecutive ranges
-  const size_t base = (size_t)kvh * rows + row;
+  int M, T, r0;
+  if (!seq_bounds(bt, b, M_max, T_max, M, T, r0) || row >= M * G) return;
+  out += (size_t)r0 * out_rs;
+  const int nb = gridDim.z / nd;
+  const size_t s_stride = (size_t)nb * Hkv * rows_stride;  // partial rows between consecutive ranges
+  const size_t base = ((size_t)b * Hkv + kvh) * rows_stride + row;
   // Range weights exp2(m_s - max) and the merged denominator.
   float mloc = -INFINITY;
   for (int s = tid; s < splits; s += 256) mloc = fmaxf(mloc, part_ml[(s * s_stride + base) * 2]);
@@ -430,20 +485,21 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 
 }  // namespace
 
-AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T) {
+AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T, int B) {
   AttnPlan p{};
   p.rows = M * (Hq / Hkv);
   p.row_tiles = (p.rows + 31) / 32;
   // About two workgroups per compute unit, at least 128 keys per range.
   const int tiles = (T + kTileKeys - 1) / kTileKeys;
-  int s = (2 * kNumCU + Hkv - 1) / Hkv;
+  int s = (2 * kNumCU + Hkv * B - 1) / (Hkv * B);
   int max_s = (tiles + 3) / 4;
   s = s > max_s ? max_s : s;
   s = s < 1 ? 1 : s;
   const int tiles_per = (tiles + s - 1) / s;
   p.keys_per_split = tiles_per * kTileKeys;
   p.splits = (T + p.keys_per_split - 1) / p.keys_per_split;
-  p.partial_bytes = p.splits > 1 ? align_up((size_t)p.splits * Hkv * p.rows * (D + 2) * sizeof(float), 256) : 0;
+  p.partial_bytes =
+      p.splits > 1 ? align_up((size_t)p.splits * B * Hkv * p.rows * (D + 2) * sizeof(float), 256) : 0;
   (void)D;
   return p;
 }
@@ -452,7 +508,8 @@ hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const 
                        int64_t kv_head_stride, int M, int Hq, int Hkv, int D, int T, float scale,
                        void* out, int64_t out_rs, void* workspace, hipStream_t stream, const void* k_new,
                        const void* v_new, int64_t new_rs, const uint32_t* tree, const uint32_t* k_sb,
-                       const uint32_t* v_sb) {
+                       const uint32_t* v_sb, const AttnBatch* batch) {
+  const AttnBatch bt = batch ? *batch : AttnBatch{nullptr, nullptr, 0, 0, 1};
   auto* kn = reinterpret_cast<const uint16_t*>(k_new);
   auto* vn = reinterpret_cast<const uint16_t*>(v_new);
   // With an append the caches are written (rows T-M .. T-1) as well as read.
@@ -460,9 +517,9 @@ hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const 
   auto* vw = k_new ? const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(v)) : nullptr;
   float* part_o = reinterpret_cast<float*>(workspace);
   float* part_ml = plan.splits > 1
-                       ? part_o + (size_t)plan.splits * Hkv * plan.rows * D
+                       ? part_o + (size_t)plan.splits * bt.B * Hkv * plan.rows * D
                        : nullptr;
-  dim3 grid(plan.splits, Hkv);
+  dim3 grid(plan.splits, Hkv, bt.B);
   auto* qp = reinterpret_cast<const uint16_t*>(q);
   auto* kp = reinterpret_cast<const uint16_t*>(k);
   auto* vp = reinterpret_cast<const uint16_t*>(v);
@@ -473,11 +530,11 @@ hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const 
   if (kv8)                                                                                                   \
     hipLaunchKernelGGL((attn_partial_kernel<DV, RTV, true>), grid, dim3(kThreads), 0, stream, qp, q_rs, kp, vp, \
                        kv_head_stride, M, Hq, Hkv, T, sl2, plan.keys_per_split, plan.splits, op, out_rs, part_o,  \
-                       part_ml, kn, vn, new_rs, kw, vw, tree, k_sb, v_sb);                                       \
+                       part_ml, kn, vn, new_rs, kw, vw, tree, k_sb, v_sb, bt, plan.rows);                        \
   else                                                                                                       \
     hipLaunchKernelGGL((attn_partial_kernel<DV, RTV, false>), grid, dim3(kThreads), 0, stream, qp, q_rs, kp, vp, \
                        kv_head_stride, M, Hq, Hkv, T, sl2, plan.keys_per_split, plan.splits, op, out_rs, part_o,   \
-                       part_ml, kn, vn, new_rs, kw, vw, tree, nullptr, nullptr)
+                       part_ml, kn, vn, new_rs, kw, vw, tree, nullptr, nullptr, bt, plan.rows)
 #define VQ_ATTN_RT(DV)                         \
   switch (plan.row_tiles) {                    \
     case 1: VQ_ATTN(DV, 1); break;             \
@@ -496,8 +553,8 @@ hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const 
 #undef VQ_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(plan.rows, Hkv, D / 64), dim3(256), 0, stream,
-                     part_o, part_ml, M, Hq, Hkv, D, plan.splits, op, out_rs);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(plan.rows, Hkv, (D / 64) * bt.B), dim3(256), 0, stream,
+                     part_o, part_ml, M, Hq, Hkv, D, plan.splits, op, out_rs, bt, plan.rows, T);
   return hipGetLastError();
 }
 

@@ -348,6 +348,43 @@ int vq_multirow_attn_tree(const void* q, int64_t q_row_stride, const void* k_new
                   D, T, scale, tree_mask, out, out_row_stride, workspace, workspace_bytes, stream);
 }
 
+size_t vq_multirow_attn_batched_workspace(int B, int max_rows, int Hq, int Hkv, int D, int max_T) {
+  if (B < 1 || B > VQ_MAX_SEQS || !attn_shape_ok(max_rows, Hq, Hkv, D, max_T)) return 0;
+  return vq::attn_plan(max_rows, Hq, Hkv, D, max_T, B).partial_bytes;
+}
+
+int vq_multirow_attn_batched(const void* q, int64_t q_row_stride, const int32_t* row_start, const int32_t* seq_len,
+                             int B, int total_rows, int max_rows, int max_T, const void* k_new, const void* v_new,
+                             int64_t new_row_stride, void* k_cache, void* v_cache, int64_t kv_batch_stride,
+                             int64_t kv_head_stride, int Hq, int Hkv, int D, float scale, const uint32_t* tree_mask,
+                             void* out, int64_t out_row_stride, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  g_err[0] = 0;
+  const char* who = "vq_multirow_attn_batched";
+  if (!row_start || !seq_len) return fail(VQ_ERR_INVALID_ARG, "%s: NULL row_start or seq_len", who);
+  if (!aligned(row_start, 4) || !aligned(seq_len, 4) || (tree_mask && !aligned(tree_mask, 4)))
+    return fail(VQ_ERR_INVALID_ARG, "%s: misaligned row_start, seq_len or tree_mask", who);
+  if (B < 1 || B > VQ_MAX_SEQS || total_rows < 1 || total_rows > 65535)
+    return fail(VQ_ERR_INVALID_ARG, "%s: B must be in [1, %d] and total_rows in [1, 65535] (B=%d total_rows=%d)", who,
+                VQ_MAX_SEQS, B, total_rows);
+  int rc = VQ_OK;
+  if (k_new || v_new) rc = append_checks(who, k_new, v_new, new_row_stride, Hkv, D);
+  if (!rc)
+    rc = attn_checks(who, q, q_row_stride, k_cache, v_cache, kv_head_stride, max_rows, Hq, Hkv, D, max_T, scale, out,
+                     out_row_stride);
+  if (rc) return rc;
+  if (kv_batch_stride < (int64_t)Hkv * kv_head_stride || kv_batch_stride % 8 != 0)
+    return fail(VQ_ERR_INVALID_ARG, "%s: kv_batch_stride must be >= Hkv * kv_head_stride and a multiple of 8", who);
+  const vq::AttnPlan plan = vq::attn_plan(max_rows, Hq, Hkv, D, max_T, B);
+  if ((rc = check_workspace(workspace, workspace_bytes, plan.partial_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  const vq::AttnBatch bt{row_start, seq_len, kv_batch_stride, total_rows, B};
+  hipError_t e = vq::attn_launch(plan, q, q_row_stride, k_cache, v_cache, kv_head_stride, max_rows, Hq, Hkv, D,
+                                 max_T, scale, out, out_row_stride, workspace, reinterpret_cast<hipStream_t>(stream),
+                                 k_new, v_new, new_row_stride, tree_mask, nullptr, nullptr, &bt);
+  return e == hipSuccess ? VQ_OK : hip_fail(e, who);
+}
+
 int vq_multirow_attn_int8(const void* q, int64_t q_row_stride, const void* k_codes, const void* k_sb,
                           const void* v_codes, const void* v_sb, int64_t kv_head_stride, int M, int Hq, int Hkv,
                           int D, int T, float scale, const uint32_t* tree_mask, void* out, int64_t out_row_stride,

@@ -65,7 +65,19 @@ struct AttnPlan {
   int keys_per_split;
   size_t partial_bytes;
 };
-AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T);
+AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T, int B = 1);
+// Several sequences in one call: sequence b has query rows row_start[b] ..
+// row_start[b+1]-1 (device int32 [B+1], clamped to [0, total_rows]) and
+// seq_len[b] keys (device int32 [B], clamped to [rows, T]) of the caches at
+// b * kv_batch_stride (elements of the cache's type); M and T of the launch are
+// the largest rows and keys of any sequence.
+struct AttnBatch {
+  const int32_t* row_start;
+  const int32_t* seq_len;
+  int64_t kv_batch_stride;
+  int total_rows;
+  int B;
+};
 // k_new / v_new (nullable): the M rows appended at positions T-M .. T-1, rows
 // new_rs elements apart, KV head h at offset h*D; they are written into the
 // caches and read from their source by the attention itself.
@@ -74,7 +86,7 @@ hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const 
                        void* out, int64_t out_rs, void* workspace, hipStream_t stream,
                        const void* k_new = nullptr, const void* v_new = nullptr, int64_t new_rs = 0,
                        const uint32_t* tree = nullptr, const uint32_t* k_sb = nullptr,
-                       const uint32_t* v_sb = nullptr);
+                       const uint32_t* v_sb = nullptr, const AttnBatch* batch = nullptr);
 // 8-bit KV cache: quantize M rows of a fused projection output into the caches
 // (codes u8 [Hkv, T_cap, D], one bf16 scale | bf16 bias word per 64 codes) at
 // positions pos .. pos+M-1; hs = head stride of the codes (elements).

@@ -16,7 +16,9 @@ Per layer, with h the bf16 residual stream and S its per-row sums of squares
     h, S = h + qmm(act, W_down)
 
 then float32 logits = qmm(rms(h), W_lm) feed spec_accept in logits mode together
-with the draft logits. Weights are held in the tiled pack of vq_qmm_pack. Every
+with the draft logits. With B > 1 sequences (each with its own caches and
+context length) the B*M rows are stacked and share every weight pass; the
+attention layers run vq_multirow_attn_batched and acceptance has B entries. Weights are held in the tiled pack of vq_qmm_pack. Every
 launch goes to one stream, so the whole step can be captured once into a HIP
 graph and replayed.
 """
@@ -48,12 +50,17 @@ class StackConfig:
     lm_bits: int = 4
     attn_every: int = 4          # attention on layers attn_every-1, 2*attn_every-1, ...
     ctx: int = 16384             # committed positions in every KV cache
-    M: int = 4                   # verify rows = K + 1
+    M: int = 4                   # verify rows = K + 1 (per sequence)
+    B: int = 1                   # sequences verified together (their B * M rows share the weight pass)
     temperature: float = 0.7
     top_k: int = 0
     top_p: float = 0.95
     group_size: int = 64
     eps: float = 1e-6
+
+    @property
+    def rows(self) -> int:
+        return self.B * self.M
 
     def is_attn(self, layer: int) -> bool:
         return layer % self.attn_every == self.attn_every - 1
@@ -101,7 +108,7 @@ class QPack:
 class StackWeights:
     layers: list = field(default_factory=list)   # per layer: dict name -> QPack ("gate_up" rows interleaved)
     lm_head: QPack | None = None
-    k_cache: list = field(default_factory=list)  # per attention layer: bf16 [Hkv, T_cap, D]
+    k_cache: list = field(default_factory=list)  # per attention layer: bf16 [Hkv, T_cap, D] ([B, Hkv, T_cap, D] for B > 1)
     v_cache: list = field(default_factory=list)
 
     def weight_bytes(self) -> int:
@@ -111,28 +118,38 @@ class StackWeights:
 class DenseVerifyStack:
     """Preallocated buffers and workspaces for one verify step (M rows)."""
 
-    def __init__(self, cfg: StackConfig, weights: StackWeights, device="cuda"):
+    def __init__(self, cfg: StackConfig, weights: StackWeights, device="cuda", ctx_per_seq=None):
+        """ctx_per_seq (B > 1 only): committed positions of each sequence (default cfg.ctx each)."""
         self.cfg = cfg
         self.w = weights
         dev = torch.device(device)
-        M = cfg.M
+        M = cfg.rows
         bf = torch.bfloat16
         self.h = torch.empty((M, cfg.hidden), dtype=bf, device=dev)
         self.ss = torch.empty((M, vq.sumsq_parts(cfg.hidden)), dtype=torch.float32, device=dev)
         self.qkv = torch.empty((M, cfg.qkv_width), dtype=bf, device=dev)
         self.ctx_out = torch.empty((M, cfg.q_width), dtype=bf, device=dev)
         self.act = torch.empty((M, cfg.inter), dtype=bf, device=dev)
-        self.logits = torch.empty((1, M, cfg.vocab), dtype=torch.float32, device=dev)
-        self.probs = torch.empty((1, 2 * M - 1, cfg.vocab), dtype=torch.float32, device=dev)
-        self.tokens = torch.empty((1, M), dtype=torch.int32, device=dev)
-        self.n_acc = torch.empty((1,), dtype=torch.int32, device=dev)
+        B, Mb = cfg.B, cfg.M
+        self.logits = torch.empty((B, Mb, cfg.vocab), dtype=torch.float32, device=dev)
+        self.probs = torch.empty((B, 2 * Mb - 1, cfg.vocab), dtype=torch.float32, device=dev)
+        self.tokens = torch.empty((B, Mb), dtype=torch.int32, device=dev)
+        self.n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
+        ctxs = [cfg.ctx] * B if ctx_per_seq is None else list(ctx_per_seq)
+        assert len(ctxs) == B
+        self.ctxs = ctxs
+        self.row_start = torch.tensor([b * Mb for b in range(B + 1)], dtype=torch.int32, device=dev)
+        self.seq_len = torch.tensor([c + Mb for c in ctxs], dtype=torch.int32, device=dev)
         sh = cfg.shapes()
         qmm_ws = max(vq.qmm_packed_workspace_bytes(b, M, N, K)
                      for name, (N, K) in sh.items()
                      for b in ([cfg.lm_bits] if name == "lm_head" else [cfg.bits]))
-        T = cfg.ctx + M
-        attn_ws = vq.attn_workspace_bytes(M, cfg.Hq, cfg.Hkv, cfg.D, T)
-        acc_ws = vq.accept_workspace_bytes(1, M - 1, cfg.vocab, vq.VQ_LOGITS, M * cfg.vocab, (M - 1) * cfg.vocab)
+        T = max(ctxs) + Mb
+        if B == 1:
+            attn_ws = vq.attn_workspace_bytes(Mb, cfg.Hq, cfg.Hkv, cfg.D, T)
+        else:
+            attn_ws = int(vq.lib.vq_multirow_attn_batched_workspace(B, Mb, cfg.Hq, cfg.Hkv, cfg.D, T))
+        acc_ws = vq.accept_workspace_bytes(B, Mb - 1, cfg.vocab, vq.VQ_LOGITS, Mb * cfg.vocab, (Mb - 1) * cfg.vocab)
         z = lambda n: torch.zeros(n + 256, dtype=torch.uint8, device=dev) if n else None
         self._ws = {"qmm": z(qmm_ws), "attn": z(attn_ws), "accept": z(acc_ws)}
 
@@ -162,12 +179,18 @@ class DenseVerifyStack:
             if cfg.is_attn(li):
                 kc, vc = self.w.k_cache[ai], self.w.v_cache[ai]
                 ai += 1
-                qv = q.as_strided((cfg.M, cfg.Hq, cfg.D), (self.qkv.stride(0), cfg.D, 1))
-                ov = self.ctx_out.view(cfg.M, cfg.Hq, cfg.D)
+                R = cfg.rows
+                qv = q.as_strided((R, cfg.Hq, cfg.D), (self.qkv.stride(0), cfg.D, 1))
+                ov = self.ctx_out.view(R, cfg.Hq, cfg.D)
                 k_new = self.qkv[:, cfg.q_width: cfg.q_width + cfg.Hkv * cfg.D]
                 v_new = self.qkv[:, cfg.q_width + cfg.Hkv * cfg.D:]
-                vq.multirow_attn(qv, kc, vc, cfg.ctx + cfg.M, cfg.D ** -0.5, out=ov, workspace=self._wsv("attn"),
-                                 k_new=k_new, v_new=v_new)
+                if cfg.B == 1:
+                    vq.multirow_attn(qv, kc, vc, self.ctxs[0] + cfg.M, cfg.D ** -0.5, out=ov,
+                                     workspace=self._wsv("attn"), k_new=k_new, v_new=v_new)
+                else:
+                    vq.multirow_attn_batched(qv, self.row_start, self.seq_len, kc, vc, cfg.M, max(self.ctxs) + cfg.M,
+                                             cfg.D ** -0.5, out=ov, k_new=k_new, v_new=v_new,
+                                             workspace=self._wsv("attn"))
                 c = self.ctx_out
             else:
                 c = q
@@ -179,12 +202,13 @@ class DenseVerifyStack:
     def step(self, h_in, draft_logits, drafts, uniforms):
         """One verify step: layers, lm_head, exact acceptance.
 
-        h_in bf16 [M, hidden]; draft_logits float32 [1, K, V]; drafts int32 [1, K];
-        uniforms float32 [1, K+1]. Returns (tokens int32 [1, K+1], n_accepted int32 [1]).
+        h_in bf16 [B*M, hidden] (sequence b's rows at b*M); draft_logits float32
+        [B, K, V]; drafts int32 [B, K]; uniforms float32 [B, K+1]. Returns
+        (tokens int32 [B, K+1], n_accepted int32 [B]).
         """
         cfg = self.cfg
         self.forward_hidden(h_in)
-        self._qmm(self.h, self.w.lm_head, self.logits[0], norm=True)
+        self._qmm(self.h, self.w.lm_head, self.logits.view(cfg.rows, cfg.vocab), norm=True)
         vq.spec_accept(self.logits, draft_logits, drafts, uniforms, logits=True, temperature=cfg.temperature,
                        top_k=cfg.top_k, top_p=cfg.top_p, probs_out=self.probs, out_tokens=self.tokens,
                        out_n=self.n_acc, workspace=self._wsv("accept"))
@@ -194,8 +218,7 @@ class DenseVerifyStack:
         """Algorithmic HBM bytes of one step: weights once, KV (K and V) once per
         attention layer, and the logit rows of the acceptance step."""
         cfg = self.cfg
-        T = cfg.ctx + cfg.M
-        kv = cfg.n_attn * 4 * cfg.Hkv * T * cfg.D
-        acc = (2 * cfg.M - 1) * cfg.vocab * 4
+        kv = cfg.n_attn * 4 * cfg.Hkv * sum(c + cfg.M for c in self.ctxs) * cfg.D
+        acc = cfg.B * (2 * cfg.M - 1) * cfg.vocab * 4
         return {"weights": self.w.weight_bytes(), "kv": kv, "accept_rows": acc,
                 "total": self.w.weight_bytes() + kv + acc}

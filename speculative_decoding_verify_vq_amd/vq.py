@@ -54,6 +54,9 @@ _proto("vq_multirow_attn_tree", _I, [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I, _
                                      _SZ, _P])
 _proto("vq_multirow_attn_int8", _I, [_P, _I64, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _I64, _P, _SZ,
                                      _P])
+_proto("vq_multirow_attn_batched_workspace", _SZ, [_I, _I, _I, _I, _I, _I])
+_proto("vq_multirow_attn_batched", _I, [_P, _I64, _P, _P, _I, _I, _I, _I, _P, _P, _I64, _P, _P, _I64, _I64, _I, _I, _I,
+                                        _F, _P, _P, _I64, _P, _SZ, _P])
 _proto("vq_kv8_append", _I, [_P, _I64, _I, _I, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _P])
 _proto("vq_spec_accept_workspace", _SZ, [_I, _I, _I, _I, _I64, _I64])
 _proto("vq_spec_accept", _I, [_P, _P, _I, _I64, _I64, _P, _P, _I, _I, _I, _F, _I, _F, _P, _P, _P, _P, _SZ, _P])
@@ -266,6 +269,31 @@ def multirow_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                          M, Hq, Hkv, D, T, float(scale), out.data_ptr(), out.stride(0), _ptr(ws),
                                          wsz, _stream(stream))
         _check("vq_multirow_attn_append", rc)
+    return out
+
+
+def multirow_attn_batched(q: torch.Tensor, row_start: torch.Tensor, seq_len: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, max_rows: int, max_T: int, scale: float | None = None,
+                          out: torch.Tensor | None = None, k_new: torch.Tensor | None = None,
+                          v_new: torch.Tensor | None = None, tree_mask: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Several sequences in one call (vq_multirow_attn_batched): q [R, Hq, D] stacked
+    rows; row_start int32 [B+1], seq_len int32 [B] (device); caches [B, Hkv, T_cap, D]."""
+    R, Hq, D = q.shape
+    B, Hkv = k_cache.shape[0], k_cache.shape[1]
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    need = int(lib.vq_multirow_attn_batched_workspace(B, max_rows, Hq, Hkv, D, max_T))
+    ws = _ws(need, q.device, workspace, "attn")
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = lib.vq_multirow_attn_batched(q.data_ptr(), q.stride(0), row_start.data_ptr(), seq_len.data_ptr(), B, R,
+                                      max_rows, max_T, _ptr(k_new), _ptr(v_new),
+                                      0 if k_new is None else k_new.stride(0), k_cache.data_ptr(), v_cache.data_ptr(),
+                                      k_cache.stride(0), k_cache.stride(1), Hq, Hkv, D, float(scale),
+                                      _ptr(tree_mask), out.data_ptr(), out.stride(0), _ptr(ws), wsz, _stream(stream))
+    _check("vq_multirow_attn_batched", rc)
     return out
 
 

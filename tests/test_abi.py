@@ -214,3 +214,27 @@ def test_kv8_append_rejects(vqmod, bad):
     rc = vqmod.lib.vq_kv8_append(a["src"], a["ld"], a["ko"], a["vo"], a["kc"], a["ks"], a["vc"], a["vs"], a["hs"],
                                  a["M"], a["Hkv"], a["D"], a["pos"], None)
     assert rc == vqmod.VQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [
+    dict(rs=None), dict(sl=None), dict(rs=A16 + 2), dict(B=0), dict(B=4097), dict(R=0), dict(mr=17), dict(mr=0),
+    dict(bs=256 * 64), dict(bs=2 * 256 * 64 + 4), dict(kn=None), dict(mask=A16 + 1), dict(T=3), dict(ws=None, T=100000),
+])
+def test_attn_batched_rejects(vqmod, bad):
+    a = dict(q=A16, qrs=128, rs=A16, sl=A16, B=3, R=12, mr=4, T=256, kn=A16, vn=A16, nrs=128, k=A16, v=A16,
+             bs=2 * 256 * 64, hs=256 * 64, Hq=2, Hkv=2, D=64, scale=0.125, mask=None, out=A16, ors=128, ws=A16,
+             wsz=1 << 30)
+    a.update(bad)
+    rc = vqmod.lib.vq_multirow_attn_batched(a["q"], a["qrs"], a["rs"], a["sl"], a["B"], a["R"], a["mr"], a["T"],
+                                            a["kn"], a["vn"], a["nrs"], a["k"], a["v"], a["bs"], a["hs"], a["Hq"],
+                                            a["Hkv"], a["D"], a["scale"], a["mask"], a["out"], a["ors"], a["ws"],
+                                            a["wsz"], None)
+    assert rc == vqmod.VQ_ERR_INVALID_ARG
+    assert "vq_multirow_attn_batched" in vqmod.last_error()
+
+
+def test_batched_workspace_grows_with_sequences(vqmod):
+    one = vqmod.lib.vq_multirow_attn_batched_workspace(1, 4, 24, 4, 256, 16388)
+    assert one == vqmod.attn_workspace_bytes(4, 24, 4, 256, 16388)
+    assert vqmod.lib.vq_multirow_attn_batched_workspace(4, 4, 24, 4, 256, 16388) > 0
+    assert vqmod.lib.vq_multirow_attn_batched_workspace(0, 4, 24, 4, 256, 16388) == 0

@@ -7,7 +7,7 @@ import torch
 
 import oracle.attn as oa
 from synth import attn_inputs
-from tests.gpu_util import assert_close, bf16_tensor, to_f64
+from tests.gpu_util import assert_close, bf16_tensor, i32_tensor, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -183,3 +183,81 @@ def test_tree_with_append(vq):
     ka[:, T - M: T] = new_bits[:, : Hkv * D].reshape(M, Hkv, D).transpose(1, 0, 2)
     va[:, T - M: T] = new_bits[:, Hkv * D:].reshape(M, Hkv, D).transpose(1, 0, 2)
     assert_close(to_f64(out), oa.tree_attention(q, ka, va, M, Hq, Hkv, D, T, T + 4, 0.1, mask), "tree + append")
+
+
+# ------------------------------------------------------------- several sequences
+def _batched_inputs(seed, Ms, Ts, Hq, Hkv, D, T_cap):
+    B = len(Ms)
+    qs, ks, vs = [], [], []
+    for b in range(B):
+        q, k, v = attn_inputs(seed, Ms[b], Hq, Hkv, D, T_cap, extra=100 * b + Ts[b])
+        qs.append(q)
+        ks.append(k)
+        vs.append(v)
+    return qs, np.stack(ks), np.stack(vs)
+
+
+@pytest.mark.parametrize("Ms,Ts,Hq,Hkv,D", [
+    ([4, 1, 7], [300, 5000, 40], 12, 2, 64),       # different rows and lengths, one long
+    ([4, 4, 4, 4], [16400, 200, 9000, 4], 24, 4, 256),   # four 27B-head streams of K = 3
+    ([16], [77], 8, 2, 128),                        # one sequence
+    ([2, 3], [2, 3], 4, 4, 128),                    # T_b == M_b
+])
+@pytest.mark.parametrize("tree", [False, True])
+def test_batched_sequences(vq, Ms, Ts, Hq, Hkv, D, tree):
+    from synth import tree_masks
+    T_cap = max(Ts) + 8
+    qs, kc, vc = _batched_inputs(28, Ms, Ts, Hq, Hkv, D, T_cap)
+    masks = [tree_masks(28, m, extra=b) if tree else None for b, m in enumerate(Ms)]
+    qall = bf16_tensor(np.concatenate(qs))
+    rs = i32_tensor(np.concatenate([[0], np.cumsum(Ms)]))
+    sl = i32_tensor(np.array(Ts))
+    mt = i32_tensor(np.concatenate(masks).view(np.int32)) if tree else None
+    out = to_f64(vq.multirow_attn_batched(qall, rs, sl, bf16_tensor(kc), bf16_tensor(vc), max(Ms), max(Ts), 0.1,
+                                          tree_mask=mt))
+    torch.cuda.synchronize()
+    r0 = 0
+    for b, (m, T) in enumerate(zip(Ms, Ts)):
+        if T > 4096:   # long sequences: sampled (row, head) pairs
+            pairs = [(i, h) for i in range(m) for h in (0, Hq - 1)]
+        else:
+            pairs = None
+        args = (qs[b], kc[b], vc[b], m, Hq, Hkv, D, T, T_cap, 0.1)
+        if tree:
+            ref = oa.tree_attention(*args, masks[b], pairs=pairs)
+        else:
+            ref = oa.multirow_attention(*args, pairs=pairs)
+        got = out[r0: r0 + m] if pairs is None else np.stack([out[r0 + i, h] for i, h in pairs])
+        assert_close(got, ref, f"sequence {b} (M={m}, T={T}, tree={tree})")
+        r0 += m
+
+
+def test_batched_append_and_empty_sequence(vq):
+    """Fused append per sequence, and a sequence with no rows (row_start[b] ==
+    row_start[b+1]) that leaves its cache and the others' results untouched."""
+    import oracle.stack as ostack
+    Ms, Ts, Hq, Hkv, D = [3, 0, 5], [1030, 50, 70], 8, 2, 128
+    T_cap = 1040
+    qs, kc, vc = _batched_inputs(29, [3, 1, 5], Ts, Hq, Hkv, D, T_cap)
+    qs[1] = qs[1][:0]
+    R = sum(Ms)
+    new_bits = ostack.to_bf16_bits(np.random.default_rng(29).standard_normal((R, 2 * Hkv * D)))
+    src = bf16_tensor(new_bits)
+    kd, vd = bf16_tensor(kc), bf16_tensor(vc)
+    rs = i32_tensor(np.array([0, 3, 3, 8]))
+    sl = i32_tensor(np.array(Ts))
+    out = to_f64(vq.multirow_attn_batched(bf16_tensor(np.concatenate(qs)), rs, sl, kd, vd, 5, max(Ts), 0.09,
+                                          k_new=src[:, : Hkv * D], v_new=src[:, Hkv * D:]))
+    torch.cuda.synchronize()
+    assert torch.equal(kd[1], bf16_tensor(kc[1])) and torch.equal(vd[1], bf16_tensor(vc[1]))
+    r0 = 0
+    for b, (m, T) in enumerate(zip(Ms, Ts)):
+        if m == 0:
+            continue
+        ka, va = kc[b].copy(), vc[b].copy()
+        ka[:, T - m: T] = new_bits[r0: r0 + m, : Hkv * D].reshape(m, Hkv, D).transpose(1, 0, 2)
+        va[:, T - m: T] = new_bits[r0: r0 + m, Hkv * D:].reshape(m, Hkv, D).transpose(1, 0, 2)
+        assert np.array_equal(to_f64(kd[b]), to_f64(bf16_tensor(ka)))
+        ref = oa.multirow_attention(qs[b], ka, va, m, Hq, Hkv, D, T, T_cap, 0.09)
+        assert_close(out[r0: r0 + m], ref, f"sequence {b} with append")
+        r0 += m

@@ -80,3 +80,73 @@ def test_stack_step_matches_oracle(vq, bits, M, layers):
     assert_close(P.astype(np.float64), oacc.softmax_f64(st.logits[0].cpu().numpy(), cfg.temperature), "probs")
     rt, rn = oacc.spec_accept(P, Q, list(drafts[0]), us[0], cfg.top_k, cfg.top_p)
     assert list(toks[0].cpu().numpy()) == rt and int(n[0]) == rn
+
+
+def test_multi_sequence_step_matches_oracle(vq):
+    """Three sequences (own caches and context lengths) verified in one step: their
+    12 rows share every weight pass; each sequence's hidden rows, appended K/V,
+    logits and accepted tokens match the oracle run on that sequence alone."""
+    B, M, layers, bits = 3, 4, 2, 4
+    ctxs = [40, 64, 17]
+    cfg = StackConfig(layers=layers, hidden=512, inter=1024, Hq=4, Hkv=2, D=64, vocab=1000, bits=bits, lm_bits=bits,
+                      attn_every=2, ctx=max(ctxs), M=M, B=B, temperature=0.8, top_k=0, top_p=0.9)
+    sh = cfg.shapes()
+    T_cap = max(ctxs) + M + 4
+    gpu_w, ora_w = StackWeights(), []
+    for li in range(layers):
+        lw, lo = {}, {}
+        for j, name in enumerate(("qkv", "o", "down")):
+            N, K = sh[name]
+            w = qmm_weights(31, N, K, bits, layer=10 * li + j)
+            lw[name], lo[name] = _pack(w), w
+        wg = qmm_weights(31, cfg.inter, cfg.hidden, bits, layer=10 * li + 7)
+        wu = qmm_weights(31, cfg.inter, cfg.hidden, bits, layer=10 * li + 8)
+        lw["gate_up"], lo["gate_up"] = _pack(interleave_gate_up(wg, wu)), stack_gate_up(wg, wu)
+        gpu_w.layers.append(lw)
+        ora_w.append(lo)
+    wl = qmm_weights(31, cfg.vocab, cfg.hidden, bits, layer=999)
+    gpu_w.lm_head = _pack(wl)
+    kv = []   # kv[a][b]
+    for a in range(cfg.n_attn):
+        ks, vs, kvb = [], [], []
+        for b in range(B):
+            _, k, v = attn_inputs(31, M, cfg.Hq, cfg.Hkv, cfg.D, T_cap, extra=10 * a + b)
+            ks.append(k)
+            vs.append(v)
+            kvb.append({"k": to_f64(bf16_tensor(k)), "v": to_f64(bf16_tensor(v))})
+        gpu_w.k_cache.append(bf16_tensor(np.stack(ks)))
+        gpu_w.v_cache.append(bf16_tensor(np.stack(vs)))
+        kv.append(kvb)
+    hb = qmm_activations(31, B * M, cfg.hidden)
+    K = M - 1
+    qls, drafts = [], []
+    for b in range(B):
+        _, ql = accept_logits(31, K, cfg.vocab, extra=b)
+        qls.append(ql)
+        drafts.append([int(np.argmax(ql[i])) for i in range(K)])
+    drafts = np.array(drafts, dtype=np.int32)
+    us = uniforms24(31, (B, K + 1))
+
+    st = DenseVerifyStack(cfg, gpu_w, ctx_per_seq=ctxs)
+    toks, n = st.step(bf16_tensor(hb), f32_tensor(np.stack(qls)), i32_tensor(drafts), f32_tensor(us))
+    torch.cuda.synchronize()
+
+    for b in range(B):
+        rows = slice(b * M, (b + 1) * M)
+        h = to_f64(bf16_tensor(hb))[rows]
+        ai = 0
+        for li in range(layers):
+            attn = cfg.is_attn(li)
+            h = ostack.layer_forward(h, ora_w[li], attn, kv[ai][b] if attn else None, ctxs[b], cfg.Hq, cfg.Hkv,
+                                     cfg.D, cfg.inter)
+            ai += int(attn)
+        assert_close(to_f64(st.h)[rows], h, f"sequence {b}: final hidden rows")
+        for a in range(cfg.n_attn):
+            new = slice(ctxs[b], ctxs[b] + M)
+            assert_close(to_f64(gpu_w.k_cache[a][b][:, new]), kv[a][b]["k"][:, new], f"sequence {b}: keys {a}")
+        logits = ostack.lm_head_logits(h, wl)
+        assert_close(to_f64(st.logits[b]), logits, f"sequence {b}: logits")
+        probs = st.probs[b].cpu().numpy()
+        P, Q = probs[: K + 1], probs[K + 1:]
+        rt, rn = oacc.spec_accept(P, Q, list(drafts[b]), us[b], cfg.top_k, cfg.top_p)
+        assert list(toks[b].cpu().numpy()) == rt and int(n[b]) == rn, f"sequence {b}: tokens"
