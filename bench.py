@@ -155,6 +155,105 @@ def qmm_roofline(torch, stack, reps: int = 5) -> dict:
             "achieved_GBs": avg_bytes / (avg_ms * 1e-3) / 1e9}
 
 
+def _time_calls(torch, fns, reps: int = 5) -> float:
+    """µs per call of the callables `fns` (one each), captured into one graph and
+    replayed `reps` times after one warm-up replay."""
+    g = capture(torch, lambda: [f() for f in fns])
+    ms = time_graph(torch, g, reps, 1)
+    del g
+    return 1e3 * ms / len(fns)
+
+
+def next_rows(torch, stack, w, single_ms: float) -> dict:
+    """Measurements of the rows after the hot path, at 27B attention heads
+    (Hq 24, Hkv 4, D 256): tree-mask against causal attention at 16k context and
+    16 drafted rows; 8-bit against bf16 KV at 128k context and 8 rows; the verify
+    step of 4 sequences x 4 rows (16k context each) against one sequence. Every
+    attention timing rotates over distinct caches of at least 2 GiB in total, so
+    that the KV is read from HBM."""
+    from speculative_decoding_verify_vq_amd import vq
+    from speculative_decoding_verify_vq_amd.stack import DenseVerifyStack, StackConfig
+    from synth import bf16_normal_torch, chain_masks, random_words_torch, tree_masks
+    dev = torch.device("cuda")
+    Hq, Hkv, D = 24, 4, 256
+    res = {}
+
+    def caches(n, T, seed):
+        return [(bf16_normal_torch((Hkv, T, D), 0.0, 1.0, seed + 2 * i, dev),
+                 bf16_normal_torch((Hkv, T, D), 0.0, 1.0, seed + 2 * i + 1, dev)) for i in range(n)]
+
+    # tree verify: 16 nodes at 16k
+    M, T = 16, 16384 + 16
+    kv = caches(32, T, 900)
+    q = bf16_normal_torch((M, Hq, D), 0.0, 1.0, 950, dev)
+    tm = torch.from_numpy(tree_masks(3, M).view(np.int32)).to(dev)
+    cm = torch.from_numpy(chain_masks(M).view(np.int32)).to(dev)
+    out = torch.empty_like(q)
+    nb = 4 * Hkv * T * D + 4 * M * Hq * D
+    us_c = _time_calls(torch, [lambda k=k, v=v: vq.multirow_attn(q, k, v, T, 1 / 16, out=out) for k, v in kv])
+    us_t = _time_calls(torch, [lambda k=k, v=v: vq.multirow_attn(q, k, v, T, 1 / 16, out=out, tree_mask=tm)
+                               for k, v in kv])
+    us_ch = _time_calls(torch, [lambda k=k, v=v: vq.multirow_attn(q, k, v, T, 1 / 16, out=out, tree_mask=cm)
+                                for k, v in kv])
+    res["tree_attention"] = {"shape": "Hq 24, Hkv 4, D 256, 16384 committed + 16 tree nodes (random tree)",
+                             "causal_us": round(us_c, 2), "tree_us": round(us_t, 2), "chain_mask_us": round(us_ch, 2),
+                             "tree_GBs": round(nb / us_t / 1e3, 1)}
+    del kv
+    torch.cuda.empty_cache()
+
+    # 8-bit KV: 8 rows at 128k
+    M, T = 8, 131072 + 8
+    q = bf16_normal_torch((M, Hq, D), 0.0, 1.0, 960, dev)
+    out = torch.empty_like(q)
+    kv = caches(4, T, 1000)
+    nb16 = 4 * Hkv * T * D + 4 * M * Hq * D
+    us16 = _time_calls(torch, [lambda k=k, v=v: vq.multirow_attn(q, k, v, T, 1 / 16, out=out) for k, v in kv])
+    del kv
+    torch.cuda.empty_cache()
+
+    def kv8(seed):
+        codes = random_words_torch(Hkv * T * D // 4, seed, dev).view(torch.uint8).view(Hkv, T, D)
+        s_ = bf16_normal_torch((Hkv, T, D // 64), 0.02, 0.005, seed + 1, dev).view(torch.int16).to(torch.int32)
+        b_ = bf16_normal_torch((Hkv, T, D // 64), -2.5, 0.1, seed + 2, dev).view(torch.int16).to(torch.int32)
+        return codes, (s_ & 0xFFFF) | (b_ << 16)
+
+    kv = [(kv8(1100 + 10 * i), kv8(1105 + 10 * i)) for i in range(8)]
+    nb8 = 2 * Hkv * T * (D + 4 * (D // 64)) + 4 * M * Hq * D
+    us8 = _time_calls(torch, [lambda a=a, b=b: vq.multirow_attn_int8(q, a[0], a[1], b[0], b[1], T, 1 / 16, out=out)
+                              for a, b in kv])
+    res["int8_kv_attention"] = {"shape": "Hq 24, Hkv 4, D 256, 131072 committed + 8 rows",
+                                "bf16_us": round(us16, 2), "bf16_GBs": round(nb16 / us16 / 1e3, 1),
+                                "int8_us": round(us8, 2), "int8_GBs": round(nb8 / us8 / 1e3, 1),
+                                "kv_bytes_ratio": round(nb8 / nb16, 4)}
+    del kv
+    torch.cuda.empty_cache()
+
+    # 4 sequences x 4 rows in one step (own caches at 16k each) against one sequence
+    B = 4
+    cfg = stack.cfg
+    cb = StackConfig(**{**cfg.__dict__, "B": B})
+    T_cap = cfg.ctx + 16
+    wb = type(w)(layers=w.layers, lm_head=w.lm_head,
+                 k_cache=[bf16_normal_torch((B, cfg.Hkv, T_cap, cfg.D), 0.0, 1.0, 1200 + a, dev)
+                          for a in range(cfg.n_attn)],
+                 v_cache=[bf16_normal_torch((B, cfg.Hkv, T_cap, cfg.D), 0.0, 1.0, 1300 + a, dev)
+                          for a in range(cfg.n_attn)])
+    st = DenseVerifyStack(cb, wb)
+    K, V = cfg.M - 1, cfg.vocab
+    h_in = torch.randn((B * cfg.M, cfg.hidden), device=dev).to(torch.bfloat16)
+    dl = torch.randn((B, K, V), device=dev) * 2
+    dr = torch.randint(0, V, (B, K), dtype=torch.int32, device=dev)
+    un = torch.rand((B, K + 1), device=dev)
+    g = capture(torch, lambda: st.step(h_in, dl, dr, un))
+    ms_b = time_graph(torch, g, 5, 2)
+    del g, st, wb
+    torch.cuda.empty_cache()
+    res["multi_sequence"] = {"sequences": B, "rows": B * cfg.M, "ms_per_step": round(ms_b, 4),
+                             "single_sequence_ms": round(single_ms, 4),
+                             "speedup_vs_sequential_steps": round(B * single_ms / ms_b, 3)}
+    return res
+
+
 def qmm_traffic(avg_bytes: float):
     """HBM bytes per QMM launch from the committed counter summary, if it was taken
     on the current kernel source (else None): FETCH_SIZE + WRITE_SIZE per dispatch,
@@ -252,6 +351,7 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ratio", action="store_true", help="skip the M=1 / M=8 weight-stream ratio")
+    ap.add_argument("--no-next", action="store_true", help="skip the tree / 8-bit KV / multi-sequence measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (for scaling hardware byte counters)")
     args = ap.parse_args()
@@ -309,6 +409,12 @@ def main() -> int:
     log(f"QMM per launch: {roof['avg_ms'] * 1e3:.1f} us, {roof['achieved_GBs']:.0f} GB/s; {roof['per_kind']}")
     traffic = qmm_traffic(roof["avg_bytes"])
 
+    nxt = None
+    if not args.no_next:
+        log("measuring tree-mask attention, 8-bit KV attention and a 4-sequence step")
+        nxt = next_rows(torch, stack, w, ms)
+        log(f"next rows: {nxt}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -332,6 +438,7 @@ def main() -> int:
                      "timing": "HIP events around replays of graphs holding the step's QMM launches, "
                                "per projection kind, weighted by the step's launch counts"},
         "cpu_baseline": cpu,
+        "next_rows": nxt,
     }
     print(json.dumps(out), flush=True)
     return 0
