@@ -56,6 +56,14 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// gfx950 transposed LDS read of 4 x 16-bit values (ds_read_b64_tr_b16); the
+// address must be 8-byte aligned.
+__device__ __forceinline__ v4i16 ds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)((__attribute__((address_space(3))) uint16_t*)(p)));
+}
 
 constexpr int kThreads = 256;
 constexpr int kTileKeys = 32;
@@ -77,7 +85,10 @@ struct AttnCfg {
   static constexpr int DS = DS0 < D / 32 ? DS0 : D / 32;  // head-dim slices per row tile
   static constexpr int DW = D / DS;                         // head dims per wave
   static constexpr int DT = DW / 32;                        // 32-wide d tiles per wave
-  static constexpr int LD = D + 8;                          // LDS row stride (elements)
+  static constexpr int LD = D + 8;                          // K and Q LDS row stride (elements)
+  // V row stride: 8 dwords past a multiple of 64 banks, so that the 16 lanes
+  // of a transposed read (4 keys x 4 8-byte chunks) hit distinct banks.
+  static constexpr int LDV = 128 * ((D - 16 + 127) / 128) + 16;
   static constexpr int UPK = KV8 ? D / 16 : D / 8;         // 16-byte units per key row
   static constexpr int UNITS = kTileKeys * UPK;             // 16-byte units per K (or V) tile
   static constexpr int PER_THREAD = (UNITS + kThreads - 1) / kThreads;
@@ -152,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
   }
   __shared__ uint16_t q_lds[RT * 32 * C::LD];
   __shared__ uint16_t k_lds[kTileKeys * C::LD];
-  __shared__ uint16_t v_lds[kTileKeys * C::LD];
+  __shared__ uint16_t v_lds[kTileKeys * C::LDV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -229,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
           *reinterpret_cast<u32x4*>(&k_lds[key * C::LD + dc * 16]) = lo;
           *reinterpret_cast<u32x4*>(&k_lds[key * C::LD + dc * 16 + 8]) = hi;
           dequant16(r.v[e], r.vs[e], lo, hi);
-          *reinterpret_cast<u32x4*>(&v_lds[key * C::LD + dc * 16]) = lo;
-          *reinterpret_cast<u32x4*>(&v_lds[key * C::LD + dc * 16 + 8]) = hi;
+          *reinterpret_cast<u32x4*>(&v_lds[key * C::LDV + dc * 16]) = lo;
+          *reinterpret_cast<u32x4*>(&v_lds[key * C::LDV + dc * 16 + 8]) = hi;
         }
         continue;
       }
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
       const int key = u / (D / 8);
       const int dc = u % (D / 8);
       *reinterpret_cast<u32x4*>(&k_lds[key * C::LD + dc * 8]) = r.k[e];
-      *reinterpret_cast<u32x4*>(&v_lds[key * C::LD + dc * 8]) = r.v[e];
+      *reinterpret_cast<u32x4*>(&v_lds[key * C::LDV + dc * 8]) = r.v[e];
     }
     __syncthreads();
   };
@@ -320,23 +331,24 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     const bf16x8 pb1 = __builtin_bit_cast(bf16x8, pw1);
 
     // O^T[d][row] += sum_key V[key][d] P[row][key]. For MFMA c, element j of
-    // this lane covers key 16c + 8*(j/4) + 4*kq + j%4, matching P's layout.
+    // this lane covers key 16c + 8*(j/4) + 4*kq + j%4, matching P's layout. The
+    // A operand (V^T: lane = head dim, elements = keys) comes from two transposed
+    // LDS reads: in each group of 16 lanes, lane s points at key kb + s/4 and
+    // head dims d0 + 4*(s%4) .. +3, and lane i receives keys kb .. kb+3 of head
+    // dim d0 + i.
+    const int tg = lane & 15;
+    const int dh = (lane >> 4) & 1;
 #pragma unroll
     for (int t = 0; t < C::DT; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-      const int d = dpart * C::DW + t * 32 + l32;
+      const int dcol = dpart * C::DW + t * 32 + 16 * dh + 4 * (tg & 3);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        u32x4 aw;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int k0 = 16 * c + 8 * ((2 * jj) >> 2) + 4 * kq + ((2 * jj) & 3);
-          const uint32_t lo = v_lds[k0 * C::LD + d];
-          const uint32_t hi = v_lds[(k0 + 1) * C::LD + d];
-          aw[jj] = lo | (hi << 16);
-        }
-        const bf16x8 a = __builtin_bit_cast(bf16x8, aw);
+        const int kb = 16 * c + 4 * kq + (tg >> 2);
+        const v4i16 lo = ds_read_tr16(&v_lds[kb * C::LDV + dcol]);
+        const v4i16 hi = ds_read_tr16(&v_lds[(kb + 8) * C::LDV + dcol]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, c ? pb1 : pb0, o[t], 0, 0, 0);
       }
     }
