@@ -51,6 +51,13 @@ struct RowMeta {
   int pad[3];
 };
 
+// logit * (log2(e) / T), rounded to float32 on its own: never fused with the
+// subtraction of the row maximum, which is taken over these rounded values.
+__device__ __forceinline__ float scaled_logit(float v, float t_scale) {
+#pragma clang fp contract(off)
+  return v * t_scale;
+}
+
 __device__ __forceinline__ bool prob_ok(float v) { return v >= 0.f && v <= 1.f; }  // false for NaN
 
 __device__ __forceinline__ u64 mass_of(float v) {
@@ -336,10 +343,13 @@ __global__ __launch_bounds__(kRowThreads) void accept_rows_kernel(
     // (max, sum) of every thread, merged over the block, one pass to write the
     // probabilities, check them and sum their masses. A NaN logit gives a NaN
     // probability, a +inf logit makes every probability NaN: both are invalid.
+    // The scaled logit is rounded to float32 before the max is subtracted in
+    // both passes (no fused multiply-subtract), so the largest element gets
+    // exp2(0) = 1 and no probability exceeds 1 however large the logits are.
     float* dst = probs + ((int64_t)e * nrows + r) * V;
     float mx = -INFINITY, sm = 0.f;
     for_row(src, V, [&](int, float v) {
-      const float a = v * t_scale;
+      const float a = scaled_logit(v, t_scale);
       if (a > mx) {
         sm = sm * exp2f(mx - a) + 1.f;
         mx = a;
@@ -352,7 +362,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_rows_kernel(
     const float sum = block_reduce_sum(part, red);
     const float inv = 1.f / sum;
     for_row(src, V, [&](int x, float v) {
-      const float pv = exp2f(v * t_scale - gmx) * inv;
+      const float pv = exp2f(scaled_logit(v, t_scale) - gmx) * inv;
       dst[x] = pv;
       if (prob_ok(pv)) msum += mass_of(pv); else local_bad = 1;
     });
@@ -670,7 +680,7 @@ __global__ __launch_bounds__(kCT) void rows_stats_kernel(const float* __restrict
   const int x0 = c * kChunk, x1 = min(V, x0 + kChunk);
   float mx = -INFINITY, sm = 0.f;
   for_range(src, x0, x1, [&](int, float v) {
-    const float a = v * t_scale;
+    const float a = scaled_logit(v, t_scale);
     if (a > mx) {
       sm = sm * exp2f(mx - a) + 1.f;
       mx = a;
@@ -739,7 +749,7 @@ __global__ __launch_bounds__(kCT) void rows_hist_kernel(
   };
   if (input_kind == 1) {
     for_range(src, x0, x1, [&](int x, float v) {
-      const float pv = exp2f(v * t_scale - gmx) * inv;
+      const float pv = exp2f(scaled_logit(v, t_scale) - gmx) * inv;
       dst[x] = pv;
       visit(x, pv);
     });

@@ -160,3 +160,29 @@ def test_crowded_rows(vq, top_k, top_p):
     got = _gpu(vq, P, Q, D, U, top_k=top_k, top_p=top_p)
     ref = _oracle(P, Q, D, U, top_k, top_p)
     assert np.array_equal(got[1], ref[1]) and np.array_equal(got[0], ref[0])
+
+
+@pytest.mark.parametrize("B,K", [(1, 7), (150, 7)])   # chunked stages; one workgroup per row (2250 rows)
+def test_huge_logits_stay_valid(vq, B, K):
+    """Logits of magnitude ~1.5e4 (float32 ulp ~0.002 after scaling): every computed
+    probability stays in [0, 1], every entry is valid, and the tokens are the
+    oracle's on the device's own probabilities."""
+    V, T, top_k, top_p = 248320, 1.0, 20, 0.95
+    g = np.random.default_rng(B)
+    pl = (15000.0 + 60.0 * g.standard_normal((B, K + 1, V))).astype(np.float32)
+    ql = (g.standard_normal((B, K, V)) * 2.0).astype(np.float32)
+    drafts = np.stack([[int(np.argmax(ql[b, i])) for i in range(K)] for b in range(B)]).astype(np.int32)
+    us = np.asarray(g.integers(0, 2 ** 24, size=(B, K + 1)) * 2.0 ** -24, np.float32)
+    probs = torch.empty((B, 2 * K + 1, V), dtype=torch.float32, device="cuda")
+    toks, n = vq.spec_accept(f32_tensor(pl), f32_tensor(ql), i32_tensor(drafts), f32_tensor(us), logits=True,
+                             temperature=T, top_k=top_k, top_p=top_p, probs_out=probs)
+    torch.cuda.synchronize()
+    pr = probs.cpu().numpy()
+    assert np.all(pr >= 0) and np.all(pr <= 1), float(pr.max())
+    n = n.cpu().numpy()
+    assert np.all(n >= 0)
+    toks = toks.cpu().numpy()
+    for b in range(min(B, 8)):
+        rt, rn = oacc.spec_accept(pr[b, : K + 1].astype(np.float64), pr[b, K + 1:].astype(np.float64),
+                                  list(drafts[b]), us[b], top_k, top_p)
+        assert list(toks[b]) == rt and int(n[b]) == rn
