@@ -119,8 +119,11 @@ int vq_skinny_qmm(const void* x, int64_t ldx,
  * vq_qmm_pack: for every tile of 32 output rows and every block of 256 (4-bit)
  * or 128 (8-bit) inputs, the tile's 32 x 128 bytes of codes followed by its
  * scales and biases, so that the kernel reads each block as one contiguous
- * run. Rows past N and groups past K are zero-filled. The pack is an opaque
- * byte buffer of vq_qmm_pack_bytes() bytes, 16-byte aligned.
+ * run. The code bytes are stored as 256 units of 16 bytes, unit 64j + l holding
+ * bytes 16(2j + l/32) .. +15 of row l%32: the 16 bytes that lane l of a 64-wide
+ * wave loads with its j-th load are its matrix-core operand as they arrive.
+ * Rows past N and groups past K are zero-filled. The pack is an opaque byte
+ * buffer of vq_qmm_pack_bytes() bytes, 16-byte aligned.
  *
  * Fused around the product, for the verify pass of a pre-norm stack (the
  * verify rows go through every projection of every layer; page "The fastest

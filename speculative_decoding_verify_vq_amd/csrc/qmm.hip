@@ -14,28 +14,33 @@
 //     (64 inputs each); each of its 4 waves owns 32 of the columns.
 //   * Codes stream in blocks of 128 bytes per row (4 groups of 4-bit codes, 2 of
 //     8-bit): one block of a wave is 32 rows x 128 B, fetched by 4 dwordx4
-//     instructions. Two (4-bit) or three (8-bit) blocks per wave are in flight.
-//     An arrived block is written to a per-wave LDS buffer (XOR-swizzled so
-//     writes and reads are bank-conflict free) and read back in the B-operand
-//     layout of v_mfma_f32_32x32x16_bf16: lane n (of 32) holds the codes of row
-//     n, lanes 0-31 the first half of the group's inputs and lanes 32-63 the
-//     second half, so a group is a chain of four MFMAs.
-//   * Two weight layouts. Row-major (the plain format: row n holds its codes,
-//     scales and biases are [N, K/64]): each instruction covers 8 rows x 128 B
-//     and each lane fetches the scales and biases of its own column. Tiled
-//     (made once by the pack kernel below): for every 32-row tile and every
-//     block, the 32 x 128 B of codes followed by the block's scales and biases
-//     row by row, so that a block is one contiguous run of 4.5 KiB (4-bit) and
-//     every fetch is a linear 1 KiB stretch. The tiled layout halves the memory
-//     requests per byte and keeps DRAM pages open; it is the fast path.
+//     instructions with the non-temporal hint (the weights are read once). Two
+//     blocks per wave are in flight.
+//   * Two weight layouts. Tiled (made once by the pack kernel below, the fast
+//     path): for every 32-row tile and every block, the 32 x 128 B of codes in
+//     the order in which the lanes of a wave take them as the B operand of
+//     v_mfma_f32_32x32x16_bf16 (lane n%32 holds row n, lanes 0-31 the first
+//     half of a group's inputs and lanes 32-63 the second), followed by the
+//     block's scales and biases row by row: a block is one contiguous run of
+//     4.5 KiB (4-bit), every fetch is a linear 1 KiB stretch, and the loaded
+//     registers are the operands, so a group is a chain of four MFMAs with no
+//     LDS round trip. As soon as a group's registers are consumed, the same
+//     loads of the block two ahead are issued into them. Row-major (the plain
+//     format: row n holds its codes, scales and biases are [N, K/64]): each
+//     instruction covers 8 rows x 128 B, an arrived block is written to a
+//     per-wave LDS buffer (XOR-swizzled, bank-conflict free) and read back in
+//     the operand layout, and each lane fetches the scales and biases of its
+//     own column.
 //   * Codes become bf16 in registers. 4-bit: OR-ing a nibble into the mantissa
 //     of 128.0 gives the exact bf16 value 128 + q, two per 32-bit word, and the
 //     constant 128 is removed per group through the group sums of x. 8-bit:
 //     v_cvt_f32_ubyte + a byte permute gives the exact bf16 q.
-//   * x (zero-padded to MT = 4, 8 or 16 rows) is staged in LDS once per workgroup,
-//     in the element order of the unpack, with its per-group sums. Optionally it
-//     is RMS-normalised on the way in (x * 1/sqrt(mean(x^2) + eps), rounded to
-//     bf16), from per-row sums of squares that the producer of x wrote.
+//   * x (zero-padded to MT = 4, 8 or 16 rows) is staged in LDS in chunks of 16
+//     groups, in the element order of the unpack, with its per-group sums.
+//     Optionally it is RMS-normalised on the way in (x * 1/sqrt(mean(x^2) +
+//     eps), rounded to bf16), from per-row sums of squares that the producer of
+//     x wrote. A workgroup whose range of groups spans several chunks loads the
+//     next chunk into registers while it computes the current one.
 //   * The MFMA gives D_g = sum_{k in g} x*q' per group; scale and bias apply in
 //     float32:
 //         acc += s * D_g + (b - 128 s) * sum_{k in g} x     (4-bit)
@@ -43,7 +48,10 @@
 //   * Parallelism beyond N/128 workgroups comes from splitting K across
 //     workgroups; float32 partials go to the workspace and the last workgroup of
 //     a column block (integer completion counter) adds them in split order, so
-//     results are bit-identical run to run.
+//     results are bit-identical run to run. Partial-sum writes interleaved with
+//     the weight stream cost read bandwidth far beyond their own size, so a wide
+//     output (at least 512 column blocks) is not split at all: its workgroups
+//     walk the whole of K.
 //   * Epilogues: store (bf16 or float32); residual (y = bf16(r + bf16(acc)),
 //     with per-row sums of squares of y per 128-column block for the next
 //     RMSNorm); SwiGLU (rows packed as 64 gate rows then the 64 matching up
@@ -63,11 +71,12 @@ constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kTileN = 32;                // columns per wave
 constexpr int kColsWG = kWaves * kTileN;  // columns per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kCG = 16;                   // max groups per workgroup (one LDS chunk of x)
+constexpr int kCG = 16;                   // groups per LDS chunk of x
 constexpr int kXUnits = kCG * 8 + 1;      // 16-byte units per LDS row of x (+1 pad)
 constexpr int kRowBytes = 128;            // bytes per row per pipeline block
 constexpr int kLoads = 32 * kRowBytes / (64 * 16);  // dwordx4 per lane per block (= 4)
 constexpr size_t kCounterBytes = 32768;   // completion counters (split-K only)
+constexpr int kPlanWGs = 2 * kNumCU;      // workgroups the split plan aims for
 
 enum { kLayoutRow = 0, kLayoutRowScalar = 1, kLayoutTiled = 2 };
 
@@ -76,7 +85,7 @@ struct BlockCfg {
   static constexpr int GB = kRowBytes / (8 * BITS);            // groups per block: 4 (4-bit), 2 (8-bit)
   static constexpr int SB = BITS == 4 ? 16 : 8;                // tiled scale|bias bytes per row per block
   static constexpr int BYTES = 32 * kRowBytes + 32 * SB;       // tiled bytes per (tile, block)
-  static constexpr int IN_FLIGHT = BITS == 4 ? 2 : 3;          // blocks in flight per wave
+  static constexpr int IN_FLIGHT = 2;                           // blocks in flight per wave
 };
 
 // Everything a launch needs; passed by value in the kernel arguments.
@@ -121,12 +130,12 @@ __device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f
 
 // Eight nibbles -> eight bf16 values 128 + q, in the element order
 // (q0, q4, q1, q5, q2, q6, q3, q7).
-__device__ __forceinline__ bf16x8 unpack4(uint32_t w) {
+__device__ __forceinline__ bf16x8 unpack4(uint32_t w, uint32_t m, uint32_t c) {
   u32x4 t;
-  t[0] = (w & 0x000F000Fu) | 0x43004300u;
-  t[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  t[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  t[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  t[0] = (w & m) | c;
+  t[1] = ((w >> 4) & m) | c;
+  t[2] = ((w >> 8) & m) | c;
+  t[3] = ((w >> 12) & m) | c;
   return __builtin_bit_cast(bf16x8, t);
 }
 
@@ -154,7 +163,10 @@ __device__ __forceinline__ bf16x8 unpack8(uint32_t w0, uint32_t w1) {
 // over all LDS banks.
 __device__ __forceinline__ int tslot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
-template <int BITS, int MT, int LAYOUT, int EPI, bool NORM>
+// CHUNK: the workgroup's range of groups may exceed one LDS chunk of x (kCG
+// groups); the next chunk is then prefetched into registers while the current
+// one is computed. Without it the range is at most kCG groups.
+template <int BITS, int MT, int LAYOUT, int EPI, bool NORM, bool CHUNK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void qmm_kernel(const QmmArgs a) {
   constexpr int GB = BlockCfg<BITS>::GB;
   constexpr int kInFlight = BlockCfg<BITS>::IN_FLIGHT;
@@ -164,7 +176,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 
   __shared__ u32x4 xl[MT * kXUnits];
   __shared__ float xsum[kCG][16];
-  __shared__ u32x4 tl[kWaves][32 * 8];
+  __shared__ u32x4 tl[LAYOUT == kLayoutTiled ? 1 : kWaves][32 * 8];
   __shared__ float red[kWaves][16];
   __shared__ float inv_rms[16];
   __shared__ int s_last;
@@ -208,25 +220,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     srow = a.scales + (size_t)ncol * G;
     brow = a.biases + (size_t)ncol * G;
   }
+  auto tiled_block = [&](int bi) __attribute__((always_inline)) -> const uint8_t* {
+    // Block index clamped inside [g0, g1); one contiguous run per block.
+    const int kb = min(g0 / GB + bi, (g1 - 1) / GB);
+    return tile_base + (size_t)kb * BlockCfg<BITS>::BYTES;
+  };
+  auto issue_codes = [&](Regs& R, int bi, int j) __attribute__((always_inline)) {
+    R.w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tiled_block(bi) + j * 1024 + lane * 16));
+  };
+  auto issue_sb = [&](Regs& R, int bi) __attribute__((always_inline)) {
+    const uint8_t* blk = tiled_block(bi);
+    if constexpr (BITS == 4) {
+      const u32x4 sb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(blk + 32 * kRowBytes + l32 * 16));
+      R.s[0] = sb[0];
+      R.s[1] = sb[1];
+      R.b[0] = sb[2];
+      R.b[1] = sb[3];
+    } else {
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 sbv = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(blk + 32 * kRowBytes + l32 * 8));
+      const uint2 sb = make_uint2(sbv[0], sbv[1]);
+      R.s[0] = sb.x;
+      R.b[0] = sb.y;
+      R.s[1] = R.b[1] = 0u;
+    }
+  };
   auto issue = [&](Regs& R, int bi) __attribute__((always_inline)) {
     if constexpr (LAYOUT == kLayoutTiled) {
-      // Block index clamped inside [g0, g1); one contiguous run per block.
-      const int kb = min(g0 / GB + bi, (g1 - 1) / GB);
-      const uint8_t* blk = tile_base + (size_t)kb * BlockCfg<BITS>::BYTES;
 #pragma unroll
-      for (int j = 0; j < kLoads; ++j) R.w[j] = *reinterpret_cast<const u32x4*>(blk + j * 1024 + lane * 16);
-      if constexpr (BITS == 4) {
-        const u32x4 sb = *reinterpret_cast<const u32x4*>(blk + 32 * kRowBytes + l32 * 16);
-        R.s[0] = sb[0];
-        R.s[1] = sb[1];
-        R.b[0] = sb[2];
-        R.b[1] = sb[3];
-      } else {
-        const uint2 sb = *reinterpret_cast<const uint2*>(blk + 32 * kRowBytes + l32 * 8);
-        R.s[0] = sb.x;
-        R.b[0] = sb.y;
-        R.s[1] = R.b[1] = 0u;
-      }
+      for (int j = 0; j < kLoads; ++j) issue_codes(R, bi, j);
+      issue_sb(R, bi);
     } else {
       // Byte offset of this lane's chunk (clamped inside [g0, g1)).
       const int gc = min(g0 + bi * GB + (lchunk * 16) / (8 * BITS), g1 - 1);
@@ -265,62 +288,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   };
 
   // Code blocks in flight per wave. Every block load is issued unconditionally
-  // (block index clamped) and the block sequence is unrolled, so the wait
-  // counts the compiler derives are exact.
+  // (block index clamped) and the blocks of an x chunk are unrolled, so the
+  // wait counts the compiler derives are exact.
   Regs R[kInFlight];
 
-  // ---- stage x (element order of the unpack) with group sums
-  {
-    constexpr int kIters = MT * kCG * 8 / kThreads;
-    static_assert(kIters * kThreads == MT * kCG * 8, "staging loop must be uniform");
-    const int gx1 = min(g1, G);  // groups past G exist only as zero padding of the tiled layout
-    u32x4 v[kIters];
+  // ---- x, staged in chunks of kCG groups in the element order of the unpack,
+  // with per-group sums. Chunk ch covers groups [g0 + ch*kCG, g0 + (ch+1)*kCG)
+  // of this workgroup's range; the next chunk is loaded into registers while the
+  // current one is computed, and written to LDS between two barriers.
+  constexpr int kIters = MT * kCG * 8 / kThreads;
+  static_assert(kIters * kThreads == MT * kCG * 8, "staging loop must be uniform");
+  const int gx1 = min(g1, G);  // groups past G exist only as zero padding of the tiled layout
+  u32x4 xv[kIters];
+  static_assert(!CHUNK || LAYOUT == kLayoutTiled, "chunked ranges are planned for the tiled layout only");
+  auto load_x = [&](int ch) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
       const int t = tid + it * kThreads;
       const int m = t / (kCG * 8);
       const int c = t % (kCG * 8);
-      const int gg = max(0, min(g0 + (c >> 3), gx1 - 1));
-      v[it] = *reinterpret_cast<const u32x4*>(a.x + (size_t)min(m, M - 1) * a.ldx + (size_t)gg * 64 + (c & 7) * 8);
+      const int gg = max(0, min(g0 + ch * kCG + (c >> 3), gx1 - 1));
+      xv[it] = *reinterpret_cast<const u32x4*>(a.x + (size_t)min(m, M - 1) * a.ldx + (size_t)gg * 64 + (c & 7) * 8);
     }
-    // RMSNorm prologue: wave w reduces the sums of squares of rows w, w+4, ...
-    // (4 parts per lane, butterfly order), loaded before the code blocks.
-    float ssv[NORM ? 4 : 1][NORM ? 4 : 1];
-    if constexpr (NORM) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = wave + kWaves * i;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int p = lane + 64 * u;
-          ssv[i][u] = (m < M && p < a.ss_parts) ? a.x_ss[(size_t)m * a.ss_parts + p] : 0.f;
-        }
-      }
-    }
-    // x is waited for before the first code blocks go out: issued together, its
-    // few lines would queue behind the burst of code requests of every
-    // workgroup at the start of the kernel.
-    __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-    for (int i = 0; i < kInFlight; ++i) issue(R[i], i);
-    if constexpr (NORM) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float t = (ssv[i][0] + ssv[i][1]) + (ssv[i][2] + ssv[i][3]);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
-        const int m = wave + kWaves * i;
-        if (lane == 0 && m < M) inv_rms[m] = 1.f / sqrtf(t / (float)K + a.eps);
-      }
-      __syncthreads();
-    }
+  };
+  auto store_x = [&](int ch) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
       const int t = tid + it * kThreads;
       const int m = t / (kCG * 8);
       const int c = t % (kCG * 8);
-      const int gg = g0 + (c >> 3);
-      u32x4 w = (m < M && gg < gx1) ? v[it] : u32x4{0, 0, 0, 0};
+      const int gg = g0 + ch * kCG + (c >> 3);
+      u32x4 w = (m < M && gg < gx1) ? xv[it] : u32x4{0, 0, 0, 0};
       if constexpr (NORM) {
         if (m < M) {
           const float r = inv_rms[m];
@@ -350,43 +348,80 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
       }
       xl[m * kXUnits + c] = w;
     }
+  };
+  load_x(0);
+  // RMSNorm prologue: wave w reduces the sums of squares of rows w, w+4, ...
+  // (4 parts per lane, butterfly order), loaded before the code blocks.
+  float ssv[NORM ? 4 : 1][NORM ? 4 : 1];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = wave + kWaves * i;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = lane + 64 * u;
+        ssv[i][u] = (m < M && p < a.ss_parts) ? a.x_ss[(size_t)m * a.ss_parts + p] : 0.f;
+      }
+    }
   }
+  // x is waited for before the first code blocks go out: issued together, its
+  // few lines would queue behind the burst of code requests of every
+  // workgroup at the start of the kernel.
+  __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+  for (int i = 0; i < kInFlight; ++i) issue(R[i], i);
+  if constexpr (NORM) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float t = (ssv[i][0] + ssv[i][1]) + (ssv[i][2] + ssv[i][3]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
+      const int m = wave + kWaves * i;
+      if (lane == 0 && m < M) inv_rms[m] = 1.f / sqrtf(t / (float)K + a.eps);
+    }
+    __syncthreads();
+  }
+  store_x(0);
   __syncthreads();
 
   float acc[kUseful];
 #pragma unroll
   for (int r = 0; r < kUseful; ++r) acc[r] = 0.f;
-  u32x4* tw = tl[wave];
+  u32x4* tw = tl[LAYOUT == kLayoutTiled ? 0 : wave];
   uint32_t cur_s[2], cur_b[2];  // scales / biases of the block being computed
-  const bool a_live = l32 < MT;  // lanes whose A row is a real (possibly zero) x row
+  uint32_t nib_mask = 0x000F000Fu, nib_bias = 0x43004300u;
+  asm volatile("" : "+v"(nib_mask), "+v"(nib_bias));
 
-  // Consume a block: transpose the codes through LDS, keep its scales / biases.
+  // Consume a block: keep its scales / biases; the row-major layouts transpose
+  // the codes through LDS (the tiled layout already holds them in operand order).
   auto consume = [&](const Regs& R) __attribute__((always_inline)) {
+    if constexpr (LAYOUT != kLayoutTiled) {
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) tw[tslot(8 * j + lrow, lchunk)] = R.w[j];
+      for (int j = 0; j < kLoads; ++j) tw[tslot(8 * j + lrow, lchunk)] = R.w[j];
+    }
     cur_s[0] = R.s[0];
     cur_s[1] = R.s[1];
     cur_b[0] = R.b[0];
     cur_b[1] = R.b[1];
   };
-  auto compute = [&](int bi) __attribute__((always_inline)) {
+  // Compute block bi of this workgroup's range, block bc of its x chunk.
+  auto compute = [&](Regs& R, int bi, int bc, bool more) __attribute__((always_inline)) {
 #pragma unroll
     for (int jb = 0; jb < GB; ++jb) {
       const int gl = bi * GB + jb;  // group index within this workgroup's range
+      const int gx = bc * GB + jb;  // group index within the staged x chunk
       if (gl >= ng) break;
       bf16x8 av[4];
-      if (a_live) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int unit = (BITS == 4) ? gl * 8 + half * 4 + i : gl * 8 + (i >> 1) * 4 + half * 2 + (i & 1);
-          av[i] = __builtin_bit_cast(bf16x8, xl[l32 * kXUnits + unit]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) av[i] = bf16x8{};
+      for (int i = 0; i < 4; ++i) {
+        const int unit = (BITS == 4) ? gx * 8 + half * 4 + i : gx * 8 + (i >> 1) * 4 + half * 2 + (i & 1);
+        av[i] = __builtin_bit_cast(bf16x8, xl[(l32 & (MT - 1)) * kXUnits + unit]);
       }
       u32x4 wv0, wv1;
-      if (BITS == 4) {
+      if constexpr (LAYOUT == kLayoutTiled) {
+        wv0 = R.w[BITS == 4 ? jb : 2 * jb];
+        wv1 = R.w[BITS == 4 ? jb : 2 * jb + 1];
+      } else if (BITS == 4) {
         wv0 = tw[tslot(l32, 2 * jb + half)];
         wv1 = wv0;
       } else {
@@ -398,12 +433,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
       for (int i = 0; i < 4; ++i) {
         bf16x8 bv;
         if (BITS == 4) {
-          bv = unpack4(wv0[i]);
+          bv = unpack4(wv0[i], nib_mask, nib_bias);
         } else {
           const u32x4 wh = (i >> 1) ? wv1 : wv0;
           bv = (i & 1) ? unpack8(wh[2], wh[3]) : unpack8(wh[0], wh[1]);
         }
         d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv, d, 0, 0, 0);
+      }
+      if constexpr (LAYOUT == kLayoutTiled) {
+        // This group's code registers are free: fetch the same loads of block bi + kInFlight.
+        if (more) {
+          issue_codes(R, bi + kInFlight, BITS == 4 ? jb : 2 * jb);
+          if (BITS == 8) issue_codes(R, bi + kInFlight, 2 * jb + 1);
+        }
       }
       const uint32_t sw = cur_s[jb >> 1], bw = cur_b[jb >> 1];
       const float s = __uint_as_float((jb & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
@@ -412,18 +454,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
       for (int r = 0; r < kUseful; ++r) {
         const int m = 8 * (r >> 2) + 4 * half + (r & 3);
-        acc[r] = __builtin_fmaf(s, d[r], __builtin_fmaf(c, xsum[gl][m], acc[r]));
+        acc[r] = __builtin_fmaf(s, d[r], __builtin_fmaf(c, xsum[gx][m], acc[r]));
       }
     }
   };
 
-  constexpr int kMaxBlocks = kCG / GB;
+  constexpr int kBPC = kCG / GB;  // blocks per x chunk
+  static_assert(kBPC % kInFlight == 0, "the register ring must restart at every chunk");
+  const int nch = CHUNK ? (ng + kCG - 1) / kCG : 1;
+  for (int ch = 0; ch < nch; ++ch) {
+    const bool next_x = CHUNK && ch + 1 < nch;
+    if (next_x) load_x(ch + 1);
 #pragma unroll
-  for (int b = 0; b < kMaxBlocks; ++b) {
-    if (b >= nblk) break;
-    consume(R[b % kInFlight]);
-    if (b + kInFlight < kMaxBlocks && b + kInFlight < nblk) issue(R[b % kInFlight], b + kInFlight);
-    compute(b);
+    for (int bc = 0; bc < kBPC; ++bc) {
+      const int b = ch * kBPC + bc;
+      if (b >= nblk) break;
+      Regs& Rb = R[bc % kInFlight];
+      const bool more = b + kInFlight < nblk;
+      consume(Rb);
+      if constexpr (LAYOUT == kLayoutTiled) {
+        if (more) issue_sb(Rb, b + kInFlight);
+      } else {
+        if (more) issue(Rb, b + kInFlight);
+      }
+      compute(Rb, b, bc, more);
+    }
+    if (next_x) {
+      __syncthreads();  // every wave is done with this chunk of x
+      store_x(ch + 1);
+      __syncthreads();
+    }
   }
 
   // ------------------------------------------------------------------ epilogue
@@ -616,8 +676,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 }
 
 // Tiled layout from the row-major one. Workgroup (tile t, block kb), thread u:
-// 16 bytes of codes of row 32t + u/8, chunk u%8; threads 0-31 also write the
-// scale|bias record of row 32t + u. Rows past N and groups past K are zero.
+// 16-byte unit u of the block, the bytes 16 * (2 * (u / 64) + (u % 64) / 32) ..
+// +15 of row 32t + (u % 64) % 32 (the operand that lane u % 64 of a wave takes
+// with its (u / 64)-th load); threads 0-31 also write the scale|bias record of
+// row 32t + u. Rows past N and groups past K are zero.
 template <int BITS>
 __global__ __launch_bounds__(256) void qmm_pack_kernel(const uint8_t* __restrict__ wq,
                                                        const uint16_t* __restrict__ scales,
@@ -630,13 +692,13 @@ __global__ __launch_bounds__(256) void qmm_pack_kernel(const uint8_t* __restrict
   const int G = K / 64;
   const size_t row_bytes = (size_t)K * BITS / 8;
   const int u = threadIdx.x;
-  const int r = u >> 3, c = u & 7;
+  const int r = (u & 63) & 31, c = 2 * (u >> 6) + ((u & 63) >> 5);
   const int n = 32 * t + r;
   uint8_t* blk = out + ((size_t)t * KB + kb) * BlockCfg<BITS>::BYTES;
   const size_t src = (size_t)kb * kRowBytes + c * 16;
   u32x4 w = {0u, 0u, 0u, 0u};
   if (n < N && src < row_bytes) w = *reinterpret_cast<const u32x4*>(wq + (size_t)n * row_bytes + src);
-  *reinterpret_cast<u32x4*>(blk + (size_t)r * kRowBytes + c * 16) = w;
+  *reinterpret_cast<u32x4*>(blk + (size_t)u * 16) = w;
   if (u < 32) {
     const int nr = 32 * t + u;
     uint32_t sv[4] = {0u, 0u, 0u, 0u}, bv[4] = {0u, 0u, 0u, 0u};
@@ -723,10 +785,23 @@ QmmPlan qmm_plan(int bits, int M, int N, int K, bool tiled) {
   p.n_blocks = (N + kColsWG - 1) / kColsWG;
   const int GB = bits == 4 ? 4 : 2;
   const int G = tiled ? (K / 64 + GB - 1) / GB * GB : K / 64;
-  // Enough workgroups for about two per compute unit, and at most kCG groups
-  // per workgroup (one LDS chunk of x). Split boundaries fall on multiples of 4
-  // groups (the scale/bias vector unit and the tiled block).
-  int s = (2 * kNumCU + p.n_blocks - 1) / p.n_blocks;
+  // About kPlanWGs workgroups. With at least that many column blocks (a wide
+  // output such as the vocabulary projection) K is not split at all: every
+  // split writes M x N float32 partial sums, and writes interleaved with the
+  // weight stream cost read bandwidth out of proportion to their size. A
+  // workgroup then walks the whole of K in LDS chunks of x (rows <= 8 only: the
+  // prefetch registers of a 16-row chunk would halve occupancy). Otherwise K is
+  // split into ranges of at most one chunk (kCG groups), split boundaries on
+  // multiples of 4 groups (the scale/bias vector unit and the tiled block).
+  if (tiled && p.mt <= 8 && p.n_blocks >= kPlanWGs) {
+    p.chunked = true;
+    p.groups_per_split = G;
+    p.splits = 1;
+    p.counter_bytes = 0;
+    p.partial_bytes = 0;
+    return p;
+  }
+  int s = (kPlanWGs + p.n_blocks - 1) / p.n_blocks;
   const int s_lds = (G + kCG - 1) / kCG;
   s = s < s_lds ? s_lds : s;
   s = s < 1 ? 1 : s;
@@ -780,31 +855,37 @@ hipError_t qmm_launch(const QmmPlan& plan, const QmmCall& c, hipStream_t stream)
     layout = vec ? kLayoutRow : kLayoutRowScalar;
   }
   const bool norm = c.x_ss != nullptr;
-#define VQ_K(B, MT, L, E, NRM) hipLaunchKernelGGL((qmm_kernel<B, MT, L, E, NRM>), grid, block, 0, stream, a)
-#define VQ_EPI_NORM(B, MT)                                         \
-  switch (c.epilogue * 2 + (norm ? 1 : 0)) {                       \
-    case 0: VQ_K(B, MT, kLayoutTiled, kEpiStore, false); break;    \
-    case 1: VQ_K(B, MT, kLayoutTiled, kEpiStore, true); break;     \
-    case 2: VQ_K(B, MT, kLayoutTiled, kEpiResidual, false); break; \
-    case 3: VQ_K(B, MT, kLayoutTiled, kEpiResidual, true); break;  \
-    case 4: VQ_K(B, MT, kLayoutTiled, kEpiSwiGLU, false); break;   \
-    default: VQ_K(B, MT, kLayoutTiled, kEpiSwiGLU, true); break;   \
+#define VQ_K(B, MT, L, E, NRM, CH) hipLaunchKernelGGL((qmm_kernel<B, MT, L, E, NRM, CH>), grid, block, 0, stream, a)
+#define VQ_EPI_NORM_CH(B, MT, CH)                                      \
+  switch (c.epilogue * 2 + (norm ? 1 : 0)) {                           \
+    case 0: VQ_K(B, MT, kLayoutTiled, kEpiStore, false, CH); break;    \
+    case 1: VQ_K(B, MT, kLayoutTiled, kEpiStore, true, CH); break;     \
+    case 2: VQ_K(B, MT, kLayoutTiled, kEpiResidual, false, CH); break; \
+    case 3: VQ_K(B, MT, kLayoutTiled, kEpiResidual, true, CH); break;  \
+    case 4: VQ_K(B, MT, kLayoutTiled, kEpiSwiGLU, false, CH); break;   \
+    default: VQ_K(B, MT, kLayoutTiled, kEpiSwiGLU, true, CH); break;   \
+  }
+#define VQ_EPI_NORM(B, MT)          \
+  if (plan.chunked) {               \
+    VQ_EPI_NORM_CH(B, MT, true)     \
+  } else {                          \
+    VQ_EPI_NORM_CH(B, MT, false)    \
   }
 #define VQ_BITS(B)                                                      \
   if (layout == kLayoutRow) {                                           \
-    if (plan.mt == 4) VQ_K(B, 4, kLayoutRow, kEpiStore, false);         \
-    else if (plan.mt == 8) VQ_K(B, 8, kLayoutRow, kEpiStore, false);    \
-    else VQ_K(B, 16, kLayoutRow, kEpiStore, false);                     \
+    if (plan.mt == 4) VQ_K(B, 4, kLayoutRow, kEpiStore, false, false);  \
+    else if (plan.mt == 8) VQ_K(B, 8, kLayoutRow, kEpiStore, false, false); \
+    else VQ_K(B, 16, kLayoutRow, kEpiStore, false, false);              \
   } else if (layout == kLayoutRowScalar) {                              \
-    if (plan.mt == 4) VQ_K(B, 4, kLayoutRowScalar, kEpiStore, false);   \
-    else if (plan.mt == 8) VQ_K(B, 8, kLayoutRowScalar, kEpiStore, false); \
-    else VQ_K(B, 16, kLayoutRowScalar, kEpiStore, false);               \
+    if (plan.mt == 4) VQ_K(B, 4, kLayoutRowScalar, kEpiStore, false, false); \
+    else if (plan.mt == 8) VQ_K(B, 8, kLayoutRowScalar, kEpiStore, false, false); \
+    else VQ_K(B, 16, kLayoutRowScalar, kEpiStore, false, false);        \
   } else if (plan.mt == 4) {                                            \
     VQ_EPI_NORM(B, 4)                                                   \
   } else if (plan.mt == 8) {                                            \
     VQ_EPI_NORM(B, 8)                                                   \
   } else {                                                              \
-    VQ_EPI_NORM(B, 16)                                                  \
+    VQ_EPI_NORM_CH(B, 16, false)                                        \
   }
   if (c.bits == 4) {
     VQ_BITS(4)
@@ -813,6 +894,7 @@ hipError_t qmm_launch(const QmmPlan& plan, const QmmCall& c, hipStream_t stream)
   }
 #undef VQ_BITS
 #undef VQ_EPI_NORM
+#undef VQ_EPI_NORM_CH
 #undef VQ_K
   return hipGetLastError();
 }

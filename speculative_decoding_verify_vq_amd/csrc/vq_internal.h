@@ -21,6 +21,7 @@ struct QmmPlan {
   int n_blocks;    // column blocks
   int splits;      // K splits (workgroups per column block)
   int groups_per_split;
+  bool chunked;    // a workgroup walks more than one LDS chunk of x (tiled layout only)
   size_t counter_bytes;  // zeroed completion counters at the start of the workspace
   size_t partial_bytes;  // float32 partial sums [splits][M][N]
 };

@@ -26,8 +26,10 @@ def _pack(vq, w):
 
 def _expected_pack(w) -> np.ndarray:
     """The tiled layout built from its definition: per 32-row tile and per block of
-    128 code bytes per row, the 32 x 128 code bytes, then per row the block's
-    scales and then its biases (4 + 4 bf16 for 4-bit, 2 + 2 for 8-bit)."""
+    128 code bytes per row, the 32 x 128 code bytes as 256 units of 16 bytes, unit
+    64j + l holding bytes 16(2j + l // 32) .. +16 of row l % 32 (the order in which
+    lane l of a wave receives them from its j-th 16-byte load), then per row the
+    block's scales and then its biases (4 + 4 bf16 for 4-bit, 2 + 2 for 8-bit)."""
     N, K, bits = w["N"], w["K"], w["bits"]
     G = K // 64
     GB = 4 if bits == 4 else 2
@@ -44,7 +46,9 @@ def _expected_pack(w) -> np.ndarray:
     for t in range(tiles):
         rows = slice(32 * t, 32 * t + 32)
         for kb in range(KB):
-            out.append(codes[rows, 128 * kb: 128 * kb + 128].reshape(-1))
+            blk = codes[rows, 128 * kb: 128 * kb + 128].reshape(32, 8, 16)   # [row, 16-byte chunk, byte]
+            units = [blk[l % 32, 2 * j + l // 32] for j in range(4) for l in range(64)]
+            out.append(np.concatenate(units))
             sb = np.concatenate([s[rows, GB * kb: GB * kb + GB], b[rows, GB * kb: GB * kb + GB]], axis=1)
             out.append(np.ascontiguousarray(sb).view(np.uint8).reshape(-1))
     return np.concatenate(out)
