@@ -128,6 +128,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_rne(f)); }
 
+// Lane exchange within rows of 16 lanes (DPP; no LDS round trip). Controls:
+// 0xB1 quad_perm [1,0,3,2] (lane ^ 1), 0x4E quad_perm [2,3,0,1] (lane ^ 2),
+// 0x141 row_half_mirror (lane i <-> 7 - i within each 8 lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of 8 lanes, the same value in all 8 (the pairs
+// of each step are those of an xor-1, xor-2, xor-4 butterfly).
+__device__ __forceinline__ float sum8_lanes(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  return v + dpp_f32<0x141>(v);
+}
+
 // Eight nibbles -> eight bf16 values 128 + q, in the element order
 // (q0, q4, q1, q5, q2, q6, q3, q7).
 __device__ __forceinline__ bf16x8 unpack4(uint32_t w, uint32_t m, uint32_t c) {
@@ -334,9 +350,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
                  bf16_bits_to_f32(w[1] & 0xFFFFu) + bf16_bits_to_f32(w[1] >> 16) +
                  bf16_bits_to_f32(w[2] & 0xFFFFu) + bf16_bits_to_f32(w[2] >> 16) +
                  bf16_bits_to_f32(w[3] & 0xFFFFu) + bf16_bits_to_f32(w[3] >> 16);
-      s8 += __shfl_xor(s8, 1);
-      s8 += __shfl_xor(s8, 2);
-      s8 += __shfl_xor(s8, 4);
+      s8 = sum8_lanes(s8);
       if ((c & 7) == 0) xsum[c >> 3][m] = s8;
       if (BITS == 4) {
         u32x4 o;
@@ -371,13 +385,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
   for (int i = 0; i < kInFlight; ++i) issue(R[i], i);
   if constexpr (NORM) {
+    // The four rows' butterflies step together: each step is four independent
+    // lane exchanges and one wait, not four dependent ones.
+    float t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = (ssv[i][0] + ssv[i][1]) + (ssv[i][2] + ssv[i][3]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] += __shfl_xor(t[i], off);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float t = (ssv[i][0] + ssv[i][1]) + (ssv[i][2] + ssv[i][3]);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
       const int m = wave + kWaves * i;
-      if (lane == 0 && m < M) inv_rms[m] = 1.f / sqrtf(t / (float)K + a.eps);
+      if (lane == 0 && m < M) inv_rms[m] = 1.f / sqrtf(t[i] / (float)K + a.eps);
     }
     __syncthreads();
   }
@@ -531,11 +552,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
       if (a.y_ss) {
         // Sum over the wave's 32 columns (lanes of one half), then over the waves.
 #pragma unroll
-        for (int r = 0; r < kUseful; ++r) {
+        for (int off = 16; off > 0; off >>= 1) {
 #pragma unroll
-          for (int off = 16; off > 0; off >>= 1) sq[r] += __shfl_xor(sq[r], off);
-          if (l32 == 0) red[wave][8 * (r >> 2) + 4 * half + (r & 3)] = sq[r];
+          for (int r = 0; r < kUseful; ++r) sq[r] += __shfl_xor(sq[r], off);
         }
+#pragma unroll
+        for (int r = 0; r < kUseful; ++r)
+          if (l32 == 0) red[wave][8 * (r >> 2) + 4 * half + (r & 3)] = sq[r];
         __syncthreads();
         if (tid < M) a.y_ss[(size_t)tid * n_cb + cb] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
       }
@@ -644,21 +667,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   } else if constexpr (EPI == kEpiResidual) {
     // Threads 0-127 of value i hold row 2i, threads 128-255 row 2i+1: each
     // wave sums half a row, then the two halves are added.
+    float sq[kVPT];
 #pragma unroll
     for (int i = 0; i < kVPT; ++i) {
       const int t = tid + i * kThreads;
-      float sq = 0.f;
+      sq[i] = 0.f;
       if (ok[i]) {
         const int col = cb * kColsWG + t % kCols;
         const float h = round_bf16(bf16_bits_to_f32(rv[i]) + round_bf16(v[i][0]));
         yb[(size_t)(t / kCols) * a.ldy + col] = f32_to_bf16_rne(h);
-        sq = h * h;
+        sq[i] = h * h;
       }
-      if (a.y_ss) {
+    }
+    if (a.y_ss) {
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
-        if (lane == 0) red[wave & 1][2 * i + (wave >> 1)] = sq;
+      for (int off = 32; off > 0; off >>= 1) {
+#pragma unroll
+        for (int i = 0; i < kVPT; ++i) sq[i] += __shfl_xor(sq[i], off);
       }
+#pragma unroll
+      for (int i = 0; i < kVPT; ++i)
+        if (lane == 0) red[wave & 1][2 * i + (wave >> 1)] = sq[i];
     }
     if (a.y_ss) {
       __syncthreads();
