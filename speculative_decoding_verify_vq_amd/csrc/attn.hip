@@ -504,9 +504,12 @@ AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T, int B) {
   AttnPlan p{};
   p.rows = M * (Hq / Hkv);
   p.row_tiles = (p.rows + 31) / 32;
-  // About two workgroups per compute unit, at least 128 keys per range.
+  // One round of resident workgroups, at least 128 keys per range. At D = 256
+  // with three or four row tiles a lane needs about 380 registers, so one
+  // workgroup fits per compute unit; otherwise two do.
   const int tiles = (T + kTileKeys - 1) / kTileKeys;
-  int s = (2 * kNumCU + Hkv * B - 1) / (Hkv * B);
+  const int per_cu = (D >= 256 && p.row_tiles >= 3) ? 1 : 2;
+  int s = (per_cu * kNumCU + Hkv * B - 1) / (Hkv * B);
   int max_s = (tiles + 3) / 4;
   s = s > max_s ? max_s : s;
   s = s < 1 ? 1 : s;
@@ -515,7 +518,6 @@ AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T, int B) {
   p.splits = (T + p.keys_per_split - 1) / p.keys_per_split;
   p.partial_bytes =
       p.splits > 1 ? align_up((size_t)p.splits * B * Hkv * p.rows * (D + 2) * sizeof(float), 256) : 0;
-  (void)D;
   return p;
 }
 
