@@ -181,15 +181,25 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
   const int j1 = min(T, j0 + keys_per_split);
 
   // Stage the query rows of this KV head: row i = (position i / G, head kvh*G + i % G).
-  for (int u = tid; u < RT * 32 * (D / 8); u += kThreads) {
-    const int i = u / (D / 8);
-    const int dc = u % (D / 8);
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (i < rows) {
-      const int m = i / G, g = i % G;
-      val = *reinterpret_cast<const uint4*>(q + (size_t)m * q_rs + ((size_t)kvh * G + g) * D + dc * 8);
+  // All loads go out together (rows past `rows` read row 0 and store zeros), so
+  // staging costs one memory round trip.
+  {
+    constexpr int kQPT = RT * 32 * (D / 8) / kThreads;
+    static_assert(kQPT * kThreads == RT * 32 * (D / 8), "query staging must be uniform");
+    uint4 qv[kQPT];
+#pragma unroll
+    for (int e = 0; e < kQPT; ++e) {
+      const int u = tid + e * kThreads;
+      const int i = u / (D / 8), dc = u % (D / 8);
+      const int ic = i < rows ? i : 0;
+      qv[e] = *reinterpret_cast<const uint4*>(q + (size_t)(ic / G) * q_rs + ((size_t)kvh * G + ic % G) * D + dc * 8);
     }
-    *reinterpret_cast<uint4*>(&q_lds[i * C::LD + dc * 8]) = val;
+#pragma unroll
+    for (int e = 0; e < kQPT; ++e) {
+      const int u = tid + e * kThreads;
+      const int i = u / (D / 8), dc = u % (D / 8);
+      *reinterpret_cast<uint4*>(&q_lds[i * C::LD + dc * 8]) = i < rows ? qv[e] : make_uint4(0, 0, 0, 0);
+    }
   }
 
   const uint16_t* kh = kc + (size_t)kvh * kv_head_stride;
@@ -256,19 +266,6 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     }
     __syncthreads();
   };
-  // Append: the rows T-M .. T-1 that fall in this key range are copied from
-  // their source into the caches (every row is in exactly one range).
-  if (k_new) {
-    const int a0 = max(j0, T - M), a1 = j1;
-    for (int u = tid; u < (a1 - a0) * (D / 8); u += kThreads) {
-      const int key = a0 + u / (D / 8);
-      const int dc = u % (D / 8);
-      const size_t src = (size_t)(key - (T - M)) * new_rs + (size_t)kvh * D + dc * 8;
-      const size_t dst = (size_t)kvh * kv_head_stride + (size_t)key * D + dc * 8;
-      *reinterpret_cast<u32x4*>(kc_w + dst) = *reinterpret_cast<const u32x4*>(k_new + src);
-      *reinterpret_cast<u32x4*>(vc_w + dst) = *reinterpret_cast<const u32x4*>(v_new + src);
-    }
-  }
   if (j0 < j1) fetch(r0, j0);
   if (j0 + kTileKeys < j1) fetch(r1, j0 + kTileKeys);
 
@@ -368,6 +365,20 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     }
   }
 
+  // Append: the rows T-M .. T-1 that fall in this key range are copied from
+  // their source into the caches (every row is in exactly one range; the
+  // tiles read those rows from the source, so the copy can come last).
+  if (k_new) {
+    const int a0 = max(j0, T - M), a1 = j1;
+    for (int u = tid; u < (a1 - a0) * (D / 8); u += kThreads) {
+      const int key = a0 + u / (D / 8);
+      const int dc = u % (D / 8);
+      const size_t src = (size_t)(key - (T - M)) * new_rs + (size_t)kvh * D + dc * 8;
+      const size_t dst = (size_t)kvh * kv_head_stride + (size_t)key * D + dc * 8;
+      *reinterpret_cast<u32x4*>(kc_w + dst) = *reinterpret_cast<const u32x4*>(k_new + src);
+      *reinterpret_cast<u32x4*>(vc_w + dst) = *reinterpret_cast<const u32x4*>(v_new + src);
+    }
+  }
   if (!active || !row_ok) return;
   const int g = row % G;
   const int h = kvh * G + g;
@@ -430,31 +441,62 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   const int nb = gridDim.z / nd;
   const size_t s_stride = (size_t)nb * Hkv * rows_stride;  // partial rows between consecutive ranges
   const size_t base = ((size_t)b * Hkv + kvh) * rows_stride + row;
+  // The first batch of partial O rows (ranges grp, grp+16, grp+32, grp+48) and
+  // the (max, sum) pairs go out together; the weights need only the pairs.
+  const int grp = tid >> 4;
+  const int d = d0 + 4 * (tid & 15);
+  const float* po = part_o + base * D + d;
+  float4 v0[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int sp = grp + u * kCombineGroups;
+    v0[u] = sp < splits ? *reinterpret_cast<const float4*>(po + sp * s_stride * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  constexpr int kMLPT = kMaxSplits / 256;
+  float2 ml[kMLPT];
+#pragma unroll
+  for (int k = 0; k < kMLPT; ++k) {
+    const int sp = tid + 256 * k;
+    ml[k] = sp < splits ? *reinterpret_cast<const float2*>(part_ml + (sp * s_stride + base) * 2)
+                        : make_float2(-INFINITY, 0.f);
+  }
   // Range weights exp2(m_s - max) and the merged denominator.
   float mloc = -INFINITY;
-  for (int s = tid; s < splits; s += 256) mloc = fmaxf(mloc, part_ml[(s * s_stride + base) * 2]);
+#pragma unroll
+  for (int k = 0; k < kMLPT; ++k) mloc = fmaxf(mloc, ml[k].x);
   for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
   if ((tid & 63) == 0) red[tid >> 6] = mloc;
   __syncthreads();
   const float mmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float dloc = 0.f;
-  for (int s = tid; s < splits; s += 256) {
-    const float ms = part_ml[(s * s_stride + base) * 2];
-    const float w = ms == -INFINITY ? 0.f : exp2f(ms - mmax);
-    w_lds[s] = w;
-    dloc += w * part_ml[(s * s_stride + base) * 2 + 1];
+#pragma unroll
+  for (int k = 0; k < kMLPT; ++k) {
+    const int sp = tid + 256 * k;
+    if (sp < splits) {
+      const float w = ml[k].x == -INFINITY ? 0.f : exp2f(ml[k].x - mmax);
+      w_lds[sp] = w;
+      dloc += w * ml[k].y;
+    }
   }
   for (int off = 32; off > 0; off >>= 1) dloc += __shfl_xor(dloc, off);
   __syncthreads();
   if ((tid & 63) == 0) red[tid >> 6] = dloc;
   __syncthreads();
   const float den = (red[0] + red[1]) + (red[2] + red[3]);
-  // Weighted sum of the partial O rows.
-  const int grp = tid >> 4;
-  const int d = d0 + 4 * (tid & 15);
-  const float* po = part_o + base * D + d;
+  // Weighted sum of the partial O rows, in range order per group.
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  int s = grp;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int sp = grp + u * kCombineGroups;
+    if (sp < splits) {
+      const float w = w_lds[sp];
+      acc.x += w * v0[u].x;
+      acc.y += w * v0[u].y;
+      acc.z += w * v0[u].z;
+      acc.w += w * v0[u].w;
+    }
+  }
+  int s = grp + 4 * kCombineGroups;
   for (; s + 3 * kCombineGroups < splits; s += 4 * kCombineGroups) {
     float4 v[4];
 #pragma unroll
