@@ -129,7 +129,7 @@ __device__ __forceinline__ bool seq_bounds(const AttnBatch& bt, int b, int M_max
 }
 
 template <int D, int RT, bool KV8>
-__global__ __launch_bounds__(kThreads) void attn_partial_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_partial_kernel(
     const uint16_t* __restrict__ q, int64_t q_rs, const uint16_t* kc, const uint16_t* vc, int64_t kv_head_stride,
     int M_max, int Hq, int Hkv, int T_max, float scale_log2, int keys_per_split, int splits, uint16_t* __restrict__ out,
     int64_t out_rs, float* __restrict__ part_o, float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
@@ -295,29 +295,48 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
       const bf16x8 b = *reinterpret_cast<const bf16x8*>(&q_lds[row * C::LD + 16 * i + 8 * kq]);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s, 0, 0, 0);
     }
-    // Scale, mask, online softmax for this lane's row (keys split between lanes l, l^32).
+    // Scale and mask, for this lane's row (keys split between lanes l, l^32). A
+    // tile wholly inside the committed keys of the range (all but the last one
+    // or two of a call) needs no mask; the masked form is branch-free.
     float mx = -INFINITY;
+    if (t0 + kTileKeys <= min(j1, t_new)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int j = t0 + 8 * (r >> 2) + 4 * kq + (r & 3);
-      const bool vis = j < j1 && (j < t_new || ((seen >> (j - t_new)) & 1u));
-      const float v = vis ? s[r] * scale_log2 : -INFINITY;
-      s[r] = v;
-      mx = fmaxf(mx, v);
+      for (int r = 0; r < 16; ++r) {
+        s[r] *= scale_log2;
+        mx = fmaxf(mx, s[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = t0 + 8 * (r >> 2) + 4 * kq + (r & 3);
+        const int jr = j - t_new;
+        const uint32_t vis = (uint32_t)(j < j1) & ((uint32_t)(jr < 0) | ((seen >> (jr & 31)) & 1u));
+        s[r] = vis ? s[r] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[r]);
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    // Online softmax with a lazily moved reference: m_run changes only when some
+    // row's maximum exceeds it by more than 8 (or at a row's first visible key),
+    // so the probabilities exp2(s - m_run) stay below 2^8 and the rescale of O
+    // (a pass through the accumulation registers) is skipped on most tiles.
+    // O and the sum l use the same reference, so O / l is the same softmax.
+    const bool rescale = __ballot(mx > m_run + 8.f) != 0ull;
+    float alpha = 1.f;
+    if (rescale) {
+      const float m_new = fmaxf(m_run, mx);
+      alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s[r] = exp2f(s[r] - m_use);
+      s[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
       psum += s[r];
     }
     psum += __shfl_xor(psum, 32);
     l_run = l_run * alpha + psum;
-    m_run = m_new;
     u32x4 pw0, pw1;
     pw0[0] = pack_bf16x2(s[0], s[1]);
     pw0[1] = pack_bf16x2(s[2], s[3]);
@@ -340,8 +359,10 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     const int dh = (lane >> 4) & 1;
 #pragma unroll
     for (int t = 0; t < C::DT; ++t) {
+      if (rescale) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      }
       const int dcol = dpart * C::DW + t * 32 + 16 * dh + 4 * (tg & 3);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
