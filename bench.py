@@ -44,6 +44,18 @@ CONFIGS = {
 }
 
 
+# The profiled commands whose CSV output --summarize-profiles reads (run from the
+# repository root on one MI355X, output under <out>).
+PROFILE_CMDS = {
+    "kt": "rocprofv3 --kernel-trace --stats -f csv -d <out>/kt -o kt -- python3 bench.py --steps 5 --warmup 1 "
+          "--no-ratio --no-cpu-baseline --no-next > <out>/kt.out",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o fetch -- python3 bench.py --steps 1 --warmup 0 "
+             "--layers 8 --no-ratio --no-cpu-baseline --no-next --copy-calibration",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o write -- python3 bench.py --steps 1 --warmup 0 "
+             "--layers 8 --no-ratio --no-cpu-baseline --no-next --copy-calibration",
+}
+
+
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -342,6 +354,157 @@ def cpu_baseline(cfg_id: int, cfg, step_bytes: float) -> dict:
             "ms_per_step_extrapolated": round(step_bytes / (rate * 1e9) * 1e3, 1)}
 
 
+# Projection kinds of the 4-bit M=4 step in the order their QMM launches first
+# appear in a profiled bench run, with their bf16/float32 output bytes per
+# element (as in qmm_roofline) and their launch counts in one step.
+_PROFILE_KINDS = [("qkv", 2, 64), ("o", 4, 64), ("gate_up", 1, 64), ("down", 4, 64), ("lm_head", 4, 1)]
+
+
+def _read_csv(directory: str, suffix: str) -> list:
+    import csv
+    import glob
+    paths = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not paths:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    with open(paths[0], newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _qmm_launch_groups(rows: list, grid_key) -> list:
+    """QMM dispatches grouped by (kernel, grid) in order of first appearance."""
+    groups = {}
+    for r in rows:
+        if "qmm_kernel<" in r["Kernel_Name"]:
+            key = (r["Kernel_Name"], grid_key(r))
+            groups.setdefault(key, []).append(r)
+    return list(groups.items())
+
+
+def summarize_profiles(prof_dir: str, out_dir: str, cmd_kt: str, cmd_fetch: str, cmd_write: str) -> None:
+    """Writes the committed profile summaries from a profiled run's CSV output:
+    <prof_dir>/kt (rocprofv3 --kernel-trace --stats -f csv), <prof_dir>/fetch and
+    <prof_dir>/write (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE -f csv, runs with
+    --copy-calibration). Produces the kernel-trace table, the HBM traffic table
+    and qmm_traffic.json (read by qmm_traffic above)."""
+    import hashlib
+    from speculative_decoding_verify_vq_amd.stack import StackConfig, qmm_algorithmic_bytes
+    cfg = StackConfig()
+    sh = cfg.shapes()
+
+    # ---- kernel trace
+    stats = _read_csv(os.path.join(prof_dir, "kt"), "_kernel_stats.csv")
+    trace = _read_csv(os.path.join(prof_dir, "kt"), "_kernel_trace.csv")
+    tot = sum(float(r["TotalDurationNs"]) for r in stats)
+    lines = [f"{'kernel':64s} {'calls':>6s} {'total_us':>10s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s} {'pct':>6s}"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:25]:
+        name = r["Name"].replace("void ", "").replace("(anonymous namespace)::", "")
+        lines.append(f"{name[:64]:64s} {int(r['Calls']):6d} {float(r['TotalDurationNs']) / 1e3:10.1f} "
+                     f"{float(r['AverageNs']) / 1e3:8.2f} {float(r['MinNs']) / 1e3:8.2f} "
+                     f"{float(r['MaxNs']) / 1e3:8.2f} {100 * float(r['TotalDurationNs']) / tot:6.2f}")
+    groups = _qmm_launch_groups(trace, lambda r: (int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]),
+                                                  int(r["Grid_Size_Y"])))
+    if len(groups) != len(_PROFILE_KINDS):
+        raise RuntimeError(f"expected {len(_PROFILE_KINDS)} QMM launch shapes, found {len(groups)}")
+    shape_lines, trace_avg = [], {}
+    for (kind, _, _), ((name, grid), rs) in zip(_PROFILE_KINDS, groups):
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
+        trace_avg[kind] = sum(d) / len(d)
+        short = name.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
+        shape_lines.append(f"  {kind:8s} {short:42s} wg={grid} calls={len(d):5d} avg_us={trace_avg[kind]:8.2f} "
+                           f"min_us={min(d):8.2f}")
+    n_step = sum(c for _, _, c in _PROFILE_KINDS)
+    trace_weighted = sum(trace_avg[k] * c for k, _, c in _PROFILE_KINDS) / n_step
+    bench_line = None
+    for fn in ("kt.out",):
+        path = os.path.join(prof_dir, fn)
+        if os.path.exists(path):
+            with open(path) as f:
+                txt = [ln for ln in f.read().splitlines() if ln.startswith("{")]
+            bench_line = json.loads(txt[-1]) if txt else None
+    md = ["# Kernel trace: verify step, 4-bit g64, M=4, 16k context", "",
+          "Command (from the repository root, on one MI355X):", "", f"    {cmd_kt}", "",
+          "Durations summed over every dispatch of the command (rocprofv3 kernel stats): weight packing, the eager",
+          "warm-up pass, the graph capture, the step replays and the per-projection QMM graphs the bench times for",
+          "its roofline record. `qmm_kernel<bits, MT, layout, epilogue, norm, chunked>`: layout 2 = tiled pack;",
+          "epilogue 0 store, 1 residual, 2 SwiGLU; chunked = the workgroup walks the whole of K (no split).", "",
+          "```", *lines, "", "qmm_kernel by projection (workgroups x, y; from the kernel trace):", *shape_lines, "```", "",
+          f"Trace average per QMM launch, weighted by the step's launch counts (64 each, lm_head once): "
+          f"{trace_weighted:.2f} us."]
+    if bench_line:
+        rf = bench_line["roofline"]
+        pk = ", ".join(f"{k} {v['us']} us" for k, v in rf["per_kind"].items())
+        md.append(f"The bench's own HIP-event timing in the same command (graph replays, per launch): {pk}; "
+                  f"weighted the same way {rf['avg_launch_us']} us per launch.")
+        md.append(f"Step: {bench_line['ms_per_step']} ms ({bench_line['value']} GB/s) under the profiler.")
+    with open(os.path.join(out_dir, "qmm_kernel_verify_step_4bit_M4.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+    # ---- HBM traffic
+    per = {}
+    scale = {}
+    for ctr, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        rows = _read_csv(os.path.join(prof_dir, sub), "_counter_collection.csv")
+        rows = [r for r in rows if r["Counter_Name"] == ctr]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        scale[ctr] = (1 << 20) / max(copies)  # the 1 GiB copy reads and writes 1048576 KiB
+        groups = _qmm_launch_groups(rows, lambda r: int(r["Grid_Size"]))
+        if len(groups) != len(_PROFILE_KINDS):
+            raise RuntimeError(f"{ctr}: expected {len(_PROFILE_KINDS)} QMM launch shapes, found {len(groups)}")
+        for (kind, _, _), (_, rs) in zip(_PROFILE_KINDS, groups):
+            v = [float(r["Counter_Value"]) for r in rs]
+            per.setdefault(kind, {})[ctr] = (sum(v) / len(v), len(v))
+    kinds = {}
+    tot_hbm = tot_alg = 0.0
+    for kind, out_b, cnt in _PROFILE_KINDS:
+        N, K = sh[kind]
+        alg = qmm_algorithmic_bytes(cfg.M, N, K, cfg.bits, out_bytes=out_b)
+        fk, nd = per[kind]["FETCH_SIZE"]
+        wk, _ = per[kind]["WRITE_SIZE"]
+        hbm = 1024 * (fk * scale["FETCH_SIZE"] + wk * scale["WRITE_SIZE"])
+        kinds[kind] = {"fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1), "dispatches": nd,
+                       "hbm_bytes": int(hbm), "algorithmic_bytes": alg, "ratio": round(hbm / alg, 3)}
+        tot_hbm += cnt * hbm
+        tot_alg += cnt * alg
+    src = os.path.join(ROOT, "speculative_decoding_verify_vq_amd", "csrc", "qmm.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    rec = {"kernel": "qmm_kernel (tiled pack; q|k|v with RMSNorm, o and down with the residual epilogue, gate|up "
+                     "with RMSNorm and SwiGLU, lm_head with RMSNorm)",
+           "workload": "4-bit g64 verify step, M=4 (hidden 5120, MLP 17408, lm_head 248320)",
+           "qmm_hip_sha256": digest, "fetch_scale": round(scale["FETCH_SIZE"], 5),
+           "write_scale": round(scale["WRITE_SIZE"], 5),
+           "calibration": "__amd_rocclr_copyBuffer of a 1 GiB bf16 tensor (torch copy_): reads and writes 1048576 KiB",
+           "per_kind": kinds, "step_launch_counts": {k: c for k, _, c in _PROFILE_KINDS},
+           "hbm_bytes_per_launch": int(tot_hbm / n_step), "algorithmic_bytes_per_launch": int(tot_alg / n_step),
+           "commands": [cmd_fetch, cmd_write]}
+    with open(os.path.join(out_dir, "qmm_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    md = ["# HBM traffic of the skinny QMM: verify step, 4-bit g64, M=4", "",
+          "Two counter passes of the same short command (8 layers, one step, plus a 1 GiB device copy for scaling):",
+          "", f"    {cmd_fetch}", f"    {cmd_write}", "",
+          f"Scaling: the 1 GiB copy (1048576 KiB read and written) reads FETCH_SIZE = "
+          f"{(1 << 20) / scale['FETCH_SIZE']:.1f} KiB and WRITE_SIZE = {(1 << 20) / scale['WRITE_SIZE']:.1f} KiB, "
+          f"so fetch counts are scaled by {scale['FETCH_SIZE']:.5f} and write counts by {scale['WRITE_SIZE']:.5f}.", "",
+          "| projection | launches in step | FETCH_SIZE KiB (raw) | WRITE_SIZE KiB (raw) | HBM bytes (scaled) | "
+          "algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|"]
+    for kind, _, cnt in _PROFILE_KINDS:
+        r = kinds[kind]
+        md.append(f"| {kind} | {cnt} | {r['fetch_kib_raw']} | {r['write_kib_raw']} | {r['hbm_bytes']} | "
+                  f"{r['algorithmic_bytes']} | {r['ratio']} |")
+    md += ["", f"Weighted by the step's launch counts: {rec['hbm_bytes_per_launch']} HBM bytes per launch against "
+               f"{rec['algorithmic_bytes_per_launch']} algorithmic bytes "
+               f"({rec['hbm_bytes_per_launch'] / rec['algorithmic_bytes_per_launch']:.3f}x).",
+           "Algorithmic bytes include the residual read of the residual epilogue (o, down) and count SwiGLU's N/2 "
+           "outputs (gate|up).",
+           "The excess of the split projections is their float32 partials (written once, read once by the last "
+           "workgroup of each column block) and the x slices re-read by every workgroup; the lm_head is not split.",
+           "", f"qmm.hip sha256 at the time of the runs: {digest} (bench.py reports the traffic only while the source "
+               "matches)."]
+    with open(os.path.join(out_dir, "qmm_traffic_4bit_M4.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -352,9 +515,16 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ratio", action="store_true", help="skip the M=1 / M=8 weight-stream ratio")
     ap.add_argument("--no-next", action="store_true", help="skip the tree / 8-bit KV / multi-sequence measurements")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="write the profiles/ summaries from a profiled run's CSV output (kt/, fetch/, write/ under "
+                         "DIR) and exit; needs no GPU")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (for scaling hardware byte counters)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, os.path.join(ROOT, "profiles"), PROFILE_CMDS["kt"],
+                           PROFILE_CMDS["fetch"], PROFILE_CMDS["write"])
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the verify step; runs on more than one GPU are not "
               "part of this build (see DESIGN.md for how the path would shard).", file=sys.stderr)
