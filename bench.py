@@ -11,7 +11,7 @@ replayed; inputs are resident in HBM when timing starts.
 
 Printed (one JSON line): verify-step HBM GB/s over the step's algorithmic bytes
 (weights once + K/V once per attention layer + the logit rows), its fraction of
-the 8 TB/s peak, ms per step, cost(M=8)/cost(M=1) of the 64-layer weight
+the 8 TB/s peak, ms per step, cost(M)/cost(M=1) of the 64-layer stack for M = 1..16
 stream, a roofline record of the dominant kernel (the skinny QMM, timed per
 launch with HIP events on its stream) and the CPU oracle timed on a bounded
 sample of the same workload.
@@ -180,7 +180,8 @@ def next_rows(torch, stack, w, single_ms: float) -> dict:
     """Measurements of the rows after the hot path, at 27B attention heads
     (Hq 24, Hkv 4, D 256): tree-mask against causal attention at 16k context and
     16 drafted rows; 8-bit against bf16 KV at 128k context and 8 rows; the verify
-    step of 4 sequences x 4 rows (16k context each) against one sequence. Every
+    step of 16 // M sequences of M rows (the step's context each) against one
+    sequence. Every
     attention timing rotates over distinct caches of at least 2 GiB in total, so
     that the KV is read from HBM."""
     from speculative_decoding_verify_vq_amd import vq
@@ -240,8 +241,9 @@ def next_rows(torch, stack, w, single_ms: float) -> dict:
     del kv
     torch.cuda.empty_cache()
 
-    # 4 sequences x 4 rows in one step (own caches at 16k each) against one sequence
-    B = 4
+    # 16 // M sequences of M rows in one step (own caches at the step's context
+    # each; at most 16 rows share the weight pass) against one sequence
+    B = max(1, 16 // stack.cfg.M)
     cfg = stack.cfg
     cb = StackConfig(**{**cfg.__dict__, "B": B})
     T_cap = cfg.ctx + 16
@@ -300,8 +302,10 @@ def copy_calibration(torch, nbytes: int = 1 << 30) -> None:
 
 def cpu_baseline(cfg_id: int, cfg, step_bytes: float) -> dict:
     """The oracle timed on a bounded sample of the same workload on this host's cores:
-    one layer's four projections (qkv, o, gate_up, down) at the step's M, one attention layer (every row and query head) at the
-    step's context, and one acceptance over the full vocabulary. Rate = algorithmic
+    one layer's four projections (qkv, o, gate_up, down) at the step's M, one
+    attention layer at the step's context (every row and query head; above 32k
+    keys one KV head and its query heads), and one acceptance over the full
+    vocabulary. Rate = algorithmic
     bytes of the sample / CPU seconds, in GB/s (the step time is extrapolated from
     the same bytes-per-second)."""
     import oracle.accept as oacc
@@ -330,13 +334,16 @@ def cpu_baseline(cfg_id: int, cfg, step_bytes: float) -> dict:
         secs += dt
         nbytes += b
     T = cfg.ctx + M
-    q, k, v = attn_inputs(2, M, cfg.Hq, cfg.Hkv, cfg.D, T)
+    # Long contexts: one KV head and its query heads, so the sample stays bounded.
+    hkv = cfg.Hkv if T <= 32768 else 1
+    hq = cfg.Hq // cfg.Hkv * hkv
+    q, k, v = attn_inputs(2, M, hq, hkv, cfg.D, T)
     t0 = time.perf_counter()
-    oattn.multirow_attention(q, k, v, M, cfg.Hq, cfg.Hkv, cfg.D, T, T, cfg.D ** -0.5)
+    oattn.multirow_attention(q, k, v, M, hq, hkv, cfg.D, T, T, cfg.D ** -0.5)
     dt = time.perf_counter() - t0
-    parts.append(f"attention {M} rows x {cfg.Hq} heads at T={T} ({dt:.2f} s)")
+    parts.append(f"attention {M} rows x {hq} heads ({hkv} KV) at T={T} ({dt:.2f} s)")
     secs += dt
-    nbytes += 2 * cfg.Hkv * T * cfg.D * 2  # K and V of every KV head, once
+    nbytes += 2 * hkv * T * cfg.D * 2  # K and V of the sampled KV heads, once
     K = M - 1
     pl, ql = accept_logits(cfg_id, K, cfg.vocab)
     P, Q = oacc.probs_f32(pl, cfg.temperature), oacc.probs_f32(ql, cfg.temperature)
@@ -562,10 +569,13 @@ def main() -> int:
     tok, n = stack.tokens.cpu().tolist(), int(stack.n_acc.item())
     log(f"step {ms:.3f} ms, {gbs:.1f} GB/s; tokens {tok} n_accepted {n}")
 
-    ratio = None
+    ratio = curve = None
     if not args.no_ratio:
+        # cost(M) / cost(M=1) of the layer stack (weights once + attention of M
+        # rows on the KV caches) over the verify widths of the dense-projection
+        # workload, M = 1, 2, 3, 4, 6, 8, 12, 16.
         res = {}
-        for m in (1, 8):
+        for m in (1, 2, 3, 4, 6, 8, 12, 16):
             cm = StackConfig(**{**cfg.__dict__, "M": m})
             st = DenseVerifyStack(cm, w)
             hm = torch.randn((m, cfg.hidden), device=dev).to(torch.bfloat16)
@@ -573,7 +583,9 @@ def main() -> int:
             res[m] = time_graph(torch, gm, max(5, args.steps // 2), 2)
             del gm, st
         ratio = res[8] / res[1]
-        log(f"64-layer stack: M=1 {res[1]:.3f} ms, M=8 {res[8]:.3f} ms, ratio {ratio:.3f}")
+        curve = {str(m): {"ms": round(v, 4), "cost_ratio": round(v / res[1], 4)} for m, v in res.items()}
+        log(f"{cfg.layers}-layer stack: M=1 {res[1]:.3f} ms, M=8 {res[8]:.3f} ms, ratio {ratio:.3f}; "
+            f"{ {m: round(v / res[1], 3) for m, v in res.items()} }")
 
     roof = qmm_roofline(torch, stack)
     log(f"QMM per launch: {roof['avg_ms'] * 1e3:.1f} us, {roof['achieved_GBs']:.0f} GB/s; {roof['per_kind']}")
@@ -598,6 +610,7 @@ def main() -> int:
                    "vocab": V, "bytes_per_step": nbytes},
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "cost_ratio_m8_m1": None if ratio is None else round(ratio, 4),
+        "cost_curve": curve,
         "roofline": {"bound": "hbm", "achieved": round(roof["achieved_GBs"], 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(roof["achieved_GBs"] / PEAK_HBM_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
