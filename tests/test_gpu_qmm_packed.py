@@ -215,3 +215,67 @@ def test_packed_deterministic(vq):
         b = vq.qmm_packed(xt, p, 4, 1024, 8192, out_dtype=torch.float32)
         torch.cuda.synchronize()
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("bits,M", [(4, 4), (8, 8)])
+def test_step_projections_full_shape_sampled(vq, bits, M):
+    """The five projections of the verify step at 27B shapes on the tiled pack, in
+    the launch configuration of the step (RMSNorm prologue on q|k|v, gate|up and
+    lm_head; residual epilogue on o and down; SwiGLU on gate|up; float32 lm_head
+    logits, whose 1940 column blocks take the unsplit path), on sampled output
+    columns that the oracle computes one by one."""
+    H, I, V = 5120, 17408, 248320
+    cfg = 3 if bits == 4 else 4
+    rng = np.random.default_rng(100 + bits)
+
+    def sample(n, k=40):
+        return np.unique(np.concatenate([rng.choice(n, size=k, replace=False), [0, n - 1]]))
+
+    def normed(seed):
+        hb = qmm_activations(cfg, M, H, extra=seed)
+        h = bf16_tensor(hb)
+        return hb, h, vq.row_sumsq(h), ostack.to_bf16_bits(ostack.rmsnorm(to_f64(h)))
+
+    # q|k|v with the RMSNorm prologue
+    w = qmm_weights(cfg, 8192, H, bits, layer=0)
+    hb, h, ss, a = normed(1)
+    y = to_f64(vq.qmm_packed(h, _pack(vq, w), bits, 8192, H, x_sumsq=ss, eps=1e-6))
+    c = sample(8192)
+    assert_close(y[:, c], oq.skinny_qmm(a, w["wq"], w["scales"], w["biases"], bits, 64, M, 8192, H, cols=c), "qkv")
+    del w
+
+    # o and down with the residual epilogue (o: K = 6144; down: K = 17408)
+    for name, K, layer in (("o", 6144, 1), ("down", I, 3)):
+        w = qmm_weights(cfg, H, K, bits, layer=layer)
+        xb = qmm_activations(cfg, M, K, extra=10 + layer)
+        rb = qmm_activations(cfg, M, H, extra=20 + layer)
+        res = bf16_tensor(rb)
+        ss = torch.empty((M, vq.sumsq_parts(H)), dtype=torch.float32, device=dev())
+        y = to_f64(vq.qmm_packed(bf16_tensor(xb), _pack(vq, w), bits, H, K, epilogue=vq.VQ_EPI_RESIDUAL,
+                                 residual=res, y_sumsq=ss))
+        c = sample(H)
+        p = oq.skinny_qmm(xb, w["wq"], w["scales"], w["biases"], bits, 64, M, H, K, cols=c)
+        ref = ostack.round_bf16(to_f64(bf16_tensor(rb))[:, c] + ostack.round_bf16(p))
+        assert_close(y[:, c], ref, name)
+        del w
+
+    # gate|up with the RMSNorm prologue and the SwiGLU epilogue
+    wg = qmm_weights(cfg, I, H, bits, layer=4)
+    wu = qmm_weights(cfg, I, H, bits, layer=5)
+    wi = interleave_gate_up(wg, wu)
+    hb, h, ss, a = normed(2)
+    y = to_f64(vq.qmm_packed(h, _pack(vq, wi), bits, 2 * I, H, x_sumsq=ss, eps=1e-6,
+                             epilogue=vq.VQ_EPI_SWIGLU))
+    del wi
+    c = sample(I)
+    g = ostack.round_bf16(oq.skinny_qmm(a, wg["wq"], wg["scales"], wg["biases"], bits, 64, M, I, H, cols=c))
+    u = ostack.round_bf16(oq.skinny_qmm(a, wu["wq"], wu["scales"], wu["biases"], bits, 64, M, I, H, cols=c))
+    assert_close(y[:, c], ostack.round_bf16(ostack.silu_mul(g, u)), "gate_up")
+    del wg, wu
+
+    # lm_head: RMSNorm prologue, float32 logits
+    w = qmm_weights(cfg, V, H, bits, layer=999)
+    hb, h, ss, a = normed(3)
+    y = to_f64(vq.qmm_packed(h, _pack(vq, w), bits, V, H, x_sumsq=ss, eps=1e-6, out_dtype=torch.float32))
+    c = sample(V, 64)
+    assert_close(y[:, c], oq.skinny_qmm(a, w["wq"], w["scales"], w["biases"], bits, 64, M, V, H, cols=c), "lm_head")
