@@ -462,14 +462,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   const int nb = gridDim.z / nd;
   const size_t s_stride = (size_t)nb * Hkv * rows_stride;  // partial rows between consecutive ranges
   const size_t base = ((size_t)b * Hkv + kvh) * rows_stride + row;
-  // The first batch of partial O rows (ranges grp, grp+16, grp+32, grp+48) and
-  // the (max, sum) pairs go out together; the weights need only the pairs.
+  // The first batch of partial O rows (ranges grp, grp+16, ..., grp+112: all
+  // of them up to 128 ranges) and the (max, sum) pairs go out together; the
+  // weights need only the pairs.
+  constexpr int kFirst = 8;
   const int grp = tid >> 4;
   const int d = d0 + 4 * (tid & 15);
   const float* po = part_o + base * D + d;
-  float4 v0[4];
+  float4 v0[kFirst];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < kFirst; ++u) {
     const int sp = grp + u * kCombineGroups;
     v0[u] = sp < splits ? *reinterpret_cast<const float4*>(po + sp * s_stride * D) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
@@ -507,7 +509,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   // Weighted sum of the partial O rows, in range order per group.
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < kFirst; ++u) {
     const int sp = grp + u * kCombineGroups;
     if (sp < splits) {
       const float w = w_lds[sp];
@@ -517,7 +519,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
       acc.w += w * v0[u].w;
     }
   }
-  int s = grp + 4 * kCombineGroups;
+  int s = grp + kFirst * kCombineGroups;
   for (; s + 3 * kCombineGroups < splits; s += 4 * kCombineGroups) {
     float4 v[4];
 #pragma unroll
