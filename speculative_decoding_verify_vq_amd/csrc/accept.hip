@@ -534,6 +534,47 @@ __device__ int draw_token(const DrawRow& d, uint32_t mu, u128* scan, u128* wsum,
 }
 
 // ---------------------------------------------------------------- entry kernel
+// The K accept tests of one verify entry (and the validity of its rows, draft
+// ids and uniforms): the first rejected position j (K if every draft passes).
+__device__ int entry_decide(const float* P, const float* Q, const RowMeta* mrow, const int32_t* dr, const float* us,
+                            int K, int V, int* bad_out) {
+  // Called by one whole wave (K <= 15, so lane i holds draft i, uniform i and the
+  // meta of rows i and K + 1 + i): the loads of every test go out together and
+  // the first rejection is the lowest lane whose test fails.
+  const int lane = threadIdx.x & 63;
+  int bad = 0;
+  RowMeta mp{}, mq{};
+  int d = 0;
+  float u = 0.f;
+  if (lane < 2 * K + 1) {
+    mp = mrow[lane];
+    bad |= mp.status;
+  }
+  if (lane < K) mq = mrow[K + 1 + lane];
+  if (lane <= K) {
+    u = us[lane];
+    bad |= !uniform_ok(u);
+  }
+  if (lane < K) {
+    d = dr[lane];
+    bad |= (d < 0 || d >= V);
+  }
+  const bool any_bad = __ballot(bad != 0) != 0ull;
+  int j = K;
+  if (!any_bad) {
+    bool fail = false;
+    if (lane < K) {
+      const u64 a = kept_mass(P + (int64_t)lane * V, d, V, mp);
+      const u64 c = kept_mass(Q + (int64_t)lane * V, d, V, mq);
+      fail = !accept_test(mu_of(u), c, mp.z, a, mq.z);
+    }
+    const unsigned long long m = __ballot(fail);
+    if (m) j = __ffsll((long long)m) - 1;
+  }
+  *bad_out = any_bad ? 1 : 0;
+  return j;
+}
+
 __global__ __launch_bounds__(kEntryThreads) void accept_entry_kernel(
     const float* __restrict__ probs_p, const float* __restrict__ probs_q, int64_t pp_stride,
     int64_t qq_stride, const RowMeta* __restrict__ meta, int64_t meta_stride, const int32_t* __restrict__ draft,
@@ -549,26 +590,13 @@ __global__ __launch_bounds__(kEntryThreads) void accept_entry_kernel(
   const float* Q = probs_q + (int64_t)b * qq_stride;
   const int32_t* dr = draft + (int64_t)b * K;
   const float* us = uniforms + (int64_t)b * (K + 1);
-  if (tid == 0) {
-    int bad = 0;
-    for (int i = 0; i < 2 * K + 1; ++i) bad |= mrow[i].status;
-    for (int i = 0; i <= K; ++i) bad |= !uniform_ok(us[i]);
-    for (int i = 0; i < K; ++i) bad |= (dr[i] < 0 || dr[i] >= V);
-    int j = K;
-    if (!bad) {
-      for (int i = 0; i < K; ++i) {
-        const int d = dr[i];
-        const RowMeta mp = mrow[i], mq = mrow[K + 1 + i];
-        const u64 a = kept_mass(P + (int64_t)i * V, d, V, mp);
-        const u64 c = kept_mass(Q + (int64_t)i * V, d, V, mq);
-        if (!accept_test(mu_of(us[i]), c, mp.z, a, mq.z)) {
-          j = i;
-          break;
-        }
-      }
+  if (tid < 64) {
+    int bad;
+    const int j = entry_decide(P, Q, mrow, dr, us, K, V, &bad);
+    if (tid == 0) {
+      s_bad = bad;
+      s_j = j;
     }
-    s_bad = bad;
-    s_j = j;
   }
   __syncthreads();
   const int j = s_j;
@@ -701,28 +729,28 @@ __global__ __launch_bounds__(kCT) void rows_hist_kernel(
   __shared__ uint32_t cnt[kBins];
   __shared__ u64 mas[kBins];
   __shared__ u64 red64[kCT / 64];
-  __shared__ float sg[2];
+  __shared__ float redf[kCT / 64];
   __shared__ int s_bad;
   const int c = blockIdx.x % C, r = blockIdx.x / C;
   const int tid = threadIdx.x;
   const int x0 = c * kChunk, x1 = min(V, x0 + kChunk);
   const float* src = row_ptr(p, q, ps, qs, K, V, r);
   float* dst = probs + (int64_t)r * V;
-  if (tid == 0) {
-    s_bad = 0;
-    if (input_kind == 1) {
-      // The row's max and sum from the chunk statistics, in chunk order: every
-      // workgroup of the row gets the same values.
-      float gmx = -INFINITY;
-      for (int i = 0; i < C; ++i) gmx = fmaxf(gmx, stats[(int64_t)r * C + i].x);
-      float gs = 0.f;
-      for (int i = 0; i < C; ++i) {
-        const float2 s2 = stats[(int64_t)r * C + i];
-        gs += (s2.x == -INFINITY) ? 0.f : s2.y * exp2f(s2.x - gmx);
-      }
-      sg[0] = gmx;
-      sg[1] = 1.f / gs;
+  if (tid == 0) s_bad = 0;
+  float gmx = 0.f, inv = 0.f;
+  if (input_kind == 1) {
+    // The row's max and sum from the chunk statistics (thread i takes chunks i,
+    // i + kCT, ..., then a fixed reduction tree): every workgroup of the row
+    // gets the same values.
+    float mx = -INFINITY;
+    for (int i = tid; i < C; i += kCT) mx = fmaxf(mx, stats[(int64_t)r * C + i].x);
+    gmx = block_reduce_max(mx, redf);
+    float part = 0.f;
+    for (int i = tid; i < C; i += kCT) {
+      const float2 s2 = stats[(int64_t)r * C + i];
+      part += (s2.x == -INFINITY) ? 0.f : s2.y * exp2f(s2.x - gmx);
     }
+    inv = 1.f / block_reduce_sum(part, redf);
   }
   if (use_hist) {
     for (int b = tid; b < kBins; b += kCT) {
@@ -731,7 +759,6 @@ __global__ __launch_bounds__(kCT) void rows_hist_kernel(
     }
   }
   __syncthreads();
-  const float gmx = sg[0], inv = sg[1];
   u64 msum = 0;
   int bad = 0;
   auto visit = [&](int x, float pv) {
@@ -1049,29 +1076,6 @@ __global__ __launch_bounds__(kRowThreads) void rows_resolve_kernel(int V, int to
 // first rejected position j — the residual, or the kept target mass when all K
 // drafts pass — and of the kept target mass of row j (used only if the
 // residual is zero everywhere).
-__device__ int entry_decide(const float* P, const float* Q, const RowMeta* mrow, const int32_t* dr, const float* us,
-                            int K, int V, int* bad_out) {
-  int bad = 0;
-  for (int i = 0; i < 2 * K + 1; ++i) bad |= mrow[i].status;
-  for (int i = 0; i <= K; ++i) bad |= !uniform_ok(us[i]);
-  for (int i = 0; i < K; ++i) bad |= (dr[i] < 0 || dr[i] >= V);
-  int j = K;
-  if (!bad) {
-    for (int i = 0; i < K; ++i) {
-      const int d = dr[i];
-      const RowMeta mp = mrow[i], mq = mrow[K + 1 + i];
-      const u64 a = kept_mass(P + (int64_t)i * V, d, V, mp);
-      const u64 c = kept_mass(Q + (int64_t)i * V, d, V, mq);
-      if (!accept_test(mu_of(us[i]), c, mp.z, a, mq.z)) {
-        j = i;
-        break;
-      }
-    }
-  }
-  *bad_out = bad;
-  return j;
-}
-
 __global__ __launch_bounds__(kCT) void draw_sums_kernel(const float* __restrict__ probs_p,
                                                         const float* __restrict__ probs_q, int64_t pp_stride,
                                                         int64_t qq_stride, const RowMeta* __restrict__ meta,
@@ -1085,7 +1089,14 @@ __global__ __launch_bounds__(kCT) void draw_sums_kernel(const float* __restrict_
   const RowMeta* mrow = meta + (int64_t)b * meta_stride;
   const float* P = probs_p + (int64_t)b * pp_stride;
   const float* Q = probs_q + (int64_t)b * qq_stride;
-  if (tid == 0) s_j = entry_decide(P, Q, mrow, draft + (int64_t)b * K, uniforms + (int64_t)b * (K + 1), K, V, &s_bad);
+  if (tid < 64) {
+    int bad;
+    const int jj = entry_decide(P, Q, mrow, draft + (int64_t)b * K, uniforms + (int64_t)b * (K + 1), K, V, &bad);
+    if (tid == 0) {
+      s_j = jj;
+      s_bad = bad;
+    }
+  }
   __syncthreads();
   if (s_bad) return;
   const int j = s_j;
@@ -1157,8 +1168,8 @@ __global__ __launch_bounds__(kRowThreads) void draw_pick_kernel(
     const float* __restrict__ uniforms, int K, int V, int C, const u128* __restrict__ esum,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_n) {
   __shared__ u128 scan[kRowThreads / 64 + 1];
-  __shared__ int s_j, s_bad, s_tok, s_fb, s_c;
-  __shared__ u128 s_before, s_tau;
+  __shared__ int s_j, s_bad, s_tok, s_c;
+  __shared__ u128 s_before;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const RowMeta* mrow = meta + (int64_t)b * meta_stride;
@@ -1166,32 +1177,21 @@ __global__ __launch_bounds__(kRowThreads) void draw_pick_kernel(
   const float* Q = probs_q + (int64_t)b * qq_stride;
   const int32_t* dr = draft + (int64_t)b * K;
   const float* us = uniforms + (int64_t)b * (K + 1);
-  if (tid == 0) {
-    s_j = entry_decide(P, Q, mrow, dr, us, K, V, &s_bad);
-    s_tok = -1;
-    if (!s_bad) {
-      u128 R = 0;
-      for (int c = 0; c < C; ++c) R += esum[((int64_t)b * C + c) * 2];
-      int fb = 0;
-      if (R == 0) {  // p~_j == q~_j and the draft lay outside both supports: draw from p~_j
-        fb = 1;
-        for (int c = 0; c < C; ++c) R += esum[((int64_t)b * C + c) * 2 + 1];
-      }
-      const u128 tau = scaled_draw(mu_of(us[K]), R);
-      u128 before = 0;
-      int cs = C - 1;
-      for (int c = 0; c < C; ++c) {
-        const u128 w = esum[((int64_t)b * C + c) * 2 + fb];
-        if (before + w > tau) {
-          cs = c;
-          break;
-        }
-        before += w;
-      }
-      s_fb = fb;
-      s_c = cs;
-      s_before = before;
-      s_tau = tau;
+  // Every chunk's two sums go out with the accept tests (V <= 2^20, so C <= 128
+  // chunks, one per thread).
+  u128 w0 = 0, w1 = 0;
+  if (tid < C) {
+    w0 = esum[((int64_t)b * C + tid) * 2];
+    w1 = esum[((int64_t)b * C + tid) * 2 + 1];
+  }
+  const float u_draw = us[K];
+  if (tid < 64) {
+    int bad;
+    const int jj = entry_decide(P, Q, mrow, dr, us, K, V, &bad);
+    if (tid == 0) {
+      s_j = jj;
+      s_bad = bad;
+      s_tok = -1;
     }
   }
   __syncthreads();
@@ -1201,27 +1201,62 @@ __global__ __launch_bounds__(kRowThreads) void draw_pick_kernel(
     if (tid == 0) out_n[b] = -1;
     return;
   }
+  // Totals and chunk-order prefix sums of both weights; if the residual is zero
+  // everywhere (p~_j == q~_j and the draft lay outside both supports) the draw
+  // is from p~_j. The chunk that holds floor(mu * R / 2^24) is the one whose
+  // prefix range contains it.
+  u128 R0, R1;
+  const u128 e0 = block_excl_scan<u128, kRowThreads>(w0, scan, R0);
+  const u128 e1 = block_excl_scan<u128, kRowThreads>(w1, scan, R1);
+  const int fb = R0 == 0 ? 1 : 0;
+  const u128 R = fb ? R1 : R0;
+  const u128 tau = scaled_draw(mu_of(u_draw), R);
+  const u128 wc = fb ? w1 : w0, ec = fb ? e1 : e0;
+  if (tid == 0) {
+    s_c = C - 1;
+    s_before = R;
+  }
+  __syncthreads();
+  if (tid < C && ec <= tau && tau < ec + wc) {
+    s_c = tid;
+    s_before = ec;
+  }
+  __syncthreads();
   DrawRow d;
   d.P = P + (int64_t)j * V;
   d.mp = mrow[j];
-  d.Q = (j < K && !s_fb) ? Q + (int64_t)j * V : nullptr;
+  d.Q = (j < K && !fb) ? Q + (int64_t)j * V : nullptr;
   d.mq = j < K ? mrow[K + 1 + j] : RowMeta{};
   d.V = V;
+  // Each thread takes kPer consecutive elements of the chunk (all loads at once;
+  // indices clamped into the chunk, elements past a1 unused).
+  constexpr int kPer = kChunk / kRowThreads;
+  static_assert(kPer * kRowThreads == kChunk, "a chunk splits evenly over the threads");
   const int x0 = s_c * kChunk, x1 = min(V, x0 + kChunk);
-  const int per = (x1 - x0 + kRowThreads - 1) / kRowThreads;
-  const int a0 = min(x1, x0 + tid * per), a1 = min(x1, a0 + per);
+  const int a0 = min(x1, x0 + tid * kPer), a1 = min(x1, a0 + kPer);
+  float pv[kPer], qv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int x = min(a0 + u, x1 - 1);
+    pv[u] = d.P[x];
+    qv[u] = d.Q ? d.Q[x] : 0.f;
+  }
   u128 mine = 0;
-  for (int x = a0; x < a1; ++x) mine += d.w(x, d.P[x], d.Q ? d.Q[x] : 0.f);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (a0 + u < a1) mine += d.w(a0 + u, pv[u], qv[u]);
   u128 tot;
   const u128 excl = s_before + block_excl_scan<u128, kRowThreads>(mine, scan, tot);
-  const u128 tau = s_tau;
   if (excl <= tau && tau < excl + mine) {
     u128 run = excl;
-    for (int x = a0; x < a1; ++x) {
-      run += d.w(x, d.P[x], d.Q ? d.Q[x] : 0.f);
-      if (run > tau) {
-        s_tok = x;
-        break;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      if (a0 + u < a1) {
+        run += d.w(a0 + u, pv[u], qv[u]);
+        if (run > tau) {
+          s_tok = a0 + u;
+          break;
+        }
       }
     }
   }
