@@ -392,13 +392,15 @@ def summarize_profiles(prof_dir: str, out_dir: str, cmd_kt: str, cmd_fetch: str,
     <prof_dir>/kt (rocprofv3 --kernel-trace --stats -f csv), <prof_dir>/fetch and
     <prof_dir>/write (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE -f csv, runs with
     --copy-calibration). Produces the kernel-trace table, the HBM traffic table
-    and qmm_traffic.json (read by qmm_traffic above)."""
-    import hashlib
-    from speculative_decoding_verify_vq_amd.stack import StackConfig, qmm_algorithmic_bytes
-    cfg = StackConfig()
-    sh = cfg.shapes()
+    and qmm_traffic.json (read by qmm_traffic above). A part whose CSV
+    directories are missing is left as it is."""
+    if os.path.isdir(os.path.join(prof_dir, "kt")):
+        _summarize_trace(prof_dir, out_dir, cmd_kt)
+    if os.path.isdir(os.path.join(prof_dir, "fetch")) and os.path.isdir(os.path.join(prof_dir, "write")):
+        _summarize_traffic(prof_dir, out_dir, cmd_fetch, cmd_write)
 
-    # ---- kernel trace
+
+def _summarize_trace(prof_dir: str, out_dir: str, cmd_kt: str) -> None:
     stats = _read_csv(os.path.join(prof_dir, "kt"), "_kernel_stats.csv")
     trace = _read_csv(os.path.join(prof_dir, "kt"), "_kernel_trace.csv")
     tot = sum(float(r["TotalDurationNs"]) for r in stats)
@@ -446,7 +448,14 @@ def summarize_profiles(prof_dir: str, out_dir: str, cmd_kt: str, cmd_fetch: str,
     with open(os.path.join(out_dir, "qmm_kernel_verify_step_4bit_M4.md"), "w") as f:
         f.write("\n".join(md) + "\n")
 
-    # ---- HBM traffic
+
+
+def _summarize_traffic(prof_dir: str, out_dir: str, cmd_fetch: str, cmd_write: str) -> None:
+    import hashlib
+    from speculative_decoding_verify_vq_amd.stack import StackConfig, qmm_algorithmic_bytes
+    cfg = StackConfig()
+    sh = cfg.shapes()
+    n_step = sum(c for _, _, c in _PROFILE_KINDS)
     per = {}
     scale = {}
     for ctr, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
