@@ -1,6 +1,6 @@
 """Verify-step benchmark on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3|4] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3|4] [--no-cpu-baseline] [--soak SECONDS]
 
 A step is one pass of the whole verify path over one batch of synthetic input:
 64 layers of 4-bit (config 3) or 8-bit (config 4) affine group-quantized
@@ -122,6 +122,44 @@ def time_graph(torch, g, steps: int, warmup: int) -> float:
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
+
+
+def replay_times(torch, g, n: int) -> list:
+    """ms of each of n back-to-back replays (an event between consecutive replays,
+    no synchronisation inside the run)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record()
+    for i in range(n):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
+
+def percentiles(xs, ps=(10, 50, 90, 99)) -> dict:
+    a = np.sort(np.asarray(xs, dtype=np.float64))
+    return {f"p{p}": round(float(np.percentile(a, p)), 4) for p in ps}
+
+
+def soak(torch, g, seconds: float, step_bytes: float) -> dict:
+    """Replays the step back to back for `seconds`, in windows of about one
+    second, each timed replay by replay; returns the per-window median and p99
+    and the drift of the median from the first window to the last."""
+    t_end = time.time() + seconds
+    windows = []
+    n = max(1, int(1000.0 / max(replay_times(torch, g, 5)[-1], 1e-3)))
+    while time.time() < t_end:
+        ts = replay_times(torch, g, n)
+        windows.append({"t_s": round(seconds - (t_end - time.time()), 1), **percentiles(ts, (50, 99))})
+        if len(windows) % 10 == 0:
+            log(f"soak {windows[-1]['t_s']:.0f} s: median {windows[-1]['p50']:.3f} ms, p99 {windows[-1]['p99']:.3f} ms")
+    p50 = [w["p50"] for w in windows]
+    return {"seconds": round(seconds, 1), "replays": n * len(windows), "windows": len(windows),
+            "median_ms_first": p50[0], "median_ms_last": p50[-1], "median_ms_max": max(p50),
+            "p99_ms_max": max(w["p99"] for w in windows),
+            "drift_pct": round(100.0 * (p50[-1] - p50[0]) / p50[0], 2),
+            "GBs_at_median_last": round(step_bytes / (p50[-1] * 1e-3) / 1e9, 1),
+            "series": windows}
 
 
 def qmm_roofline(torch, stack, reps: int = 5) -> dict:
@@ -534,6 +572,9 @@ def main() -> int:
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write the profiles/ summaries from a profiled run's CSV output (kt/, fetch/, write/ under "
                          "DIR) and exit; needs no GPU")
+    ap.add_argument("--soak", type=float, default=0.0, metavar="SECONDS",
+                    help="after the measurements, replay the step back to back for this long and report the "
+                         "per-second median / p99 series (sustained-run check)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (for scaling hardware byte counters)")
     args = ap.parse_args()
@@ -577,6 +618,8 @@ def main() -> int:
     gbs = nbytes["total"] / (ms * 1e-3) / 1e9
     tok, n = stack.tokens.cpu().tolist(), int(stack.n_acc.item())
     log(f"step {ms:.3f} ms, {gbs:.1f} GB/s; tokens {tok} n_accepted {n}")
+    dist = percentiles(replay_times(torch, g, args.steps))
+    log(f"per-replay ms: {dist}")
 
     ratio = curve = None
     if not args.no_ratio:
@@ -611,9 +654,17 @@ def main() -> int:
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(args.config, cfg, nbytes["total"])
 
+    soak_rec = None
+    if args.soak > 0:
+        log(f"soak: replaying the step for {args.soak:.0f} s")
+        soak_rec = soak(torch, g, args.soak, nbytes["total"])
+        log(f"soak: median {soak_rec['median_ms_first']} -> {soak_rec['median_ms_last']} ms, "
+            f"drift {soak_rec['drift_pct']}%, p99 max {soak_rec['p99_ms_max']} ms")
+
     out = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "step_ms_percentiles": dist,
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": c["workload"], "layers": cfg.layers, "M": M, "ctx": cfg.ctx, "bits": cfg.bits,
                    "vocab": V, "bytes_per_step": nbytes},
@@ -631,6 +682,7 @@ def main() -> int:
                                "per projection kind, weighted by the step's launch counts"},
         "cpu_baseline": cpu,
         "next_rows": nxt,
+        "soak": soak_rec,
     }
     print(json.dumps(out), flush=True)
     return 0
