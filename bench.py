@@ -205,6 +205,48 @@ def qmm_roofline(torch, stack, reps: int = 5) -> dict:
             "achieved_GBs": avg_bytes / (avg_ms * 1e-3) / 1e9}
 
 
+def qmm_cost_curve(torch, bits: int, N: int = 17408, K: int = 5120,
+                   Ms=(1, 2, 3, 4, 6, 8, 12, 16)) -> dict:
+    """µs per skinny-QMM launch at each verify width M for one dense projection
+    of the shape the pages tabulate, (M, 5120) x (17408, 5120)^T (page
+    "Speculative decoding and MTP on Apple silicon", Facts), on the tiled pack
+    with the store epilogue (bf16 out): the launches of each M are captured into
+    one graph that rotates over distinct weights totalling at least 2 GiB, so
+    every weight byte comes from HBM. Returns µs, GB/s and cost(M)/cost(M=1)."""
+    from speculative_decoding_verify_vq_amd import vq
+    from speculative_decoding_verify_vq_amd.stack import QPack, qmm_algorithmic_bytes
+    from synth import bf16_normal_torch, random_words_torch
+    dev = torch.device("cuda")
+    one = QPack(torch.empty(0), N, K, bits).nbytes()
+    n = max(8, -(-(2 << 30) // one))
+    packs = []
+    for i in range(n):
+        wq = random_words_torch(N * K * bits // 32, 700 + i, dev)
+        sc = bf16_normal_torch((N, K // 64), 0.02, 0.005, 800 + i, dev)
+        bi = bf16_normal_torch((N, K // 64), 0.0, 0.01, 900 + i, dev)
+        packs.append(QPack.from_rows(wq, sc, bi, bits, N, K))
+        del wq, sc, bi
+    torch.cuda.synchronize()
+    ws = torch.zeros(max(vq.qmm_packed_workspace_bytes(bits, m, N, K) for m in Ms) + 256, dtype=torch.uint8,
+                     device=dev)
+    wsv = ws[(-ws.data_ptr()) % 256:]
+    res = {}
+    for m in Ms:
+        x = torch.randn((m, K), device=dev).to(torch.bfloat16)
+        y = torch.empty((m, N), device=dev, dtype=torch.bfloat16)
+        g = capture(torch, lambda: [vq.qmm_packed(x, p.packed, bits, N, K, out=y, workspace=wsv) for p in packs])
+        us = 1e3 * time_graph(torch, g, 5, 1) / n
+        del g
+        res[str(m)] = {"us": round(us, 2),
+                       "GBs": round(qmm_algorithmic_bytes(m, N, K, bits) / (us * 1e-6) / 1e9, 1)}
+    base = res[str(Ms[0])]["us"]
+    for v in res.values():
+        v["cost_ratio"] = round(v["us"] / base, 4)
+    del packs, ws
+    torch.cuda.empty_cache()
+    return {"shape": f"(M, {K}) x ({N}, {K})^T, {bits}-bit g64, tiled pack, bf16 out", "per_M": res}
+
+
 def _time_calls(torch, fns, reps: int = 5) -> float:
     """µs per call of the callables `fns` (one each), captured into one graph and
     replayed `reps` times after one warm-up replay."""
@@ -639,6 +681,12 @@ def main() -> int:
         log(f"{cfg.layers}-layer stack: M=1 {res[1]:.3f} ms, M=8 {res[8]:.3f} ms, ratio {ratio:.3f}; "
             f"{ {m: round(v / res[1], 3) for m, v in res.items()} }")
 
+    curves = None
+    if not args.no_ratio:
+        curves = {f"{b}bit": qmm_cost_curve(torch, b) for b in (4, 8)}
+        log("QMM cost(M)/cost(1) at (M,5120)x(17408,5120)^T: " + "; ".join(
+            f"{k}: " + " ".join(f"{m}:{v['cost_ratio']}" for m, v in c["per_M"].items()) for k, c in curves.items()))
+
     roof = qmm_roofline(torch, stack)
     log(f"QMM per launch: {roof['avg_ms'] * 1e3:.1f} us, {roof['achieved_GBs']:.0f} GB/s; {roof['per_kind']}")
     traffic = qmm_traffic(roof["avg_bytes"])
@@ -671,6 +719,7 @@ def main() -> int:
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "cost_ratio_m8_m1": None if ratio is None else round(ratio, 4),
         "cost_curve": curve,
+        "qmm_cost_curve": curves,
         "roofline": {"bound": "hbm", "achieved": round(roof["achieved_GBs"], 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(roof["achieved_GBs"] / PEAK_HBM_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
