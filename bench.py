@@ -53,6 +53,10 @@ PROFILE_CMDS = {
              "--layers 8 --no-ratio --no-cpu-baseline --no-next --copy-calibration",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o write -- python3 bench.py --steps 1 --warmup 0 "
              "--layers 8 --no-ratio --no-cpu-baseline --no-next --copy-calibration",
+    "curve_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o fetch -- python3 bench.py "
+                   "--qmm-curve-counters {bits} --copy-calibration",
+    "curve_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o write -- python3 bench.py "
+                   "--qmm-curve-counters {bits} --copy-calibration",
 }
 
 
@@ -245,6 +249,78 @@ def qmm_cost_curve(torch, bits: int, N: int = 17408, K: int = 5120,
     del packs, ws
     torch.cuda.empty_cache()
     return {"shape": f"(M, {K}) x ({N}, {K})^T, {bits}-bit g64, tiled pack, bf16 out", "per_M": res}
+
+
+CURVE_MS = (1, 2, 3, 4, 6, 8, 12, 16)
+CURVE_PACKS = 8
+
+
+def qmm_curve_counter_run(torch, bits: int, N: int = 17408, K: int = 5120) -> None:
+    """For hardware counters: CURVE_PACKS distinct (N, K) weights, then for each
+    verify width M in CURVE_MS one eager launch on each weight, in that order
+    (the dispatch order is what the counter summary relies on)."""
+    from speculative_decoding_verify_vq_amd import vq
+    from speculative_decoding_verify_vq_amd.stack import QPack
+    from synth import bf16_normal_torch, random_words_torch
+    dev = torch.device("cuda")
+    packs = []
+    for i in range(CURVE_PACKS):
+        wq = random_words_torch(N * K * bits // 32, 700 + i, dev)
+        sc = bf16_normal_torch((N, K // 64), 0.02, 0.005, 800 + i, dev)
+        bi = bf16_normal_torch((N, K // 64), 0.0, 0.01, 900 + i, dev)
+        packs.append(QPack.from_rows(wq, sc, bi, bits, N, K))
+        del wq, sc, bi
+    ws = torch.zeros(max(vq.qmm_packed_workspace_bytes(bits, m, N, K) for m in CURVE_MS) + 256,
+                     dtype=torch.uint8, device=dev)
+    wsv = ws[(-ws.data_ptr()) % 256:]
+    torch.cuda.synchronize()
+    for m in CURVE_MS:
+        x = torch.randn((m, K), device=dev).to(torch.bfloat16)
+        y = torch.empty((m, N), device=dev, dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        for p in packs:
+            vq.qmm_packed(x, p.packed, bits, N, K, out=y, workspace=wsv)
+        torch.cuda.synchronize()
+    log(f"counter run: {len(CURVE_MS)} widths x {CURVE_PACKS} launches of ({N}, {K}) {bits}-bit")
+
+
+def summarize_curve_counters(prof_dir: str, out_dir: str, bits: int, cmd_fetch: str, cmd_write: str,
+                             N: int = 17408, K: int = 5120) -> None:
+    """HBM bytes per launch of one (M, K) x (N, K)^T projection at every verify
+    width, from FETCH_SIZE / WRITE_SIZE passes of qmm_curve_counter_run (the
+    QMM dispatches in order: CURVE_PACKS per width), scaled by the 1 GiB copy."""
+    from speculative_decoding_verify_vq_amd.stack import qmm_algorithmic_bytes
+    per = {}
+    scale = {}
+    for ctr, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        rows = [r for r in _read_csv(os.path.join(prof_dir, sub), "_counter_collection.csv")
+                if r["Counter_Name"] == ctr]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        scale[ctr] = (1 << 20) / max(copies)
+        q = [float(r["Counter_Value"]) for r in rows if "qmm_kernel<" in r["Kernel_Name"]]
+        if len(q) != len(CURVE_MS) * CURVE_PACKS:
+            raise RuntimeError(f"{ctr}: expected {len(CURVE_MS) * CURVE_PACKS} QMM dispatches, found {len(q)}")
+        for i, m in enumerate(CURVE_MS):
+            v = q[i * CURVE_PACKS:(i + 1) * CURVE_PACKS]
+            per.setdefault(m, {})[ctr] = sum(v) / len(v)
+    md = [f"# HBM traffic of one (M, {K}) x ({N}, {K})^T projection, {bits}-bit g64, at every verify width", "",
+          "Two counter passes of the same command (8 distinct weights, one eager launch on each per width, plus a "
+          "1 GiB device copy for scaling):", "", f"    {cmd_fetch}", f"    {cmd_write}", "",
+          f"Scaling: fetch counts x {scale['FETCH_SIZE']:.5f}, write counts x {scale['WRITE_SIZE']:.5f} (the copy "
+          "reads and writes 1048576 KiB).", "",
+          "| M | FETCH_SIZE KiB (raw) | WRITE_SIZE KiB (raw) | HBM bytes (scaled) | algorithmic bytes | ratio | "
+          "HBM bytes / HBM bytes at M=1 |", "|---|---|---|---|---|---|---|"]
+    base = None
+    for m in CURVE_MS:
+        f, w = per[m]["FETCH_SIZE"], per[m]["WRITE_SIZE"]
+        hbm = 1024 * (f * scale["FETCH_SIZE"] + w * scale["WRITE_SIZE"])
+        alg = qmm_algorithmic_bytes(m, N, K, bits)
+        base = base or hbm
+        md.append(f"| {m} | {f:.1f} | {w:.1f} | {int(hbm)} | {alg} | {hbm / alg:.3f} | {hbm / base:.3f} |")
+    md += ["", "The weight stream is read once per launch whatever M is: the bytes grow only by the activations, "
+               "the outputs and the split-K partials of the extra rows."]
+    with open(os.path.join(out_dir, f"qmm_traffic_by_M_{bits}bit.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
 
 
 def _time_calls(torch, fns, reps: int = 5) -> float:
@@ -614,6 +690,11 @@ def main() -> int:
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write the profiles/ summaries from a profiled run's CSV output (kt/, fetch/, write/ under "
                          "DIR) and exit; needs no GPU")
+    ap.add_argument("--qmm-curve-counters", type=int, default=0, metavar="BITS",
+                    help="only the launches that the per-width counter summary reads (with --copy-calibration), "
+                         "then exit")
+    ap.add_argument("--summarize-curve-profiles", metavar="DIR", default=None,
+                    help="write profiles/qmm_traffic_by_M_<bits>bit.md from fetch/ and write/ under DIR (no GPU)")
     ap.add_argument("--soak", type=float, default=0.0, metavar="SECONDS",
                     help="after the measurements, replay the step back to back for this long and report the "
                          "per-second median / p99 series (sustained-run check)")
@@ -623,6 +704,11 @@ def main() -> int:
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, os.path.join(ROOT, "profiles"), PROFILE_CMDS["kt"],
                            PROFILE_CMDS["fetch"], PROFILE_CMDS["write"])
+        return 0
+    if args.summarize_curve_profiles:
+        b = args.qmm_curve_counters or 4
+        summarize_curve_counters(args.summarize_curve_profiles, os.path.join(ROOT, "profiles"), b,
+                                 PROFILE_CMDS["curve_fetch"].format(bits=b), PROFILE_CMDS["curve_write"].format(bits=b))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the verify step; runs on more than one GPU are not "
@@ -640,6 +726,9 @@ def main() -> int:
     T_cap = cfg.ctx + 16
     if args.copy_calibration:
         copy_calibration(torch)
+    if args.qmm_curve_counters:
+        qmm_curve_counter_run(torch, args.qmm_curve_counters)
+        return 0
     log(f"config {args.config}: generating weights and KV caches on the device")
     w = make_weights(cfg, torch, 1000 * args.config, T_cap)
     stack = DenseVerifyStack(cfg, w)

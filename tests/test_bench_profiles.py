@@ -76,3 +76,20 @@ def test_summarize_profiles(tmp_path):
     want = (64 * (1 + 2 + 3 + 4) + 5) / 257
     assert f"{want:.2f} us" in kt and "cmd-kt" in kt
     assert "| gate_up | 64 |" in open(os.path.join(out, "qmm_traffic_4bit_M4.md")).read()
+
+
+def test_summarize_curve_counters(tmp_path):
+    """Per-width counter summary: CURVE_PACKS dispatches per width, in order."""
+    prof, out = str(tmp_path / "prof"), str(tmp_path / "out")
+    os.makedirs(out)
+    name = QMM.format(e=0, n="false", c="false")
+    ctr_h = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    for ctr, sub, copy_val in (("FETCH_SIZE", "fetch", 524288.0), ("WRITE_SIZE", "write", 1048576.0)):
+        rows = [[COPY, 131072, ctr, copy_val]]
+        for i, m in enumerate(bench.CURVE_MS):
+            rows += [[name, 136 * 5 * 256, ctr, 1000.0 + 10 * i]] * bench.CURVE_PACKS
+        _write(os.path.join(prof, sub, f"{sub}_counter_collection.csv"), ctr_h, rows)
+    bench.summarize_curve_counters(prof, out, 4, "f", "w")
+    md = open(os.path.join(out, "qmm_traffic_by_M_4bit.md")).read()
+    # width 3 (index 2): fetch 1020 KiB x 2 + write 1020 KiB x 1
+    assert f"| 3 | 1020.0 | 1020.0 | {1024 * 3 * 1020} |" in md
