@@ -424,10 +424,11 @@ def next_rows(torch, stack, w, single_ms: float) -> dict:
     return res
 
 
-def qmm_traffic(avg_bytes: float):
+def qmm_traffic(avg_bytes: float, bits: int, M: int):
     """HBM bytes per QMM launch from the committed counter summary, if it was taken
-    on the current kernel source (else None): FETCH_SIZE + WRITE_SIZE per dispatch,
-    each scaled by what the counter reads for a copy of known size."""
+    on the current kernel source and on this workload's weight width and verify
+    rows (else None): FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by what the
+    counter reads for a copy of known size."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "qmm_traffic.json")
     src = os.path.join(ROOT, "speculative_decoding_verify_vq_amd", "csrc", "qmm.hip")
@@ -438,7 +439,7 @@ def qmm_traffic(avg_bytes: float):
             digest = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
-    if rec.get("qmm_hip_sha256") != digest:
+    if rec.get("qmm_hip_sha256") != digest or rec.get("bits") != bits or rec.get("M") != M:
         return None
     return {"bytes_per_launch": rec["hbm_bytes_per_launch"],
             "ratio_to_algorithmic": round(rec["hbm_bytes_per_launch"] / avg_bytes, 3),
@@ -643,6 +644,7 @@ def _summarize_traffic(prof_dir: str, out_dir: str, cmd_fetch: str, cmd_write: s
     rec = {"kernel": "qmm_kernel (tiled pack; q|k|v with RMSNorm, o and down with the residual epilogue, gate|up "
                      "with RMSNorm and SwiGLU, lm_head with RMSNorm)",
            "workload": "4-bit g64 verify step, M=4 (hidden 5120, MLP 17408, lm_head 248320)",
+           "bits": cfg.bits, "M": cfg.M,
            "qmm_hip_sha256": digest, "fetch_scale": round(scale["FETCH_SIZE"], 5),
            "write_scale": round(scale["WRITE_SIZE"], 5),
            "calibration": "__amd_rocclr_copyBuffer of a 1 GiB bf16 tensor (torch copy_): reads and writes 1048576 KiB",
@@ -778,7 +780,7 @@ def main() -> int:
 
     roof = qmm_roofline(torch, stack)
     log(f"QMM per launch: {roof['avg_ms'] * 1e3:.1f} us, {roof['achieved_GBs']:.0f} GB/s; {roof['per_kind']}")
-    traffic = qmm_traffic(roof["avg_bytes"])
+    traffic = qmm_traffic(roof["avg_bytes"], cfg.bits, cfg.M)
 
     nxt = None
     if not args.no_next:
