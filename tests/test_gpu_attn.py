@@ -52,6 +52,21 @@ def test_config2_sampled(vq, ctx, M):
     assert_close(got, ref, f"ctx={ctx} M={M}")
 
 
+def test_config4_context_sampled(vq):
+    """The 8-bit step's attention shape: 8 rows over 131072 committed positions
+    (T = 131080, 129 key ranges of 32 tiles per KV head and the combine), on
+    sampled (row, head) pairs."""
+    M, Hq, Hkv, D, ctx = 8, 24, 4, 256, 131072
+    T = ctx + M
+    q, k, v = attn_inputs(4, M, Hq, Hkv, D, T, extra=ctx)
+    out = _run(vq, q, k, v, T, 1 / 16)
+    rng = np.random.default_rng(ctx + M)
+    pairs = [(m, int(h)) for m in range(M) for h in rng.choice(Hq, 2, replace=False)]
+    ref = oa.multirow_attention(q, k, v, M, Hq, Hkv, D, T, T, 1 / 16, pairs=pairs)
+    got = np.stack([out[m, h] for m, h in pairs])
+    assert_close(got, ref, f"ctx={ctx} M={M}")
+
+
 def test_deterministic(vq):
     q, k, v = attn_inputs(21, 8, 24, 4, 256, 8200)
     a = _run(vq, q, k, v, 8200, 1 / 16)
