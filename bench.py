@@ -544,7 +544,8 @@ def _qmm_launch_groups(rows: list, grid_key) -> list:
     return list(groups.items())
 
 
-def summarize_profiles(prof_dir: str, out_dir: str, cmd_kt: str, cmd_fetch: str, cmd_write: str) -> None:
+def summarize_profiles(prof_dir: str, out_dir: str, cmd_kt: str, cmd_fetch: str, cmd_write: str,
+                       config: int = 3) -> None:
     """Writes the committed profile summaries from a profiled run's CSV output:
     <prof_dir>/kt (rocprofv3 --kernel-trace --stats -f csv), <prof_dir>/fetch and
     <prof_dir>/write (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE -f csv, runs with
@@ -552,12 +553,15 @@ def summarize_profiles(prof_dir: str, out_dir: str, cmd_kt: str, cmd_fetch: str,
     and qmm_traffic.json (read by qmm_traffic above). A part whose CSV
     directories are missing is left as it is."""
     if os.path.isdir(os.path.join(prof_dir, "kt")):
-        _summarize_trace(prof_dir, out_dir, cmd_kt)
+        _summarize_trace(prof_dir, out_dir, cmd_kt, config)
     if os.path.isdir(os.path.join(prof_dir, "fetch")) and os.path.isdir(os.path.join(prof_dir, "write")):
         _summarize_traffic(prof_dir, out_dir, cmd_fetch, cmd_write)
 
 
-def _summarize_trace(prof_dir: str, out_dir: str, cmd_kt: str) -> None:
+def _summarize_trace(prof_dir: str, out_dir: str, cmd_kt: str, config: int = 3) -> None:
+    c = CONFIGS[config]
+    tag = f"{c['bits']}bit_M{c['M']}"
+    ctx_k = c["ctx"] // 1024
     stats = _read_csv(os.path.join(prof_dir, "kt"), "_kernel_stats.csv")
     trace = _read_csv(os.path.join(prof_dir, "kt"), "_kernel_trace.csv")
     tot = sum(float(r["TotalDurationNs"]) for r in stats)
@@ -587,7 +591,7 @@ def _summarize_trace(prof_dir: str, out_dir: str, cmd_kt: str) -> None:
             with open(path) as f:
                 txt = [ln for ln in f.read().splitlines() if ln.startswith("{")]
             bench_line = json.loads(txt[-1]) if txt else None
-    md = ["# Kernel trace: verify step, 4-bit g64, M=4, 16k context", "",
+    md = [f"# Kernel trace: verify step, {c['bits']}-bit g64, M={c['M']}, {ctx_k}k context", "",
           "Command (from the repository root, on one MI355X):", "", f"    {cmd_kt}", "",
           "Durations summed over every dispatch of the command (rocprofv3 kernel stats): weight packing, the eager",
           "warm-up pass, the graph capture, the step replays and the per-projection QMM graphs the bench times for",
@@ -602,7 +606,7 @@ def _summarize_trace(prof_dir: str, out_dir: str, cmd_kt: str) -> None:
         md.append(f"The bench's own HIP-event timing in the same command (graph replays, per launch): {pk}; "
                   f"weighted the same way {rf['avg_launch_us']} us per launch.")
         md.append(f"Step: {bench_line['ms_per_step']} ms ({bench_line['value']} GB/s) under the profiler.")
-    with open(os.path.join(out_dir, "qmm_kernel_verify_step_4bit_M4.md"), "w") as f:
+    with open(os.path.join(out_dir, f"qmm_kernel_verify_step_{tag}.md"), "w") as f:
         f.write("\n".join(md) + "\n")
 
 
@@ -704,8 +708,11 @@ def main() -> int:
                     help="run a 1 GiB device copy first (for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles, os.path.join(ROOT, "profiles"), PROFILE_CMDS["kt"],
-                           PROFILE_CMDS["fetch"], PROFILE_CMDS["write"])
+        kt_cmd = PROFILE_CMDS["kt"]
+        if args.config != 3:
+            kt_cmd = kt_cmd.replace("bench.py ", f"bench.py --config {args.config} ")
+        summarize_profiles(args.summarize_profiles, os.path.join(ROOT, "profiles"), kt_cmd,
+                           PROFILE_CMDS["fetch"], PROFILE_CMDS["write"], args.config)
         return 0
     if args.summarize_curve_profiles:
         b = args.qmm_curve_counters or 4
