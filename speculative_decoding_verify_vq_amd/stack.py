@@ -166,9 +166,11 @@ class DenseVerifyStack:
                       residual=self.h if epilogue == vq.VQ_EPI_RESIDUAL else None, out=out, y_sumsq=y_sumsq,
                       workspace=self._wsv("qmm"))
 
-    def forward_hidden(self, h_in: torch.Tensor) -> torch.Tensor:
+    def forward_hidden(self, h_in: torch.Tensor, after_layer=None) -> torch.Tensor:
         """Runs the layers on h_in [M, hidden] (bf16); returns the final hidden rows
-        (their sums of squares are left in self.ss for the final RMSNorm)."""
+        (their sums of squares are left in self.ss for the final RMSNorm).
+        ``after_layer(layer, h)``, if given, is called after each layer with the
+        hidden rows (on the stream, before the next layer's launches)."""
         cfg = self.cfg
         self.h.copy_(h_in)
         vq.row_sumsq(self.h, out=self.ss)
@@ -197,17 +199,20 @@ class DenseVerifyStack:
             self._qmm(c, lay["o"], self.h, epilogue=vq.VQ_EPI_RESIDUAL, y_sumsq=self.ss)
             self._qmm(self.h, lay["gate_up"], self.act, norm=True, epilogue=vq.VQ_EPI_SWIGLU)
             self._qmm(self.act, lay["down"], self.h, epilogue=vq.VQ_EPI_RESIDUAL, y_sumsq=self.ss)
+            if after_layer is not None:
+                after_layer(li, self.h)
         return self.h
 
-    def step(self, h_in, draft_logits, drafts, uniforms):
+    def step(self, h_in, draft_logits, drafts, uniforms, after_layer=None):
         """One verify step: layers, lm_head, exact acceptance.
 
         h_in bf16 [B*M, hidden] (sequence b's rows at b*M); draft_logits float32
         [B, K, V]; drafts int32 [B, K]; uniforms float32 [B, K+1]. Returns
-        (tokens int32 [B, K+1], n_accepted int32 [B]).
+        (tokens int32 [B, K+1], n_accepted int32 [B]). ``after_layer`` as in
+        forward_hidden.
         """
         cfg = self.cfg
-        self.forward_hidden(h_in)
+        self.forward_hidden(h_in, after_layer)
         self._qmm(self.h, self.w.lm_head, self.logits.view(cfg.rows, cfg.vocab), norm=True)
         vq.spec_accept(self.logits, draft_logits, drafts, uniforms, logits=True, temperature=cfg.temperature,
                        top_k=cfg.top_k, top_p=cfg.top_p, probs_out=self.probs, out_tokens=self.tokens,

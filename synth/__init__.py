@@ -51,21 +51,24 @@ def bf16_normal(g: np.random.Generator, shape, mean: float = 0.0, std: float = 1
 
 # --------------------------------------------------------------------------- QMM
 def qmm_weights(config: int, N: int, K: int, bits: int = 4, group_size: int = 64,
-                seed: int = 0, layer: int = 0):
+                seed: int = 0, layer: int = 0, scale_mean: float = 0.02, scale_std: float = 0.005,
+                bias_std: float = 0.01):
     """Quantized weight pack of one linear layer W[N, K].
 
     * codes: uniform integers in [0, 2**bits); drawn as uniform random 32-bit
       words, which makes every 4-bit or 8-bit field uniform. Stored as
       ``uint32[N, K * bits // 32]`` (the packing convention is documented in
       include/vq.h).
-    * scales ~ N(0.02, 0.005), biases ~ N(0, 0.01), bf16, ``[N, K // group_size]``.
+    * scales ~ N(0.02, 0.005), biases ~ N(0, 0.01), bf16, ``[N, K // group_size]``
+      (the distribution of the dense-layer configurations; other means and
+      spreads give stacks whose activations stay O(1)).
     """
     assert K % group_size == 0 and (K * bits) % 32 == 0
     words = rng(config, "W", seed, layer).integers(0, 2**32, size=(N, K * bits // 32),
                                                    dtype=np.uint64).astype(np.uint32)
     G = K // group_size
-    scales = bf16_normal(rng(config, "S", seed, layer), (N, G), 0.02, 0.005)
-    biases = bf16_normal(rng(config, "B", seed, layer), (N, G), 0.0, 0.01)
+    scales = bf16_normal(rng(config, "S", seed, layer), (N, G), scale_mean, scale_std)
+    biases = bf16_normal(rng(config, "B", seed, layer), (N, G), 0.0, bias_std)
     return {"wq": words, "scales": scales, "biases": biases,
             "bits": bits, "group_size": group_size, "N": N, "K": K}
 
