@@ -176,24 +176,35 @@ struct SelectLds {
 // ------------------------------------------- state of the chunked pipeline
 constexpr int kChunk = 8192;
 constexpr int kCT = 256;           // threads of the chunk kernels
-constexpr int kCandCap = 16384;    // keys gathered per row
-constexpr int kTopShift = 38;      // the histogram bin of a key is key >> 38 (12 bits)
+constexpr int kCandCap = 16384;    // keys gathered per row (2^14: a level-2 region never holds more)
+constexpr int kTopShift = 38;      // level 0: the histogram bin of a key is key >> 38 (12 bits)
+constexpr int kLevels = 3;         // histogram levels: shifts 38, 26, 14 (12 bits each)
 constexpr int kCandBits = 8;       // digit width of the selects over gathered keys
 
+// The select state of a row. A region is the set of keys with
+// (key >> shift) == prefix; the select is known to cross inside the current
+// region. A region too crowded to gather is refined by one more histogram level
+// over the whole chip (shift 38 -> 26 -> 14); a level-2 region holds at most
+// 2^14 distinct keys, so it can always be gathered.
 struct RowState {
   u64 total;         // mass of the row
-  u64 above;         // weight of the keys above the candidate bin
+  u64 above;         // select weight (count or mass) of the keys above the region
+  u64 above_mass;    // mass of the keys above the region
   u64 thr;           // weight the select must reach
+  u64 prefix;        // the region
   uint32_t bad;      // an invalid probability was seen
   uint32_t cand_n;   // keys gathered
-  int bin;           // candidate bin
+  int shift;         // 38, 26 or 14
   int phase;         // 0 top-k select, 1 top-p select, 3 left to the rows kernel
   int pending;       // a compact + resolve is due
-  int pad;
+  int refine;        // the histogram level due (1 or 2), 0 none
+  int levels;        // levels the top-k select went through (1..3)
+  int kbin[kLevels]; // its crossing bin at each of them
 };
 
-// Clears a row's histogram and select state: the first kernel of every call
-// (the workspace layout depends on the shapes, so nothing is assumed zero).
+// Clears a row's level-0 histogram and select state: the first kernel of every
+// call (the workspace layout depends on the shapes, so nothing is assumed zero;
+// the level-1 and level-2 histograms are cleared when a row needs them).
 __global__ __launch_bounds__(256) void rows_clear_kernel(RowState* __restrict__ st, uint32_t* __restrict__ hcnt,
                                                          u64* __restrict__ hmass) {
   const int r = blockIdx.x;
@@ -636,13 +647,18 @@ __global__ __launch_bounds__(kEntryThreads) void accept_entry_kernel(
 //            merged into a per-row histogram with global atomics
 //   find     (one workgroup per row) the bin where the first select crosses;
 //            rows without truncation, invalid rows or an empty select finish
-//   compact  the keys of that bin gathered per row (at most kCandCap)
+//   refine   (levels 1 and 2, a chunked histogram pass + a per-row find each)
+//            a crossing bin holding more than kCandCap keys is narrowed by the
+//            next 12 key bits, over the whole chip; after level 2 a region
+//            holds at most 2^14 = kCandCap keys
+//   compact  the keys of the crossing region gathered per row
 //   resolve  (one workgroup per row) radix select over the gathered keys; a
-//            top-p walk after top-k that crosses in a higher bin asks for a
-//            second compact + resolve
-// A row whose crossing bin holds more than kCandCap keys is left to the
-// single-workgroup rows kernel above. Every count is an integer, so the
-// result does not depend on how the work is split.
+//            top-p walk after top-k that crosses in a bin above the top-k
+//            path asks for a second compact + resolve
+// Only a top-p walk after a top-k wider than kCandCap can meet a region too
+// crowded to gather; the single-workgroup rows kernel above finishes those
+// rows. Every count is an integer, so the result does not depend on how the
+// work is split.
 // f(x, v) for x in [x0, x1): scalar head to 16-byte alignment, float4 body with
 // kUnroll units per thread in flight, scalar tail.
 template <typename F>
@@ -797,42 +813,49 @@ __global__ __launch_bounds__(kCT) void rows_hist_kernel(
   }
 }
 
-// Walks the row histogram from the top bin down (bins > `below` only when
+// Walks a 4096-bin histogram from the top bin down (bins > `below` only when
 // below >= 0): the bin where the running weight (count or mass) first reaches
-// thr, the weight above it and its count. Returns -1 if thr is not reached.
+// thr, its count, and the weight and mass of the bins above it; also the weight
+// of every bin considered. bin = -1 if thr is not reached.
 struct Crossing {
   int bin;
-  u64 above;
   uint32_t count;
+  u64 above;
+  u64 above_mass;
+  u64 total;
 };
 
 __device__ Crossing find_bin(const uint32_t* hc, const u64* hm, bool by_mass, u64 thr, int below, u64* scan,
                              Crossing* out) {
   const int tid = threadIdx.x;  // 1024 threads, 4 bins each, descending
-  u64 w[4];
+  u64 w[4], m[4];
   uint32_t cc[4];
-  u64 lsum = 0;
+  u64 lsum = 0, lmass = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int b = kBins - 1 - (4 * tid + i);
     const bool in = b > below;
     cc[i] = in ? hc[b] : 0u;
-    w[i] = in ? (by_mass ? hm[b] : (u64)cc[i]) : 0ull;
+    m[i] = in ? hm[b] : 0ull;
+    w[i] = by_mass ? m[i] : (u64)cc[i];
     lsum += w[i];
+    lmass += m[i];
   }
-  u64 tot;
+  u64 tot, totm;
   const u64 excl = block_excl_scan<u64, kRowThreads>(lsum, scan, tot);
-  if (tid == 0) *out = Crossing{-1, 0, 0};
+  const u64 exclm = block_excl_scan<u64, kRowThreads>(lmass, scan, totm);
+  if (tid == 0) *out = Crossing{-1, 0u, 0ull, 0ull, tot};
   __syncthreads();
   if (excl < thr && thr <= excl + lsum) {
-    u64 run = excl;
+    u64 run = excl, runm = exclm;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (run + w[i] >= thr) {
-        *out = Crossing{kBins - 1 - (4 * tid + i), run, cc[i]};
+        *out = Crossing{kBins - 1 - (4 * tid + i), cc[i], run, runm, tot};
         break;
       }
       run += w[i];
+      runm += m[i];
     }
   }
   __syncthreads();
@@ -841,10 +864,18 @@ __device__ Crossing find_bin(const uint32_t* hc, const u64* hm, bool by_mass, u6
   return res;
 }
 
+// Zeroes one row's histogram of a level (all threads of the workgroup).
+__device__ __forceinline__ void clear_hist(uint32_t* hc, u64* hm) {
+  for (int b = threadIdx.x; b < kBins; b += blockDim.x) {
+    hc[b] = 0u;
+    hm[b] = 0ull;
+  }
+}
+
 __global__ __launch_bounds__(kRowThreads) void rows_find_kernel(int V, int top_k, uint32_t tp,
                                                                 RowState* __restrict__ st,
-                                                                uint32_t* __restrict__ hcnt,
-                                                                u64* __restrict__ hmass, RowMeta* __restrict__ meta) {
+                                                                uint32_t* __restrict__ hcnt, u64* __restrict__ hmass,
+                                                                int64_t lvl_stride, RowMeta* __restrict__ meta) {
   __shared__ u64 scan[kRowThreads / 64 + 1];
   __shared__ Crossing cr;
   const int r = blockIdx.x;
@@ -867,19 +898,105 @@ __global__ __launch_bounds__(kRowThreads) void rows_find_kernel(int V, int top_k
     if (threadIdx.x == 0) meta[r] = out;
     return;
   }
+  const bool crowded = c.count > (uint32_t)kCandCap;
+  if (crowded)
+    clear_hist(hcnt + lvl_stride + (int64_t)r * kBins, hmass + lvl_stride + (int64_t)r * kBins);
   if (threadIdx.x == 0) {
     RowState s = s0;
-    s.bin = c.bin;
+    s.prefix = (u64)c.bin;
+    s.shift = kTopShift;
     s.above = c.above;
+    s.above_mass = c.above_mass;
     s.thr = thr;
     s.cand_n = 0;
-    if (c.count > (uint32_t)kCandCap) {
-      s.phase = 3;
+    s.phase = use_k ? 0 : 1;
+    s.levels = 1;
+    s.kbin[0] = c.bin;
+    s.pending = crowded ? 0 : 1;
+    s.refine = crowded ? 1 : 0;
+    st[r] = s;
+  }
+}
+
+// One more histogram level over a crowded region, spread over the chip like
+// rows_hist: per (chunk, row) the next 12 key bits of the region's keys, merged
+// into the row's level histogram with global atomics. Rows with nothing to
+// refine at this level return at once.
+__global__ __launch_bounds__(kCT) void rows_refine_hist_kernel(
+    const float* __restrict__ p, const float* __restrict__ q, int input_kind, int64_t ps, int64_t qs, int K, int V,
+    int C, const float* __restrict__ probs, const RowState* __restrict__ st, uint32_t* __restrict__ hcnt,
+    u64* __restrict__ hmass, int64_t lvl_stride, int level) {
+  __shared__ uint32_t cnt[kBins];
+  __shared__ u64 mas[kBins];
+  const int c = blockIdx.x % C, r = blockIdx.x / C;
+  if (st[r].refine != level) return;
+  const u64 prefix = st[r].prefix;
+  const int shift = st[r].shift;
+  const int sub = shift - kDigitBits;
+  const float* row = input_kind == 1 ? probs + (int64_t)r * V : row_ptr(p, q, ps, qs, K, V, r);
+  const int x0 = c * kChunk, x1 = min(V, x0 + kChunk);
+  for (int b = threadIdx.x; b < kBins; b += kCT) {
+    cnt[b] = 0u;
+    mas[b] = 0ull;
+  }
+  __syncthreads();
+  for_range(row, x0, x1, [&](int x, float v) {
+    const u64 key = key_of(v, x, V);
+    if ((key >> shift) != prefix) return;
+    const int bin = (int)((key >> sub) & (u64)(kBins - 1));
+    atomicAdd(&cnt[bin], 1u);
+    const u64 m = mass_of(v);
+    if (m) atomicAdd(&mas[bin], m);
+  });
+  __syncthreads();
+  uint32_t* hc = hcnt + (int64_t)level * lvl_stride + (int64_t)r * kBins;
+  u64* hm = hmass + (int64_t)level * lvl_stride + (int64_t)r * kBins;
+  for (int b = threadIdx.x; b < kBins; b += kCT) {
+    if (cnt[b]) atomicAdd(&hc[b], cnt[b]);
+    if (mas[b]) atomicAdd(&hm[b], mas[b]);
+  }
+}
+
+// The crossing bin of a refined region (one workgroup per row at this level):
+// the region narrows by 12 bits; gathered next if it holds at most kCandCap
+// keys, else refined once more.
+__global__ __launch_bounds__(kRowThreads) void rows_refine_find_kernel(RowState* __restrict__ st,
+                                                                       uint32_t* __restrict__ hcnt,
+                                                                       u64* __restrict__ hmass, int64_t lvl_stride,
+                                                                       int level, RowMeta* __restrict__ meta) {
+  __shared__ u64 scan[kRowThreads / 64 + 1];
+  __shared__ Crossing cr;
+  const int r = blockIdx.x;
+  const RowState s0 = st[r];
+  if (s0.refine != level) return;
+  const Crossing c = find_bin(hcnt + (int64_t)level * lvl_stride + (int64_t)r * kBins,
+                              hmass + (int64_t)level * lvl_stride + (int64_t)r * kBins, s0.phase == 1,
+                              s0.thr - s0.above, -1, scan, &cr);
+  // The region's keys weigh at least thr - above, so a crossing exists; a
+  // region at the last level holds at most 2^14 <= kCandCap keys.
+  const bool crowded = c.bin >= 0 && c.count > (uint32_t)kCandCap;
+  if (crowded && level + 1 < kLevels)
+    clear_hist(hcnt + (int64_t)(level + 1) * lvl_stride + (int64_t)r * kBins,
+               hmass + (int64_t)(level + 1) * lvl_stride + (int64_t)r * kBins);
+  if (threadIdx.x == 0) {
+    RowState s = s0;
+    if (c.bin < 0 || (crowded && level + 1 >= kLevels)) {  // not reached
+      s.refine = 0;
       s.pending = 0;
-    } else {
-      s.phase = use_k ? 0 : 1;
-      s.pending = 1;
+      meta[r] = RowMeta{0ull, 0ull, 1, {0, 0, 0}};
+      st[r] = s;
+      return;
     }
+    s.prefix = (s0.prefix << kDigitBits) | (u64)c.bin;
+    s.shift = s0.shift - kDigitBits;
+    s.above = s0.above + c.above;
+    s.above_mass = s0.above_mass + c.above_mass;
+    if (s0.phase == 0) {
+      s.kbin[level] = c.bin;
+      s.levels = level + 1;
+    }
+    s.refine = crowded ? level + 1 : 0;
+    s.pending = crowded ? 0 : 1;
     st[r] = s;
   }
 }
@@ -891,7 +1008,8 @@ __global__ __launch_bounds__(kCT) void rows_compact_kernel(const float* __restri
   __shared__ uint32_t n_lds, w_lds, base;
   const int c = blockIdx.x % C, r = blockIdx.x / C;
   if (!st[r].pending) return;
-  const int bin = st[r].bin;
+  const u64 prefix = st[r].prefix;
+  const int shift = st[r].shift;
   const float* row = input_kind == 1 ? probs + (int64_t)r * V : row_ptr(p, q, ps, qs, K, V, r);
   const int x0 = c * kChunk, x1 = min(V, x0 + kChunk);
   if (threadIdx.x == 0) {
@@ -901,7 +1019,7 @@ __global__ __launch_bounds__(kCT) void rows_compact_kernel(const float* __restri
   __syncthreads();
   // Count this chunk's keys of the bin, reserve their slots, then write them.
   uint32_t mine = 0;
-  for_range(row, x0, x1, [&](int x, float v) { mine += (int)(key_of(v, x, V) >> kTopShift) == bin; });
+  for_range(row, x0, x1, [&](int x, float v) { mine += (key_of(v, x, V) >> shift) == prefix; });
   if (mine) atomicAdd(&n_lds, mine);
   __syncthreads();
   const uint32_t n = n_lds;
@@ -911,29 +1029,28 @@ __global__ __launch_bounds__(kCT) void rows_compact_kernel(const float* __restri
   u64* dst = cand + (int64_t)r * kCandCap + base;
   for_range(row, x0, x1, [&](int x, float v) {
     const u64 key = key_of(v, x, V);
-    if ((int)(key >> kTopShift) == bin) dst[atomicAdd(&w_lds, 1u)] = key;
+    if ((key >> shift) == prefix) dst[atomicAdd(&w_lds, 1u)] = key;
   });
 }
 
 __device__ __forceinline__ float key_value(u64 key) { return __uint_as_float((uint32_t)(key >> 20)); }
 
-// Radix select over gathered keys that share the top 12 bits (key >> 38 ==
-// prefix): the first key, walking down from the largest, at which the running
-// weight (count or mass; only keys >= lo count) reaches thr, given the weight
-// `above` of everything above the bin. 8-bit digits from bit 30 down (the last
-// one 6 bits); a level whose crossing digit holds one key ends the walk.
+// Radix select over gathered keys of one region ((key >> hi_shift) == prefix):
+// the first key, walking down from the largest, at which the running weight
+// (count or mass; only keys >= lo count) reaches thr, given the weight `above`
+// of everything above the region. 8-bit digits from hi_shift down (the last
+// one narrower); a level whose crossing digit holds one key ends the walk.
 struct Sel {
   u64 key;
   u64 mass;
   u64 above;
 };
 
-__device__ Sel select_keys(const u64* __restrict__ keys, int n, u64 prefix, u64 above, u64 thr, bool by_mass, u64 lo,
-                           uint32_t* cnt, u64* mas, u64* scan, Sel* res, int* flag) {
+__device__ Sel select_keys(const u64* __restrict__ keys, int n, u64 prefix, int hi_shift, u64 above, u64 thr,
+                           bool by_mass, u64 lo, uint32_t* cnt, u64* mas, u64* scan, Sel* res, int* flag) {
   const int tid = threadIdx.x;
-  int hi_shift = kTopShift;
-  for (int level = 0; level < 5; ++level) {
-    const int bits = level < 4 ? kCandBits : 6;
+  for (;;) {
+    const int bits = min(kCandBits, hi_shift);
     const int shift = hi_shift - bits;
     const int nb = 1 << bits;
     for (int b = tid; b < nb; b += kRowThreads) {
@@ -970,7 +1087,7 @@ __device__ Sel select_keys(const u64* __restrict__ keys, int n, u64 prefix, u64 
     prefix = s.key;
     above = s.above;
     hi_shift = shift;
-    if (s.mass == 1 || level == 4) {
+    if (s.mass == 1 || shift == 0) {
       // One key left in the crossing digit: it is the answer.
       for (int i = tid; i < n; i += kRowThreads) {
         const u64 key = keys[i];
@@ -982,13 +1099,12 @@ __device__ Sel select_keys(const u64* __restrict__ keys, int n, u64 prefix, u64 
       return out;
     }
   }
-  return Sel{0, 0, 0};  // not reached
 }
 
 __global__ __launch_bounds__(kRowThreads) void rows_resolve_kernel(int V, int top_k, uint32_t tp,
                                                                    RowState* __restrict__ st,
                                                                    uint32_t* __restrict__ hcnt,
-                                                                   u64* __restrict__ hmass,
+                                                                   u64* __restrict__ hmass, int64_t lvl_stride,
                                                                    const u64* __restrict__ cand,
                                                                    RowMeta* __restrict__ meta) {
   __shared__ uint32_t cnt[1 << kCandBits];
@@ -1008,7 +1124,8 @@ __global__ __launch_bounds__(kRowThreads) void rows_resolve_kernel(int V, int to
   const bool use_p = tp < (1u << 24);
   RowMeta out{};
   if (s0.phase == 1) {
-    const Sel sel = select_keys(keys, n, (u64)s0.bin, s0.above, s0.thr, true, 0ull, cnt, mas, scan, &res, &flag);
+    const Sel sel = select_keys(keys, n, s0.prefix, s0.shift, s0.above, s0.thr, true, 0ull, cnt, mas, scan, &res,
+                                &flag);
     out.thresh = sel.key;
     out.z = sel.above + sel.mass;
     out.status = out.z == 0 ? 1 : 0;
@@ -1018,16 +1135,15 @@ __global__ __launch_bounds__(kRowThreads) void rows_resolve_kernel(int V, int to
     }
     return;
   }
-  // Top-k: the top_k-th key, then the kept mass Z_k (bins above + gathered keys >= it).
-  const Sel sk = select_keys(keys, n, (u64)s0.bin, s0.above, s0.thr, false, 0ull, cnt, mas, scan, &res, &flag);
+  // Top-k: the top_k-th key, then the kept mass Z_k (everything above the region
+  // + the region's keys >= it).
+  const Sel sk = select_keys(keys, n, s0.prefix, s0.shift, s0.above, s0.thr, false, 0ull, cnt, mas, scan, &res,
+                             &flag);
   const u64 theta = sk.key;
   u64 m_in = 0;
   for (int i = tid; i < n; i += kRowThreads)
     if (keys[i] >= theta) m_in += mass_of(key_value(keys[i]));
-  u64 m_above = 0;
-  for (int b = s0.bin + 1 + tid; b < kBins; b += kRowThreads) m_above += hmass[(int64_t)r * kBins + b];
-  const u64 zk_above = wg_sum<u64>(m_above, red64);
-  const u64 zk = wg_sum<u64>(m_in, red64) + zk_above;
+  const u64 zk = s0.above_mass + wg_sum<u64>(m_in, red64);
   if (!use_p || zk == 0) {
     out.thresh = theta;
     out.z = zk;
@@ -1038,29 +1154,42 @@ __global__ __launch_bounds__(kRowThreads) void rows_resolve_kernel(int V, int to
     }
     return;
   }
+  // Top-p over the kept set: walking down from the largest key, the mass-weighted
+  // select with thr = ceil(tp * Z_k / 2^24) <= Z_k crosses at a key >= theta, so it
+  // is the walk over the whole row. At each level of the top-k path, the bins
+  // above its crossing bin come first.
   const u64 thr = (u64)(((u128)tp * zk + ((u128)1 << 24) - 1) >> 24);
-  const Crossing c = find_bin(hcnt + (int64_t)r * kBins, hmass + (int64_t)r * kBins, true, thr, s0.bin, scan, &cr);
-  if (c.bin >= 0) {
-    // The top-p walk crosses in a higher bin: gather it next.
-    if (tid == 0) {
-      RowState s = s0;
-      s.bin = c.bin;
-      s.above = c.above;
-      s.thr = thr;
-      s.cand_n = 0;
-      if (c.count > (uint32_t)kCandCap) {
-        s.phase = 3;
-        s.pending = 0;
-      } else {
-        s.phase = 1;
-        s.pending = 1;
+  u64 run = 0, pre = 0;
+  for (int L = 0; L < s0.levels; ++L) {
+    const Crossing c = find_bin(hcnt + (int64_t)L * lvl_stride + (int64_t)r * kBins,
+                                hmass + (int64_t)L * lvl_stride + (int64_t)r * kBins, true, thr - run, s0.kbin[L],
+                                scan, &cr);
+    if (c.bin >= 0) {
+      // The walk crosses in a bin above the top-k path at this level (all of its
+      // keys are kept by top-k, so it holds fewer than top_k keys): gather it next.
+      if (tid == 0) {
+        RowState s = s0;
+        s.prefix = (pre << kDigitBits) | (u64)c.bin;
+        s.shift = kTopShift - kDigitBits * L;
+        s.above = run + c.above;
+        s.thr = thr;
+        s.cand_n = 0;
+        if (c.count > (uint32_t)kCandCap) {
+          s.phase = 3;
+          s.pending = 0;
+        } else {
+          s.phase = 1;
+          s.pending = 1;
+        }
+        st[r] = s;
       }
-      st[r] = s;
+      return;
     }
-    return;
+    run += c.total;
+    pre = (pre << kDigitBits) | (u64)s0.kbin[L];
   }
   // It crosses among the gathered keys kept by top-k.
-  const Sel sp = select_keys(keys, n, (u64)s0.bin, zk_above, thr, true, theta, cnt, mas, scan, &res, &flag);
+  const Sel sp = select_keys(keys, n, s0.prefix, s0.shift, run, thr, true, theta, cnt, mas, scan, &res, &flag);
   out.thresh = sp.key;
   out.z = sp.above + sp.mass;
   out.status = out.z == 0 ? 1 : 0;
@@ -1369,7 +1498,8 @@ AcceptPlan accept_plan(int B, int K, int V, int input_kind, int64_t p_stride, in
   p.table_bytes = p.shared ? align_up((size_t)(K + 1) * V * sizeof(u128), 256) : 0;
   if (p.chunked) {
     p.state_bytes = align_up((size_t)R * sizeof(RowState), 256);
-    p.hist_bytes = align_up((size_t)R * kBins * (sizeof(uint32_t) + sizeof(u64)), 256);
+    p.hist_bytes = align_up((size_t)kLevels * R * kBins * sizeof(uint32_t), 256) +
+                   align_up((size_t)kLevels * R * kBins * sizeof(u64), 256);
     p.cand_bytes = align_up((size_t)R * kCandCap * sizeof(u64), 256);
     p.stats_bytes = input_kind == 1 ? align_up((size_t)R * p.chunks * sizeof(float2), 256) : 0;
   }
@@ -1397,7 +1527,8 @@ hipError_t accept_launch(const AcceptPlan& plan, const float* p, const float* q,
   ws += plan.state_bytes;
   uint32_t* hcnt = reinterpret_cast<uint32_t*>(ws);
   const int64_t R = (int64_t)plan.entries * plan.rows_per_entry;
-  u64* hmass = reinterpret_cast<u64*>(ws + align_up((size_t)R * kBins * sizeof(uint32_t), 16));
+  u64* hmass = reinterpret_cast<u64*>(ws + align_up((size_t)kLevels * R * kBins * sizeof(uint32_t), 256));
+  const int64_t lvl_stride = R * kBins;  // one level's histograms of every row
   ws += plan.hist_bytes;
   u64* cand = reinterpret_cast<u64*>(ws);
   ws += plan.cand_bytes;
@@ -1433,23 +1564,34 @@ hipError_t accept_launch(const AcceptPlan& plan, const float* p, const float* q,
                        C, t_scale, (int)(use_k || use_p), probs, stats, st, hcnt, hmass);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(rows_find_kernel, dim3((unsigned)R), dim3(kRowThreads), 0, stream, V, top_k, tp, st, hcnt,
-                       hmass, meta);
+                       hmass, lvl_stride, meta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (use_k || use_p) {
+      for (int level = 1; level < kLevels; ++level) {
+        hipLaunchKernelGGL(rows_refine_hist_kernel, dim3(cg), dim3(kCT), 0, stream, p, q, input_kind, p_stride,
+                           q_stride, K, V, C, probs, st, hcnt, hmass, lvl_stride, level);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(rows_refine_find_kernel, dim3((unsigned)R), dim3(kRowThreads), 0, stream, st, hcnt, hmass,
+                           lvl_stride, level, meta);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
       const int rounds = (use_k && use_p) ? 2 : 1;
       for (int round = 0; round < rounds; ++round) {
         hipLaunchKernelGGL(rows_compact_kernel, dim3(cg), dim3(kCT), 0, stream, p, q, input_kind, p_stride, q_stride,
                            K, V, C, probs, st, cand);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(rows_resolve_kernel, dim3((unsigned)R), dim3(kRowThreads), 0, stream, V, top_k, tp, st,
-                           hcnt, hmass, cand, meta);
+                           hcnt, hmass, lvl_stride, cand, meta);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
-      // Rows whose crossing bin was too crowded to gather.
-      hipLaunchKernelGGL(accept_rows_kernel, dim3(plan.rows_per_entry, plan.entries), dim3(kRowThreads), 0, stream,
-                         p, q, input_kind, p_stride, q_stride, K, V, t_scale, top_k, tp, probs, meta, st, hcnt,
-                         hmass);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (use_k && use_p && top_k > kCandCap) {
+        // Top-p after a top-k wider than the gather buffer can cross in a bin
+        // too crowded to gather; such rows are finished by the rows kernel.
+        hipLaunchKernelGGL(accept_rows_kernel, dim3(plan.rows_per_entry, plan.entries), dim3(kRowThreads), 0,
+                           stream, p, q, input_kind, p_stride, q_stride, K, V, t_scale, top_k, tp, probs, meta, st,
+                           hcnt, hmass);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
     }
   } else {
     hipLaunchKernelGGL(accept_rows_kernel, dim3(plan.rows_per_entry, plan.entries), dim3(kRowThreads), 0, stream, p,

@@ -186,3 +186,60 @@ def test_huge_logits_stay_valid(vq, B, K):
         rt, rn = oacc.spec_accept(pr[b, : K + 1].astype(np.float64), pr[b, K + 1:].astype(np.float64),
                                   list(drafts[b]), us[b], top_k, top_p)
         assert list(toks[b]) == rt and int(n[b]) == rn
+
+
+def _structured_row(kind: str, V: int, rng) -> np.ndarray:
+    """float32 probability rows whose keys crowd the first histogram levels:
+    one_hot: a few head tokens, every other probability exactly 0 (the zeros
+      share every key bit above the token id: three levels deep);
+    flat_tail: half the mass on a few tokens, the rest uniform over the tail;
+    l1_spread: 20000 tokens whose probabilities share the top key bits and
+      differ in mantissa bits 11..6 (separated at level 1), the rest 0;
+    l2_spread: 30000 tokens differing only in mantissa bits 5..0 (level 2);
+    two_bins: 20000 tokens at 2^-15, 20000 at 2^-17, the rest 0."""
+    p = np.zeros(V, np.float32)
+    ids = rng.permutation(V)
+    if kind == "one_hot":
+        p[ids[0]] = 0.9
+        p[ids[1:6]] = 0.02
+    elif kind == "flat_tail":
+        p[ids[:4]] = 0.125
+        p[ids[4:]] = np.float32(0.5 / (V - 4))
+    elif kind == "l1_spread":
+        j = rng.integers(0, 64, 20000)
+        p[ids[:20000]] = (2.0 ** -16 * (1.0 + j * 2.0 ** -17)).astype(np.float32)
+    elif kind == "l2_spread":
+        j = rng.integers(0, 64, 30000)
+        p[ids[:30000]] = (2.0 ** -16 * (1.0 + j * 2.0 ** -23)).astype(np.float32)
+    elif kind == "two_bins":
+        p[ids[:20000]] = 2.0 ** -15
+        p[ids[20000:40000]] = 2.0 ** -17
+    else:
+        raise ValueError(kind)
+    return p
+
+
+@pytest.mark.parametrize("kind,top_k,top_p", [
+    ("one_hot", 20, 0.95), ("one_hot", 20, 1.0), ("flat_tail", 0, 0.95), ("flat_tail", 20, 0.95),
+    ("l1_spread", 5000, 0.95), ("l1_spread", 5000, 0.9999), ("l1_spread", 0, 0.5),
+    ("l2_spread", 7000, 0.95), ("l2_spread", 7000, 0.99999), ("two_bins", 25000, 0.5), ("two_bins", 30000, 1.0),
+])
+def test_refined_regions(vq, kind, top_k, top_p):
+    """Rows whose crossing bin holds more keys than one gather: the chunked
+    pipeline narrows it by one or two more histogram levels (and the top-p walk
+    after top-k crosses at those levels); a top-p walk after a top-k wider than
+    the gather buffer may still end in the single-workgroup rows kernel
+    (two_bins, top-k 25000). Bit-exact against the oracle at V = 248320, K = 7."""
+    K, V, B = 7, 248320, 2
+    rng = np.random.default_rng(sum(map(ord, kind)) + top_k)
+    P = np.stack([np.stack([_structured_row(kind, V, rng) for _ in range(K + 1)]) for _ in range(B)])
+    Q = np.stack([np.stack([_structured_row(kind, V, rng) for _ in range(K)]) for _ in range(B)])
+    Q[0] = P[0, :K]          # entry 0: q = p, every draft accepted, then the bonus draw
+    ud = uniforms24(9, (B, K), stream="draft-u")
+    U = uniforms24(9, (B, K + 1))
+    D = np.array([[oacc.sample_truncated(Q[b, i], top_k, top_p, ud[b, i]) for i in range(K)] for b in range(B)])
+    # a draft the target may reject (drawn from another row's support)
+    D[1, 0] = int(np.argmax(P[0, 3]))
+    got = _gpu(vq, P, Q, D, U, top_k=top_k, top_p=top_p)
+    ref = _oracle(P, Q, D, U, top_k, top_p)
+    assert np.array_equal(got[1], ref[1]) and np.array_equal(got[0], ref[0]), (got, ref)
