@@ -715,11 +715,45 @@ __device__ T wg_sum(T v, T* lds /* blockDim/64 entries */) {
   return t;
 }
 
+// A thread's run of consecutive elements in one histogram bin, added to the
+// workgroup's LDS histogram in one atomic per run: rows whose keys crowd one
+// bin (e.g. every zero probability) would otherwise serialise 64 lanes on one
+// LDS address for every element.
+struct BinRun {
+  int bin = -1;
+  uint32_t cnt = 0;
+  u64 mass = 0;
+  __device__ __forceinline__ void flush(uint32_t* c, u64* m) {
+    if (cnt) {
+      atomicAdd(&c[bin], cnt);
+      if (mass) atomicAdd(&m[bin], mass);
+    }
+    cnt = 0;
+    mass = 0;
+  }
+  __device__ __forceinline__ void add(int b, u64 w, uint32_t* c, u64* m) {
+    if (b != bin) {
+      flush(c, m);
+      bin = b;
+    }
+    ++cnt;
+    mass += w;
+  }
+};
+
 __global__ __launch_bounds__(kCT) void rows_stats_kernel(const float* __restrict__ p, const float* __restrict__ q,
                                                          int64_t ps, int64_t qs, int K, int V, int C, float t_scale,
-                                                         float2* __restrict__ stats) {
+                                                         float2* __restrict__ stats, RowState* __restrict__ st,
+                                                         uint32_t* __restrict__ hcnt, u64* __restrict__ hmass) {
   __shared__ float red[kCT / 64];
   const int c = blockIdx.x % C, r = blockIdx.x / C;
+  // The clear of the row's level-0 histogram and select state, shared by the
+  // row's C workgroups (the histogram kernel that follows adds into them).
+  for (int b = c * kCT + threadIdx.x; b < kBins; b += C * kCT) {
+    hcnt[(int64_t)r * kBins + b] = 0u;
+    hmass[(int64_t)r * kBins + b] = 0ull;
+  }
+  if (c == 0 && threadIdx.x == 0) st[r] = RowState{};
   const float* src = row_ptr(p, q, ps, qs, K, V, r);
   const int x0 = c * kChunk, x1 = min(V, x0 + kChunk);
   float mx = -INFINITY, sm = 0.f;
@@ -777,6 +811,7 @@ __global__ __launch_bounds__(kCT) void rows_hist_kernel(
   __syncthreads();
   u64 msum = 0;
   int bad = 0;
+  BinRun run;
   auto visit = [&](int x, float pv) {
     if (!prob_ok(pv)) {
       bad = 1;
@@ -784,11 +819,7 @@ __global__ __launch_bounds__(kCT) void rows_hist_kernel(
     }
     const u64 m = mass_of(pv);
     msum += m;
-    if (use_hist) {
-      const int bin = (int)(key_of(pv, x, V) >> kTopShift);
-      atomicAdd(&cnt[bin], 1u);
-      if (m) atomicAdd(&mas[bin], m);
-    }
+    if (use_hist) run.add((int)(key_of(pv, x, V) >> kTopShift), m, cnt, mas);
   };
   if (input_kind == 1) {
     for_range(src, x0, x1, [&](int x, float v) {
@@ -799,6 +830,7 @@ __global__ __launch_bounds__(kCT) void rows_hist_kernel(
   } else {
     for_range(src, x0, x1, visit);
   }
+  if (use_hist) run.flush(cnt, mas);
   if (bad) s_bad = 1;
   const u64 tot = wg_sum<u64>(msum, red64);  // barriers inside
   if (tid == 0) {
@@ -940,14 +972,13 @@ __global__ __launch_bounds__(kCT) void rows_refine_hist_kernel(
     mas[b] = 0ull;
   }
   __syncthreads();
+  BinRun run;
   for_range(row, x0, x1, [&](int x, float v) {
     const u64 key = key_of(v, x, V);
     if ((key >> shift) != prefix) return;
-    const int bin = (int)((key >> sub) & (u64)(kBins - 1));
-    atomicAdd(&cnt[bin], 1u);
-    const u64 m = mass_of(v);
-    if (m) atomicAdd(&mas[bin], m);
+    run.add((int)((key >> sub) & (u64)(kBins - 1)), mass_of(v), cnt, mas);
   });
+  run.flush(cnt, mas);
   __syncthreads();
   uint32_t* hc = hcnt + (int64_t)level * lvl_stride + (int64_t)r * kBins;
   u64* hm = hmass + (int64_t)level * lvl_stride + (int64_t)r * kBins;
@@ -1005,32 +1036,38 @@ __global__ __launch_bounds__(kCT) void rows_compact_kernel(const float* __restri
                                                            int input_kind, int64_t ps, int64_t qs, int K, int V,
                                                            int C, const float* __restrict__ probs,
                                                            RowState* __restrict__ st, u64* __restrict__ cand) {
-  __shared__ uint32_t n_lds, w_lds, base;
+  __shared__ u64 keys[kChunk];
+  __shared__ uint32_t n_lds, base;
   const int c = blockIdx.x % C, r = blockIdx.x / C;
   if (!st[r].pending) return;
   const u64 prefix = st[r].prefix;
   const int shift = st[r].shift;
   const float* row = input_kind == 1 ? probs + (int64_t)r * V : row_ptr(p, q, ps, qs, K, V, r);
   const int x0 = c * kChunk, x1 = min(V, x0 + kChunk);
-  if (threadIdx.x == 0) {
-    n_lds = 0u;
-    w_lds = 0u;
-  }
+  if (threadIdx.x == 0) n_lds = 0u;
   __syncthreads();
-  // Count this chunk's keys of the bin, reserve their slots, then write them.
-  uint32_t mine = 0;
-  for_range(row, x0, x1, [&](int x, float v) { mine += (key_of(v, x, V) >> shift) == prefix; });
-  if (mine) atomicAdd(&n_lds, mine);
+  // The chunk's keys of the region, staged in LDS: one LDS atomic per wave and
+  // element position (ballot of the matching lanes), then one reservation in
+  // the row's gather buffer and a coalesced copy.
+  const uint32_t lane = threadIdx.x & 63;
+  for_range(row, x0, x1, [&](int x, float v) {
+    const u64 key = key_of(v, x, V);
+    const bool hit = (key >> shift) == prefix;
+    const u64 m = __ballot(hit);
+    if (!m) return;
+    const int lead = __ffsll((long long)m) - 1;
+    uint32_t off = 0;
+    if ((int)lane == lead) off = atomicAdd(&n_lds, (uint32_t)__popcll(m));
+    off = __shfl(off, lead);
+    if (hit) keys[off + __popcll(m & ((1ull << lane) - 1ull))] = key;
+  });
   __syncthreads();
   const uint32_t n = n_lds;
   if (n == 0) return;
   if (threadIdx.x == 0) base = atomicAdd(&st[r].cand_n, n);
   __syncthreads();
   u64* dst = cand + (int64_t)r * kCandCap + base;
-  for_range(row, x0, x1, [&](int x, float v) {
-    const u64 key = key_of(v, x, V);
-    if ((key >> shift) == prefix) dst[atomicAdd(&w_lds, 1u)] = key;
-  });
+  for (uint32_t i = threadIdx.x; i < n; i += kCT) dst[i] = keys[i];
 }
 
 __device__ __forceinline__ float key_value(u64 key) { return __uint_as_float((uint32_t)(key >> 20)); }
@@ -1553,11 +1590,12 @@ hipError_t accept_launch(const AcceptPlan& plan, const float* p, const float* q,
   hipError_t e;
   if (plan.chunked) {
     const unsigned cg = (unsigned)(C * R);
-    hipLaunchKernelGGL(rows_clear_kernel, dim3((unsigned)R), dim3(256), 0, stream, st, hcnt, hmass);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (input_kind == 1) {
+    if (input_kind == 1) {  // the statistics pass also clears the rows' state and level-0 histograms
       hipLaunchKernelGGL(rows_stats_kernel, dim3(cg), dim3(kCT), 0, stream, p, q, p_stride, q_stride, K, V, C,
-                         t_scale, stats);
+                         t_scale, stats, st, hcnt, hmass);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL(rows_clear_kernel, dim3((unsigned)R), dim3(256), 0, stream, st, hcnt, hmass);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(rows_hist_kernel, dim3(cg), dim3(kCT), 0, stream, p, q, input_kind, p_stride, q_stride, K, V,
