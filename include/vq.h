@@ -113,6 +113,30 @@ int vq_skinny_qmm(const void* x, int64_t ldx,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * vq_skinny_qmm for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The same product, arguments and result as vq_skinny_qmm (bit-identical), with
+ * no workspace argument: the split-K partials and completion counters live in a
+ * device array of VQ_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on
+ * every GPU it runs on, from its load until the process ends. The call neither
+ * allocates nor frees memory; it clears the counters itself (a small kernel on
+ * `stream`, so it can be captured).
+ * Limits: a shape whose vq_skinny_qmm_workspace() exceeds 16 MiB is rejected
+ * with VQ_ERR_INVALID_ARG (every projection of a 27B-shaped layer fits up to
+ * M = 16; a 248320-wide output fits up to M = 3).
+ * Concurrency: all calls on one GPU share that GPU's array, so calls that may
+ * overlap on one GPU (different streams, or host threads) race and must be
+ * serialised by the caller; calls in order on one stream are safe.
+ * ---------------------------------------------------------------------- */
+#define VQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int vq_skinny_qmm_noalloc(const void* x, int64_t ldx,
+                          const void* wq, const void* scales, const void* biases,
+                          int bits, int group_size, int M, int N, int K,
+                          void* y, int64_t ldy, int y_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Skinny quantized matmul on a prepacked weight, with fused glue
  *
  * The same product as vq_skinny_qmm on a layout made once per weight by

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "vq.h"
 #include "vq_glue.h"
@@ -108,27 +109,31 @@ size_t vq_skinny_qmm_workspace(int bits, int group_size, int M, int N, int K) {
   return p.counter_bytes + p.partial_bytes;
 }
 
-int vq_skinny_qmm(const void* x, int64_t ldx, const void* wq, const void* scales, const void* biases, int bits,
-                  int group_size, int M, int N, int K, void* y, int64_t ldy, int y_dtype, void* workspace,
-                  size_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
-  if (!x || !wq || !scales || !biases || !y) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: NULL data pointer");
-  if (bits != 4 && bits != 8) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: bits must be 4 or 8 (got %d)", bits);
-  if (group_size != 64) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: group_size must be 64 (got %d)", group_size);
-  if (M < 1 || M > VQ_MAX_ROWS) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: M must be in [1, 16] (got %d)", M);
+}  // extern "C"
+
+namespace {
+
+// The argument checks of the row-major skinny QMM (fn names the entry point).
+int qmm_rowmajor_args(const char* fn, const void* x, int64_t ldx, const void* wq, const void* scales,
+                      const void* biases, int bits, int group_size, int M, int N, int K, const void* y, int64_t ldy,
+                      int y_dtype) {
+  if (!x || !wq || !scales || !biases || !y) return fail(VQ_ERR_INVALID_ARG, "%s: NULL data pointer", fn);
+  if (bits != 4 && bits != 8) return fail(VQ_ERR_INVALID_ARG, "%s: bits must be 4 or 8 (got %d)", fn, bits);
+  if (group_size != 64) return fail(VQ_ERR_INVALID_ARG, "%s: group_size must be 64 (got %d)", fn, group_size);
+  if (M < 1 || M > VQ_MAX_ROWS) return fail(VQ_ERR_INVALID_ARG, "%s: M must be in [1, 16] (got %d)", fn, M);
   if (!qmm_shape_ok(bits, group_size, M, N, K))
-    return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: unsupported shape N=%d K=%d (K a positive multiple of 64)", N, K);
-  if (ldx < K || ldx % 8 != 0) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: ldx must be >= K and a multiple of 8");
-  if (ldy < N) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: ldy must be >= N");
-  if (y_dtype != VQ_BF16 && y_dtype != VQ_F32) return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: bad y_dtype %d", y_dtype);
-  if (!aligned(x, 16) || !aligned(wq, 16))
-    return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: x and wq must be 16-byte aligned");
+    return fail(VQ_ERR_INVALID_ARG, "%s: unsupported shape N=%d K=%d (K a positive multiple of 64)", fn, N, K);
+  if (ldx < K || ldx % 8 != 0) return fail(VQ_ERR_INVALID_ARG, "%s: ldx must be >= K and a multiple of 8", fn);
+  if (ldy < N) return fail(VQ_ERR_INVALID_ARG, "%s: ldy must be >= N", fn);
+  if (y_dtype != VQ_BF16 && y_dtype != VQ_F32) return fail(VQ_ERR_INVALID_ARG, "%s: bad y_dtype %d", fn, y_dtype);
+  if (!aligned(x, 16) || !aligned(wq, 16)) return fail(VQ_ERR_INVALID_ARG, "%s: x and wq must be 16-byte aligned", fn);
   if (!aligned(scales, 2) || !aligned(biases, 2) || !aligned(y, y_dtype == VQ_F32 ? 4 : 2))
-    return fail(VQ_ERR_INVALID_ARG, "vq_skinny_qmm: misaligned scales, biases or y");
-  const vq::QmmPlan plan = vq::qmm_plan(bits, M, N, K, false);
-  int rc = check_workspace(workspace, workspace_bytes, plan.counter_bytes + plan.partial_bytes);
-  if (rc) return rc;
-  if ((rc = check_device())) return rc;
+    return fail(VQ_ERR_INVALID_ARG, "%s: misaligned scales, biases or y", fn);
+  return VQ_OK;
+}
+
+vq::QmmCall qmm_rowmajor_call(const void* x, int64_t ldx, const void* wq, const void* scales, const void* biases,
+                              int bits, int M, int N, int K, void* y, int64_t ldy, int y_dtype, void* workspace) {
   vq::QmmCall c{};
   c.x = x;
   c.ldx = ldx;
@@ -145,8 +150,97 @@ int vq_skinny_qmm(const void* x, int64_t ldx, const void* wq, const void* scales
   c.ldy = ldy;
   c.y_f32 = y_dtype == VQ_F32;
   c.workspace = workspace;
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vq_skinny_qmm(const void* x, int64_t ldx, const void* wq, const void* scales, const void* biases, int bits,
+                  int group_size, int M, int N, int K, void* y, int64_t ldy, int y_dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc = qmm_rowmajor_args("vq_skinny_qmm", x, ldx, wq, scales, biases, bits, group_size, M, N, K, y, ldy, y_dtype);
+  if (rc) return rc;
+  const vq::QmmPlan plan = vq::qmm_plan(bits, M, N, K, false);
+  if ((rc = check_workspace(workspace, workspace_bytes, plan.counter_bytes + plan.partial_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  const vq::QmmCall c = qmm_rowmajor_call(x, ldx, wq, scales, biases, bits, M, N, K, y, ldy, y_dtype, workspace);
   hipError_t e = vq::qmm_launch(plan, c, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_skinny_qmm launch");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- the entry point without allocation
+// The library's own scratch for vq_skinny_qmm_noalloc: one copy per GPU, held
+// from the library's load until the process ends. In host code `scratch` only
+// names the symbol; its device address on the current GPU is looked up once
+// per device with hipGetSymbolAddress and used from then on.
+static __device__ __align__(256) unsigned char scratch[VQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each GPU (null until looked up)
+
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(VQ_ERR_UNSUPPORTED_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(VQ_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VQ_OK;
+}
+
+// Zeroes n 32-bit words (a fill kernel rather than a memset node, so that the
+// call can be captured into a graph).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) p[i] = 0u;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vq_skinny_qmm_noalloc(const void* x, int64_t ldx, const void* wq, const void* scales, const void* biases,
+                          int bits, int group_size, int M, int N, int K, void* y, int64_t ldy, int y_dtype,
+                          void* stream) {
+  g_err[0] = 0;
+  int rc = qmm_rowmajor_args("vq_skinny_qmm_noalloc", x, ldx, wq, scales, biases, bits, group_size, M, N, K, y, ldy,
+                             y_dtype);
+  if (rc) return rc;
+  const vq::QmmPlan plan = vq::qmm_plan(bits, M, N, K, false);
+  const size_t need = plan.counter_bytes + plan.partial_bytes;
+  if (need > VQ_NOALLOC_SCRATCH_BYTES)
+    return fail(VQ_ERR_INVALID_ARG,
+                "vq_skinny_qmm_noalloc: M=%d N=%d K=%d needs %zu bytes of scratch, more than the library's %zu "
+                "(use vq_skinny_qmm with a workspace)", M, N, K, need, (size_t)VQ_NOALLOC_SCRATCH_BYTES);
+  if ((rc = check_device())) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws))) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (plan.counter_bytes) {
+    // The completion counters start at zero on every call, whatever the last
+    // call on this GPU left behind.
+    const uint32_t words = (uint32_t)(plan.counter_bytes / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, s,
+                       reinterpret_cast<uint32_t*>(ws), words);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "vq_skinny_qmm_noalloc clear");
+  }
+  const vq::QmmCall c = qmm_rowmajor_call(x, ldx, wq, scales, biases, bits, M, N, K, y, ldy, y_dtype, ws);
+  hipError_t e = vq::qmm_launch(plan, c, s);
+  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_skinny_qmm_noalloc launch");
 }
 
 size_t vq_qmm_pack_bytes(int bits, int group_size, int N, int K) {

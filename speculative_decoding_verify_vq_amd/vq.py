@@ -39,6 +39,7 @@ _proto("vq_last_error", _c.c_char_p, [])
 _proto("vq_version", _c.c_char_p, [])
 _proto("vq_skinny_qmm_workspace", _SZ, [_I, _I, _I, _I, _I])
 _proto("vq_skinny_qmm", _I, [_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I64, _I, _P, _SZ, _P])
+_proto("vq_skinny_qmm_noalloc", _I, [_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I64, _I, _P])
 _proto("vq_qmm_pack_bytes", _SZ, [_I, _I, _I, _I])
 _proto("vq_qmm_pack", _I, [_P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P])
 _proto("vq_sumsq_parts", _I, [_I])
@@ -161,6 +162,19 @@ def skinny_qmm(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: 
                            group_size, M, N, K, out.data_ptr(), out.stride(0), y_dtype, _ptr(ws), wsz,
                            _stream(stream))
     _check("vq_skinny_qmm", rc)
+    return out
+
+
+def skinny_qmm_noalloc(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, bits: int,
+                       N: int, K: int, out: torch.Tensor, group_size: int = 64, stream=None) -> torch.Tensor:
+    """skinny_qmm into a caller-given ``out`` with the library's own scratch
+    (vq_skinny_qmm_noalloc: no workspace, nothing allocated in the call)."""
+    M = x.shape[0]
+    y_dtype = VQ_F32 if out.dtype == torch.float32 else VQ_BF16
+    rc = lib.vq_skinny_qmm_noalloc(x.data_ptr(), x.stride(0), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                                   bits, group_size, M, N, K, out.data_ptr(), out.stride(0), y_dtype,
+                                   _stream(stream))
+    _check("vq_skinny_qmm_noalloc", rc)
     return out
 
 

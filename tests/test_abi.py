@@ -60,6 +60,38 @@ def test_qmm_rejects(vqmod, bad):
     assert vqmod.last_error()
 
 
+def _qmm_noalloc(vq, **kw):
+    a = dict(x=A16, ldx=1024, wq=A16, s=A16, b=A16, bits=4, gs=64, M=4, N=512, K=1024, y=A16, ldy=512, yd=0,
+             stream=None)
+    a.update(kw)
+    return vq.lib.vq_skinny_qmm_noalloc(a["x"], a["ldx"], a["wq"], a["s"], a["b"], a["bits"], a["gs"], a["M"],
+                                        a["N"], a["K"], a["y"], a["ldy"], a["yd"], a["stream"])
+
+
+@pytest.mark.parametrize("bad", [
+    dict(x=None), dict(wq=None), dict(y=None), dict(bits=3), dict(gs=32), dict(M=0), dict(M=17), dict(N=0),
+    dict(K=96), dict(ldx=1000), dict(ldy=100), dict(yd=7), dict(x=A16 + 8), dict(y=A16 + 1),
+    dict(M=16, N=248320, K=5120, ldx=5120, ldy=248320), dict(M=4, N=248320, K=5120, ldx=5120, ldy=248320),
+])
+def test_qmm_noalloc_rejects(vqmod, bad):
+    """Invalid arguments, and shapes whose scratch exceeds the library's 16 MiB
+    array, are rejected on the host before anything is launched."""
+    assert _qmm_noalloc(vqmod, **bad) == vqmod.VQ_ERR_INVALID_ARG
+    assert vqmod.last_error()
+    if "N" in bad and bad["N"] == 248320:
+        assert "scratch" in vqmod.last_error()
+        assert vqmod.lib.vq_skinny_qmm_workspace(4, 64, bad["M"], bad["N"], bad["K"]) > (16 << 20)
+
+
+def test_qmm_noalloc_limit_covers_layer_projections(vqmod):
+    """Every projection of a 27B-shaped layer (fused q|k|v and gate|up included)
+    fits the no-allocation scratch at every verify width up to 16."""
+    for N, K in ((8192, 5120), (5120, 6144), (34816, 5120), (5120, 17408)):
+        for M in (1, 4, 8, 16):
+            for bits in (4, 8):
+                assert vqmod.lib.vq_skinny_qmm_workspace(bits, 64, M, N, K) <= (16 << 20)
+
+
 def _attn(vq, **kw):
     a = dict(q=A16, qrs=128, k=A16, v=A16, hs=256 * 64, M=4, Hq=2, Hkv=2, D=64, T=256, scale=0.125, out=A16,
              ors=128, ws=A16, wsz=1 << 30)
