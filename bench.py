@@ -1,20 +1,25 @@
 """Verify-step benchmark on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3|4] [--no-cpu-baseline] [--soak SECONDS]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4|3] [--single] [--no-cpu-baseline]
+                    [--soak SECONDS]
 
 A step is one pass of the whole verify path over one batch of synthetic input:
-64 layers of 4-bit (config 3) or 8-bit (config 4) affine group-quantized
-projections of 27B-like shape, multi-row attention over a bf16 KV cache on
-every fourth layer, the float32 lm_head and exact acceptance over the
-vocabulary (logits mode). The step is captured once into a HIP graph and
+64 layers of 8-bit (the long-context pack, the headline) or 4-bit affine
+group-quantized projections of 27B-like shape, multi-row attention over a bf16
+KV cache on every fourth layer, the float32 lm_head and exact acceptance over
+the vocabulary (logits mode). The step is captured once into a HIP graph and
 replayed; inputs are resident in HBM when timing starts.
 
-Printed (one JSON line): verify-step HBM GB/s over the step's algorithmic bytes
-(weights once + K/V once per attention layer + the logit rows), its fraction of
-the 8 TB/s peak, ms per step, cost(M)/cost(M=1) of the 64-layer stack for M = 1..16
-stream, a roofline record of the dominant kernel (the skinny QMM, timed per
-launch with HIP events on its stream) and the CPU oracle timed on a bounded
-sample of the same workload.
+Printed (one JSON line), for the headline step (8-bit, M = 8, KV at 128k):
+verify-step HBM GB/s over the step's algorithmic bytes (weights once + K/V once
+per attention layer + the logit rows), its fraction of the 8 TB/s peak, ms per
+step, cost(M)/cost(M=1) of the 64-layer stack for M = 1..16, a roofline record
+of the dominant kernel (the skinny QMM, timed per launch with HIP events on its
+stream), the acceptance call's µs, and the CPU oracle timed on a bounded sample
+of the same workload. The same record for the 4-bit step (M = 4, KV at 16k) is
+nested under "other_configs" (unless --single), with per-call records of the
+multi-row attention at 8k and 32k context for M = 1..8 and the streaming-read
+ceiling of the HBM.
 """
 from __future__ import annotations
 
@@ -47,12 +52,18 @@ CONFIGS = {
 # The profiled commands whose CSV output --summarize-profiles reads (run from the
 # repository root on one MI355X, output under <out>).
 PROFILE_CMDS = {
-    "kt": "rocprofv3 --kernel-trace --stats -f csv -d <out>/kt -o kt -- python3 bench.py --steps 5 --warmup 1 "
-          "--no-ratio --no-cpu-baseline --no-next > <out>/kt.out",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o fetch -- python3 bench.py --steps 1 --warmup 0 "
-             "--layers 8 --no-ratio --no-cpu-baseline --no-next --copy-calibration",
-    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o write -- python3 bench.py --steps 1 --warmup 0 "
-             "--layers 8 --no-ratio --no-cpu-baseline --no-next --copy-calibration",
+    "kt": "rocprofv3 --kernel-trace --stats -f csv -d <out>/kt -o kt -- python3 bench.py --config {config} --single "
+          "--steps 5 --warmup 1 --no-ratio --no-cpu-baseline --no-next --no-extras > <out>/kt.out",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o fetch -- python3 bench.py --config {config} "
+             "--single --steps 1 --warmup 0 --layers 8 --no-ratio --no-cpu-baseline --no-next --no-extras "
+             "--copy-calibration",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o write -- python3 bench.py --config {config} "
+             "--single --steps 1 --warmup 0 --layers 8 --no-ratio --no-cpu-baseline --no-next --no-extras "
+             "--copy-calibration",
+    "attn_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o fetch -- python3 bench.py --attn-counters "
+                  "--copy-calibration",
+    "attn_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o write -- python3 bench.py --attn-counters "
+                  "--copy-calibration",
     "curve_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o fetch -- python3 bench.py "
                    "--qmm-curve-counters {bits} --copy-calibration",
     "curve_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o write -- python3 bench.py "
@@ -424,13 +435,169 @@ def next_rows(torch, stack, w, single_ms: float) -> dict:
     return res
 
 
+ATTN_HEADS = (24, 4, 256)          # Hq, Hkv, D of the 27B-shaped attention layers
+ATTN_CTXS = (8192, 32768)
+ATTN_MS = (1, 2, 3, 4, 5, 6, 7, 8)
+
+
+def attention_config2(torch) -> dict:
+    """µs per multi-row attention call at the 27B heads (Hq 24, Hkv 4, D 256,
+    scale 1/16) for 8k and 32k committed keys plus M = 1..8 drafted rows causal
+    among themselves: GB/s over the call's algorithmic bytes (K and V once, q in,
+    out) and cost(M)/cost(M=1). Every timing is a graph of calls rotating over
+    distinct caches of at least 2 GiB in total, so the KV comes from HBM (page
+    "Speculative decoding and MTP on Apple silicon", Facts: 8 query rows at 32k
+    context, each KV tile read once rather than once per row)."""
+    from speculative_decoding_verify_vq_amd import vq
+    from synth import bf16_normal_torch
+    dev = torch.device("cuda")
+    Hq, Hkv, D = ATTN_HEADS
+    out = {}
+    for ctx in ATTN_CTXS:
+        Tcap = ctx + max(ATTN_MS)
+        per = 4 * Hkv * Tcap * D
+        n = max(8, -(-(2 << 30) // per))
+        kv = [(bf16_normal_torch((Hkv, Tcap, D), 0.0, 1.0, 5000 + 2 * i, dev),
+               bf16_normal_torch((Hkv, Tcap, D), 0.0, 1.0, 5001 + 2 * i, dev)) for i in range(n)]
+        rec = {}
+        for M in ATTN_MS:
+            T = ctx + M
+            q = bf16_normal_torch((M, Hq, D), 0.0, 1.0, 5900 + M, dev)
+            o = torch.empty_like(q)
+            ws = torch.zeros(vq.attn_workspace_bytes(M, Hq, Hkv, D, T) + 256, dtype=torch.uint8, device=dev)
+            wsv = ws[(-ws.data_ptr()) % 256:]
+            us = _time_calls(torch, [lambda k=k, v=v: vq.multirow_attn(q, k, v, T, 1 / 16, out=o, workspace=wsv)
+                                     for k, v in kv], reps=5)
+            nb = 4 * Hkv * T * D + 4 * M * Hq * D
+            rec[str(M)] = {"us": round(us, 2), "GBs": round(nb / us / 1e3, 1)}
+        base = rec["1"]["us"]
+        for v in rec.values():
+            v["cost_ratio"] = round(v["us"] / base, 4)
+        out[f"{ctx // 1024}k"] = rec
+        del kv
+        torch.cuda.empty_cache()
+    return {"shape": "Hq 24, Hkv 4, D 256, bf16 KV, ctx committed keys + M causal drafted rows", "per_ctx": out}
+
+
+ATTN_COUNTER_CACHES = 4
+
+
+def attn_counter_run(torch) -> None:
+    """For hardware counters: at 32k context, for M = 1..8 in order, one eager
+    multi-row attention call on each of ATTN_COUNTER_CACHES distinct caches
+    (the dispatch order is what the counter summary relies on)."""
+    from speculative_decoding_verify_vq_amd import vq
+    from synth import bf16_normal_torch
+    dev = torch.device("cuda")
+    Hq, Hkv, D = ATTN_HEADS
+    ctx = 32768
+    Tcap = ctx + max(ATTN_MS)
+    kv = [(bf16_normal_torch((Hkv, Tcap, D), 0.0, 1.0, 6000 + 2 * i, dev),
+           bf16_normal_torch((Hkv, Tcap, D), 0.0, 1.0, 6001 + 2 * i, dev)) for i in range(ATTN_COUNTER_CACHES)]
+    ws = torch.zeros(vq.attn_workspace_bytes(max(ATTN_MS), Hq, Hkv, D, ctx + max(ATTN_MS)) + 256,
+                     dtype=torch.uint8, device=dev)
+    wsv = ws[(-ws.data_ptr()) % 256:]
+    torch.cuda.synchronize()
+    for M in ATTN_MS:
+        q = bf16_normal_torch((M, Hq, D), 0.0, 1.0, 6900 + M, dev)
+        o = torch.empty_like(q)
+        torch.cuda.synchronize()
+        for k, v in kv:
+            vq.multirow_attn(q, k, v, ctx + M, 1 / 16, out=o, workspace=wsv)
+        torch.cuda.synchronize()
+    log(f"attention counter run: {len(ATTN_MS)} widths x {ATTN_COUNTER_CACHES} calls at 32k")
+
+
+def summarize_attn_counters(prof_dir: str, out_dir: str, cmd_fetch: str, cmd_write: str) -> None:
+    """HBM bytes per multi-row attention call at 32k context for M = 1..8 from
+    the FETCH_SIZE / WRITE_SIZE passes of attn_counter_run (partial and combine
+    kernels of each call summed), scaled by the 1 GiB copy."""
+    Hq, Hkv, D = ATTN_HEADS
+    ctx = 32768
+    per, scale = {}, {}
+    for ctr, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        rows = [r for r in _read_csv(os.path.join(prof_dir, sub), "_counter_collection.csv")
+                if r["Counter_Name"] == ctr]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        scale[ctr] = (1 << 20) / max(copies)
+        for kname in ("attn_partial_kernel", "attn_combine_kernel"):
+            vals = [float(r["Counter_Value"]) for r in rows if kname in r["Kernel_Name"]]
+            if len(vals) != len(ATTN_MS) * ATTN_COUNTER_CACHES:
+                raise RuntimeError(f"{ctr}: expected {len(ATTN_MS) * ATTN_COUNTER_CACHES} {kname} dispatches, "
+                                   f"found {len(vals)}")
+            for i, M in enumerate(ATTN_MS):
+                v = vals[i * ATTN_COUNTER_CACHES:(i + 1) * ATTN_COUNTER_CACHES]
+                per.setdefault(M, {}).setdefault(ctr, 0.0)
+                per[M][ctr] += sum(v) / len(v)
+    md = ["# HBM traffic of one multi-row attention call at 32k context, M = 1..8", "",
+          f"Hq {Hq}, Hkv {Hkv}, D {D}, bf16 KV, T = 32768 + M. Two counter passes of the same command "
+          f"({ATTN_COUNTER_CACHES} distinct caches, one eager call on each per width, plus a 1 GiB device copy for "
+          "scaling); the partial and combine kernels of a call are summed:", "",
+          f"    {cmd_fetch}", f"    {cmd_write}", "",
+          f"Scaling: fetch counts x {scale['FETCH_SIZE']:.5f}, write counts x {scale['WRITE_SIZE']:.5f} (the copy "
+          "reads and writes 1048576 KiB).", "",
+          "| M | FETCH_SIZE KiB (raw) | WRITE_SIZE KiB (raw) | HBM bytes (scaled) | algorithmic bytes | ratio | "
+          "HBM bytes / HBM bytes at M=1 |", "|---|---|---|---|---|---|---|"]
+    base = None
+    for M in ATTN_MS:
+        f, w = per[M]["FETCH_SIZE"], per[M]["WRITE_SIZE"]
+        hbm = 1024 * (f * scale["FETCH_SIZE"] + w * scale["WRITE_SIZE"])
+        alg = 4 * Hkv * (ctx + M) * D + 4 * M * Hq * D
+        base = base or hbm
+        md.append(f"| {M} | {f:.1f} | {w:.1f} | {int(hbm)} | {alg} | {hbm / alg:.3f} | {hbm / base:.3f} |")
+    md += ["", "Each K/V byte is read once per call whatever M is: the bytes grow only by the queries, the outputs "
+               "and the per-range partial results of the extra rows."]
+    with open(os.path.join(out_dir, "attn_traffic_by_M_32k.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
+def acceptance_us(torch, stack, draft_logits, drafts, uniforms, reps: int = 20) -> float:
+    """µs per acceptance call of the step (logits mode over the step's own lm_head
+    logits and the draft logits, the step's sampler settings), as a graph of one
+    call replayed `reps` times."""
+    from speculative_decoding_verify_vq_amd import vq
+    cfg = stack.cfg
+
+    def call():
+        vq.spec_accept(stack.logits, draft_logits, drafts, uniforms, logits=True, temperature=cfg.temperature,
+                       top_k=cfg.top_k, top_p=cfg.top_p, probs_out=stack.probs, out_tokens=stack.tokens,
+                       out_n=stack.n_acc, workspace=stack._wsv("accept"))
+    g = capture(torch, call)
+    ms = time_graph(torch, g, reps, 2)
+    del g
+    return 1e3 * ms
+
+
+def stream_ceiling(torch, nbytes: int = 1 << 30) -> dict:
+    """The HBM streaming-read ceiling: vq_stream_read over a 1 GiB buffer (4x the
+    256 MB Infinity Cache, so every byte comes from HBM), ordinary and
+    non-temporal 16-byte loads, at several grid sizes; TB/s of the best grid."""
+    from speculative_decoding_verify_vq_amd import vq
+    dev = torch.device("cuda")
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).random_()
+    grids = (1024, 2048, 4096, 8192, 16384, 32768)
+    sink = torch.empty(4 * max(grids), dtype=torch.int32, device=dev)
+    res = {}
+    for nt in (False, True):
+        best = None
+        for wg in grids:
+            ms = 1e-3 * _time_calls(torch, [lambda: vq.stream_read(src, sink, wg, nontemporal=nt)] * 4, reps=5)
+            tbs = nbytes / (ms * 1e-3) / 1e12
+            if best is None or tbs > best[0]:
+                best = (tbs, wg)
+        res["nontemporal" if nt else "ordinary"] = {"TBs": round(best[0], 3), "workgroups": best[1]}
+    del src, sink
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "kernel": "vq_stream_read (include/vq_bench.h)", **res}
+
+
 def qmm_traffic(avg_bytes: float, bits: int, M: int):
     """HBM bytes per QMM launch from the committed counter summary, if it was taken
     on the current kernel source and on this workload's weight width and verify
     rows (else None): FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by what the
     counter reads for a copy of known size."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "qmm_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"qmm_traffic_{bits}bit_M{M}.json")
     src = os.path.join(ROOT, "speculative_decoding_verify_vq_amd", "csrc", "qmm.hip")
     try:
         with open(path) as f:
@@ -443,7 +610,7 @@ def qmm_traffic(avg_bytes: float, bits: int, M: int):
         return None
     return {"bytes_per_launch": rec["hbm_bytes_per_launch"],
             "ratio_to_algorithmic": round(rec["hbm_bytes_per_launch"] / avg_bytes, 3),
-            "source": "profiles/qmm_traffic.json"}
+            "source": f"profiles/qmm_traffic_{bits}bit_M{M}.json"}
 
 
 def copy_calibration(torch, nbytes: int = 1 << 30) -> None:
@@ -555,7 +722,7 @@ def summarize_profiles(prof_dir: str, out_dir: str, cmd_kt: str, cmd_fetch: str,
     if os.path.isdir(os.path.join(prof_dir, "kt")):
         _summarize_trace(prof_dir, out_dir, cmd_kt, config)
     if os.path.isdir(os.path.join(prof_dir, "fetch")) and os.path.isdir(os.path.join(prof_dir, "write")):
-        _summarize_traffic(prof_dir, out_dir, cmd_fetch, cmd_write)
+        _summarize_traffic(prof_dir, out_dir, cmd_fetch, cmd_write, config)
 
 
 def _summarize_trace(prof_dir: str, out_dir: str, cmd_kt: str, config: int = 3) -> None:
@@ -611,10 +778,12 @@ def _summarize_trace(prof_dir: str, out_dir: str, cmd_kt: str, config: int = 3) 
 
 
 
-def _summarize_traffic(prof_dir: str, out_dir: str, cmd_fetch: str, cmd_write: str) -> None:
+def _summarize_traffic(prof_dir: str, out_dir: str, cmd_fetch: str, cmd_write: str, config: int = 3) -> None:
     import hashlib
     from speculative_decoding_verify_vq_amd.stack import StackConfig, qmm_algorithmic_bytes
-    cfg = StackConfig()
+    c = CONFIGS[config]
+    cfg = StackConfig(bits=c["bits"], lm_bits=c["lm_bits"], M=c["M"])
+    tag = f"{cfg.bits}bit_M{cfg.M}"
     sh = cfg.shapes()
     n_step = sum(c for _, _, c in _PROFILE_KINDS)
     per = {}
@@ -647,7 +816,7 @@ def _summarize_traffic(prof_dir: str, out_dir: str, cmd_fetch: str, cmd_write: s
         digest = hashlib.sha256(f.read()).hexdigest()
     rec = {"kernel": "qmm_kernel (tiled pack; q|k|v with RMSNorm, o and down with the residual epilogue, gate|up "
                      "with RMSNorm and SwiGLU, lm_head with RMSNorm)",
-           "workload": "4-bit g64 verify step, M=4 (hidden 5120, MLP 17408, lm_head 248320)",
+           "workload": f"{cfg.bits}-bit g64 verify step, M={cfg.M} (hidden 5120, MLP 17408, lm_head 248320)",
            "bits": cfg.bits, "M": cfg.M,
            "qmm_hip_sha256": digest, "fetch_scale": round(scale["FETCH_SIZE"], 5),
            "write_scale": round(scale["WRITE_SIZE"], 5),
@@ -655,10 +824,10 @@ def _summarize_traffic(prof_dir: str, out_dir: str, cmd_fetch: str, cmd_write: s
            "per_kind": kinds, "step_launch_counts": {k: c for k, _, c in _PROFILE_KINDS},
            "hbm_bytes_per_launch": int(tot_hbm / n_step), "algorithmic_bytes_per_launch": int(tot_alg / n_step),
            "commands": [cmd_fetch, cmd_write]}
-    with open(os.path.join(out_dir, "qmm_traffic.json"), "w") as f:
+    with open(os.path.join(out_dir, f"qmm_traffic_{tag}.json"), "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    md = ["# HBM traffic of the skinny QMM: verify step, 4-bit g64, M=4", "",
+    md = [f"# HBM traffic of the skinny QMM: verify step, {cfg.bits}-bit g64, M={cfg.M}", "",
           "Two counter passes of the same short command (8 layers, one step, plus a 1 GiB device copy for scaling):",
           "", f"    {cmd_fetch}", f"    {cmd_write}", "",
           f"Scaling: the 1 GiB copy (1048576 KiB read and written) reads FETCH_SIZE = "
@@ -679,76 +848,31 @@ def _summarize_traffic(prof_dir: str, out_dir: str, cmd_fetch: str, cmd_write: s
            "workgroup of each column block) and the x slices re-read by every workgroup; the lm_head is not split.",
            "", f"qmm.hip sha256 at the time of the runs: {digest} (bench.py reports the traffic only while the source "
                "matches)."]
-    with open(os.path.join(out_dir, "qmm_traffic_4bit_M4.md"), "w") as f:
+    with open(os.path.join(out_dir, f"qmm_traffic_{tag}.md"), "w") as f:
         f.write("\n".join(md) + "\n")
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, choices=[3, 4])
-    ap.add_argument("--layers", type=int, default=64)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-ratio", action="store_true", help="skip the M=1 / M=8 weight-stream ratio")
-    ap.add_argument("--no-next", action="store_true", help="skip the tree / 8-bit KV / multi-sequence measurements")
-    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
-                    help="write the profiles/ summaries from a profiled run's CSV output (kt/, fetch/, write/ under "
-                         "DIR) and exit; needs no GPU")
-    ap.add_argument("--qmm-curve-counters", type=int, default=0, metavar="BITS",
-                    help="only the launches that the per-width counter summary reads (with --copy-calibration), "
-                         "then exit")
-    ap.add_argument("--summarize-curve-profiles", metavar="DIR", default=None,
-                    help="write profiles/qmm_traffic_by_M_<bits>bit.md from fetch/ and write/ under DIR (no GPU)")
-    ap.add_argument("--soak", type=float, default=0.0, metavar="SECONDS",
-                    help="after the measurements, replay the step back to back for this long and report the "
-                         "per-second median / p99 series (sustained-run check)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="run a 1 GiB device copy first (for scaling hardware byte counters)")
-    args = ap.parse_args()
-    if args.summarize_profiles:
-        kt_cmd = PROFILE_CMDS["kt"]
-        if args.config != 3:
-            kt_cmd = kt_cmd.replace("bench.py ", f"bench.py --config {args.config} ")
-        summarize_profiles(args.summarize_profiles, os.path.join(ROOT, "profiles"), kt_cmd,
-                           PROFILE_CMDS["fetch"], PROFILE_CMDS["write"], args.config)
-        return 0
-    if args.summarize_curve_profiles:
-        b = args.qmm_curve_counters or 4
-        summarize_curve_counters(args.summarize_curve_profiles, os.path.join(ROOT, "profiles"), b,
-                                 PROFILE_CMDS["curve_fetch"].format(bits=b), PROFILE_CMDS["curve_write"].format(bits=b))
-        return 0
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the verify step; runs on more than one GPU are not "
-              "part of this build (see DESIGN.md for how the path would shard).", file=sys.stderr)
-        return 2
-
-    import torch
-    from speculative_decoding_verify_vq_amd import vq
+def run_config(torch, cfg_id: int, args, headline: bool) -> dict:
+    """Builds the stack of one step configuration on the device, times the step
+    and the measurements that go with it; returns the JSON record (the headline
+    adds the next rows, the CPU baseline and the soak)."""
     from speculative_decoding_verify_vq_amd.stack import DenseVerifyStack, StackConfig
     from synth import accept_logits, uniforms24
-
-    c = CONFIGS[args.config]
+    c = CONFIGS[cfg_id]
     cfg = StackConfig(layers=args.layers, bits=c["bits"], lm_bits=c["lm_bits"], M=c["M"], ctx=c["ctx"],
                       temperature=c["temperature"], top_k=c["top_k"], top_p=c["top_p"])
     T_cap = cfg.ctx + 16
-    if args.copy_calibration:
-        copy_calibration(torch)
-    if args.qmm_curve_counters:
-        qmm_curve_counter_run(torch, args.qmm_curve_counters)
-        return 0
-    log(f"config {args.config}: generating weights and KV caches on the device")
-    w = make_weights(cfg, torch, 1000 * args.config, T_cap)
+    log(f"config {cfg_id}: generating weights and KV caches on the device")
+    w = make_weights(cfg, torch, 1000 * cfg_id, T_cap)
     stack = DenseVerifyStack(cfg, w)
     dev = torch.device("cuda")
     M, K, V = cfg.M, cfg.M - 1, cfg.vocab
     h_in = (torch.randn((M, cfg.hidden), generator=torch.Generator(device=dev).manual_seed(5), device=dev)
             .to(torch.bfloat16))
-    pl, ql = accept_logits(args.config, K, V)
+    pl, ql = accept_logits(cfg_id, K, V)
     draft_logits = torch.from_numpy(ql[None]).to(dev)
     drafts = torch.tensor([[int(np.argmax(ql[i])) for i in range(K)]], dtype=torch.int32, device=dev)
-    uniforms = torch.from_numpy(uniforms24(args.config, (1, K + 1))).to(dev)
+    uniforms = torch.from_numpy(uniforms24(cfg_id, (1, K + 1))).to(dev)
 
     log("capturing the verify step")
     g = capture(torch, lambda: stack.step(h_in, draft_logits, drafts, uniforms))
@@ -779,45 +903,33 @@ def main() -> int:
         log(f"{cfg.layers}-layer stack: M=1 {res[1]:.3f} ms, M=8 {res[8]:.3f} ms, ratio {ratio:.3f}; "
             f"{ {m: round(v / res[1], 3) for m, v in res.items()} }")
 
-    curves = None
-    if not args.no_ratio:
-        curves = {f"{b}bit": qmm_cost_curve(torch, b) for b in (4, 8)}
-        log("QMM cost(M)/cost(1) at (M,5120)x(17408,5120)^T: " + "; ".join(
-            f"{k}: " + " ".join(f"{m}:{v['cost_ratio']}" for m, v in c["per_M"].items()) for k, c in curves.items()))
-
     roof = qmm_roofline(torch, stack)
     log(f"QMM per launch: {roof['avg_ms'] * 1e3:.1f} us, {roof['achieved_GBs']:.0f} GB/s; {roof['per_kind']}")
     traffic = qmm_traffic(roof["avg_bytes"], cfg.bits, cfg.M)
+    acc_us = acceptance_us(torch, stack, draft_logits, drafts, uniforms)
+    log(f"acceptance: {acc_us:.1f} us per call")
 
-    nxt = None
-    if not args.no_next:
-        log("measuring tree-mask attention, 8-bit KV attention and a 4-sequence step")
+    nxt = cpu = soak_rec = None
+    if headline and not args.no_next:
+        log("measuring tree-mask attention, 8-bit KV attention and a multi-sequence step")
         nxt = next_rows(torch, stack, w, ms)
         log(f"next rows: {nxt}")
-
-    cpu = None
-    if not args.no_cpu_baseline:
+    if headline and not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(args.config, cfg, nbytes["total"])
-
-    soak_rec = None
-    if args.soak > 0:
+        cpu = cpu_baseline(cfg_id, cfg, nbytes["total"])
+    if headline and args.soak > 0:
         log(f"soak: replaying the step for {args.soak:.0f} s")
         soak_rec = soak(torch, g, args.soak, nbytes["total"])
         log(f"soak: median {soak_rec['median_ms_first']} -> {soak_rec['median_ms_last']} ms, "
             f"drift {soak_rec['drift_pct']}%, p99 max {soak_rec['p99_ms_max']} ms")
-
-    out = {
-        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "step_ms_percentiles": dist,
-        "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+    rec = {
+        "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(ms, 4), "step_ms_percentiles": dist,
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "config": {"workload": c["workload"], "layers": cfg.layers, "M": M, "ctx": cfg.ctx, "bits": cfg.bits,
                    "vocab": V, "bytes_per_step": nbytes},
-        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "cost_ratio_m8_m1": None if ratio is None else round(ratio, 4),
         "cost_curve": curve,
-        "qmm_cost_curve": curves,
+        "acceptance_us": round(acc_us, 2),
         "roofline": {"bound": "hbm", "achieved": round(roof["achieved_GBs"], 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(roof["achieved_GBs"] / PEAK_HBM_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
@@ -827,9 +939,112 @@ def main() -> int:
                      "per_kind": roof["per_kind"],
                      "timing": "HIP events around replays of graphs holding the step's QMM launches, "
                                "per projection kind, weighted by the step's launch counts"},
-        "cpu_baseline": cpu,
-        "next_rows": nxt,
-        "soak": soak_rec,
+    }
+    if headline:
+        rec.update({"cpu_baseline": cpu, "next_rows": nxt, "soak": soak_rec})
+    del g, stack, w
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, choices=[3, 4],
+                    help="the headline step configuration (default 4: 8-bit, M=8, KV at 128k)")
+    ap.add_argument("--single", action="store_true", help="measure the headline configuration only")
+    ap.add_argument("--layers", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ratio", action="store_true", help="skip the cost(M)/cost(1) curves")
+    ap.add_argument("--no-next", action="store_true", help="skip the tree / 8-bit KV / multi-sequence measurements")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the per-call attention records and the streaming-read ceiling")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="write the profiles/ summaries of the --config step from a profiled run's CSV output (kt/, "
+                         "fetch/, write/ under DIR) and exit; needs no GPU")
+    ap.add_argument("--qmm-curve-counters", type=int, default=0, metavar="BITS",
+                    help="only the launches that the per-width counter summary reads (with --copy-calibration), "
+                         "then exit")
+    ap.add_argument("--summarize-curve-profiles", metavar="DIR", default=None,
+                    help="write profiles/qmm_traffic_by_M_<bits>bit.md from fetch/ and write/ under DIR (no GPU)")
+    ap.add_argument("--attn-counters", action="store_true",
+                    help="only the attention calls that the 32k counter summary reads (with --copy-calibration)")
+    ap.add_argument("--summarize-attn-profiles", metavar="DIR", default=None,
+                    help="write profiles/attn_traffic_by_M_32k.md from fetch/ and write/ under DIR (no GPU)")
+    ap.add_argument("--soak", type=float, default=0.0, metavar="SECONDS",
+                    help="after the measurements, replay the step back to back for this long and report the "
+                         "per-second median / p99 series (sustained-run check)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device copy first (for scaling hardware byte counters)")
+    args = ap.parse_args()
+    if args.summarize_profiles:
+        fmt = {"config": args.config}
+        summarize_profiles(args.summarize_profiles, os.path.join(ROOT, "profiles"), PROFILE_CMDS["kt"].format(**fmt),
+                           PROFILE_CMDS["fetch"].format(**fmt), PROFILE_CMDS["write"].format(**fmt), args.config)
+        return 0
+    if args.summarize_curve_profiles:
+        b = args.qmm_curve_counters or 4
+        summarize_curve_counters(args.summarize_curve_profiles, os.path.join(ROOT, "profiles"), b,
+                                 PROFILE_CMDS["curve_fetch"].format(bits=b), PROFILE_CMDS["curve_write"].format(bits=b))
+        return 0
+    if args.summarize_attn_profiles:
+        summarize_attn_counters(args.summarize_attn_profiles, os.path.join(ROOT, "profiles"),
+                                PROFILE_CMDS["attn_fetch"], PROFILE_CMDS["attn_write"])
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the verify step; runs on more than one GPU are not "
+              "part of this build (see DESIGN.md for how the path would shard).", file=sys.stderr)
+        return 2
+
+    import torch
+    from speculative_decoding_verify_vq_amd import vq  # noqa: F401  (fails loudly without the HIP library)
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+    if args.qmm_curve_counters:
+        qmm_curve_counter_run(torch, args.qmm_curve_counters)
+        return 0
+    if args.attn_counters:
+        attn_counter_run(torch)
+        return 0
+
+    head = run_config(torch, args.config, args, headline=True)
+    others = {}
+    if not args.single:
+        other = 3 if args.config == 4 else 4
+        others[str(other)] = run_config(torch, other, args, headline=False)
+
+    curves = attn = ceiling = None
+    if not args.no_ratio:
+        curves = {f"{b}bit": qmm_cost_curve(torch, b) for b in (4, 8)}
+        log("QMM cost(M)/cost(1) at (M,5120)x(17408,5120)^T: " + "; ".join(
+            f"{k}: " + " ".join(f"{m}:{v['cost_ratio']}" for m, v in c["per_M"].items()) for k, c in curves.items()))
+    if not args.no_extras:
+        attn = attention_config2(torch)
+        log(f"attention per call: {attn}")
+        ceiling = stream_ceiling(torch)
+        log(f"streaming-read ceiling: {ceiling}")
+
+    out = {
+        "metric": METRIC, "value": head["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "step_ms_percentiles": head["step_ms_percentiles"],
+        "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": head["config"],
+        "pct_of_peak": head["pct_of_peak"],
+        "cost_ratio_m8_m1": head["cost_ratio_m8_m1"],
+        "cost_curve": head["cost_curve"],
+        "acceptance_us": head["acceptance_us"],
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
+        "other_configs": others,
+        "qmm_cost_curve": curves,
+        "attention_per_call": attn,
+        "stream_ceiling": ceiling,
+        "next_rows": head["next_rows"],
+        "soak": head["soak"],
     }
     print(json.dumps(out), flush=True)
     return 0

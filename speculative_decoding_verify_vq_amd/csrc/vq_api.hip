@@ -10,6 +10,7 @@
 #include <mutex>
 
 #include "vq.h"
+#include "vq_bench.h"
 #include "vq_glue.h"
 #include "vq_internal.h"
 
@@ -619,6 +620,22 @@ int vq_kv_append_bf16(const void* src, int64_t ld_src, int k_off, int v_off, voi
   hipError_t e = vq::glue_kv_append(src, ld_src, k_off, v_off, k_cache, v_cache, kv_head_stride, M, Hkv, D, pos,
                                     reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_kv_append_bf16 launch");
+}
+
+// ------------------------------------------------------ streaming-read ceiling
+int vq_stream_read(const void* src, size_t bytes, int nontemporal, int workgroups, uint32_t* sink, void* stream) {
+  g_err[0] = 0;
+  if (!src || !sink) return fail(VQ_ERR_INVALID_ARG, "vq_stream_read: NULL pointer");
+  if (bytes == 0 || bytes % 16 != 0) return fail(VQ_ERR_INVALID_ARG, "vq_stream_read: bytes must be a positive multiple of 16");
+  if (!aligned(src, 16) || !aligned(sink, 4)) return fail(VQ_ERR_INVALID_ARG, "vq_stream_read: misaligned src or sink");
+  if (nontemporal != 0 && nontemporal != 1) return fail(VQ_ERR_INVALID_ARG, "vq_stream_read: nontemporal must be 0 or 1");
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(VQ_ERR_INVALID_ARG, "vq_stream_read: workgroups must be in [1, 2^20] (got %d)", workgroups);
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = vq::stream_read_launch(src, bytes, nontemporal == 1, workgroups, sink,
+                                        reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VQ_OK : hip_fail(e, "vq_stream_read launch");
 }
 
 }  // extern "C"

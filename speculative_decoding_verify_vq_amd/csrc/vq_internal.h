@@ -128,4 +128,9 @@ hipError_t glue_silu_mul(const void* gu, int64_t ldgu, void* y, int64_t ldy, int
 hipError_t glue_kv_append(const void* src, int64_t ld, int k_off, int v_off, void* kc, void* vc, int64_t hs,
                           int M, int Hkv, int D, int pos, hipStream_t s);
 
+// Streaming-read ceiling (stream.hip): reads `bytes` (a multiple of 16) from src
+// with `workgroups` workgroups; sink receives workgroups * 4 words.
+hipError_t stream_read_launch(const void* src, size_t bytes, bool nontemporal, int workgroups, uint32_t* sink,
+                              hipStream_t stream);
+
 }  // namespace vq

@@ -40,6 +40,7 @@ _proto("vq_version", _c.c_char_p, [])
 _proto("vq_skinny_qmm_workspace", _SZ, [_I, _I, _I, _I, _I])
 _proto("vq_skinny_qmm", _I, [_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I64, _I, _P, _SZ, _P])
 _proto("vq_skinny_qmm_noalloc", _I, [_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I64, _I, _P])
+_proto("vq_stream_read", _I, [_P, _SZ, _I, _I, _P, _P])
 _proto("vq_qmm_pack_bytes", _SZ, [_I, _I, _I, _I])
 _proto("vq_qmm_pack", _I, [_P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P])
 _proto("vq_sumsq_parts", _I, [_I])
@@ -176,6 +177,15 @@ def skinny_qmm_noalloc(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, 
                                    _stream(stream))
     _check("vq_skinny_qmm_noalloc", rc)
     return out
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int, nontemporal: bool = False,
+                stream=None) -> None:
+    """Reads every byte of ``src`` (vq_stream_read in include/vq_bench.h: the
+    streaming-read ceiling); ``sink`` holds at least 4 * workgroups int32."""
+    rc = lib.vq_stream_read(src.data_ptr(), src.numel() * src.element_size(), int(nontemporal), workgroups,
+                            sink.data_ptr(), _stream(stream))
+    _check("vq_stream_read", rc)
 
 
 def qmm_pack_bytes(bits: int, N: int, K: int, group_size: int = 64) -> int:

@@ -55,7 +55,7 @@ def test_summarize_profiles(tmp_path):
     os.makedirs(out)
     _make(prof)
     bench.summarize_profiles(prof, out, "cmd-kt", "cmd-fetch", "cmd-write")
-    rec = json.load(open(os.path.join(out, "qmm_traffic.json")))
+    rec = json.load(open(os.path.join(out, "qmm_traffic_4bit_M4.json")))
     assert abs(rec["fetch_scale"] - 2.0) < 1e-9 and abs(rec["write_scale"] - 1.0) < 1e-9
     cfg = StackConfig()
     sh = cfg.shapes()
@@ -93,3 +93,38 @@ def test_summarize_curve_counters(tmp_path):
     md = open(os.path.join(out, "qmm_traffic_by_M_4bit.md")).read()
     # width 3 (index 2): fetch 1020 KiB x 2 + write 1020 KiB x 1
     assert f"| 3 | 1020.0 | 1020.0 | {1024 * 3 * 1020} |" in md
+
+
+def test_summarize_profiles_config4(tmp_path):
+    """The 8-bit M=8 step: the same summaries under the configuration's tag, with
+    its own algorithmic bytes."""
+    prof, out = str(tmp_path / "prof"), str(tmp_path / "out")
+    os.makedirs(out)
+    _make(prof)
+    bench.summarize_profiles(prof, out, "cmd-kt", "cmd-fetch", "cmd-write", 4)
+    rec = json.load(open(os.path.join(out, "qmm_traffic_8bit_M8.json")))
+    assert rec["bits"] == 8 and rec["M"] == 8
+    cfg = StackConfig(bits=8, lm_bits=8, M=8)
+    assert rec["per_kind"]["o"]["algorithmic_bytes"] == qmm_algorithmic_bytes(8, 5120, 6144, 8, out_bytes=4)
+    assert os.path.exists(os.path.join(out, "qmm_kernel_verify_step_8bit_M8.md"))
+    assert "| down | 64 |" in open(os.path.join(out, "qmm_traffic_8bit_M8.md")).read()
+    assert cfg.M == 8
+
+
+def test_summarize_attn_counters(tmp_path):
+    """Attention counter summary: partial + combine dispatches per call, in width order."""
+    prof, out = str(tmp_path / "prof"), str(tmp_path / "out")
+    os.makedirs(out)
+    part = "void vq::(anonymous namespace)::attn_partial_kernel<256, 2, false>(unsigned short const*)"
+    comb = "void vq::(anonymous namespace)::attn_combine_kernel(float const*)"
+    ctr_h = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    for ctr, sub, copy_val in (("FETCH_SIZE", "fetch", 524288.0), ("WRITE_SIZE", "write", 1048576.0)):
+        rows = [[COPY, 131072, ctr, copy_val]]
+        for i, m in enumerate(bench.ATTN_MS):
+            for _ in range(bench.ATTN_COUNTER_CACHES):
+                rows += [[part, 512 * 256, ctr, 1000.0 + 10 * i], [comb, 96 * 256, ctr, 5.0]]
+        _write(os.path.join(prof, sub, f"{sub}_counter_collection.csv"), ctr_h, rows)
+    bench.summarize_attn_counters(prof, out, "f", "w")
+    md = open(os.path.join(out, "attn_traffic_by_M_32k.md")).read()
+    # width 2 (index 1): fetch (1010 + 5) KiB x 2 + write (1010 + 5) KiB x 1
+    assert f"| 2 | 1015.0 | 1015.0 | {1024 * 3 * 1015} |" in md
