@@ -22,8 +22,9 @@
 // Waves split the query rows into tiles of 32 and, when there are few rows,
 // the head dimension of O across waves (each of those waves recomputes the
 // same S tile, which costs MFMA time the memory-bound kernel has to spare).
-// With several key ranges per head, unnormalised partial O and the (max, sum)
-// statistics go to the workspace and a combine kernel merges them.
+// With several key ranges per head, each range's output normalised by its own
+// sum (bf16) and its (max, sum) statistics (float32) go to the workspace, and a
+// combine kernel merges them.
 //
 // 8-bit KV cache (same page, Facts: KV-quantized caches used together with
 // speculation): codes u8 [Hkv, T_cap, D] and one (bf16 scale, bf16 bias) word
@@ -132,7 +133,7 @@ template <int D, int RT, bool KV8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_partial_kernel(
     const uint16_t* __restrict__ q, int64_t q_rs, const uint16_t* kc, const uint16_t* vc, int64_t kv_head_stride,
     int M_max, int Hq, int Hkv, int T_max, float scale_log2, int keys_per_split, int splits, uint16_t* __restrict__ out,
-    int64_t out_rs, float* __restrict__ part_o, float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
+    int64_t out_rs, uint16_t* __restrict__ part_o, float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, int64_t new_rs, uint16_t* kc_w, uint16_t* vc_w,
     const uint32_t* __restrict__ tree, const uint32_t* __restrict__ ksb, const uint32_t* __restrict__ vsb,
     const AttnBatch bt, int rows_stride) {
@@ -418,15 +419,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
     return;
   }
+  // The range's output normalised by its own sum, o / l (a convex combination
+  // of value rows, so no larger than the largest of them), rounded to bf16;
+  // the combine weighs it by l and the range maximum. A range with no visible
+  // key (l = 0) stores zeros and gets weight 0.
   const size_t prow = (((size_t)split * gridDim.z + b) * Hkv + kvh) * rows_stride + row;
-  float* po = part_o + prow * D;
+  uint16_t* po = part_o + prow * D;
+  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
   for (int t = 0; t < C::DT; ++t) {
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       const int d = dpart * C::DW + t * 32 + 8 * a4 + 4 * kq;
-      *reinterpret_cast<float4*>(po + d) =
-          make_float4(o[t][4 * a4], o[t][4 * a4 + 1], o[t][4 * a4 + 2], o[t][4 * a4 + 3]);
+      uint2 w;
+      w.x = pack_bf16x2(o[t][4 * a4] * inv_l, o[t][4 * a4 + 1] * inv_l);
+      w.y = pack_bf16x2(o[t][4 * a4 + 2] * inv_l, o[t][4 * a4 + 3] * inv_l);
+      *reinterpret_cast<uint2*>(po + d) = w;
     }
   }
   if (dpart == 0 && kq == 0) {
@@ -436,7 +444,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   }
 }
 
-// Merge the per-range partials of one (query row, KV head, 64 head dims).
+// Merge the per-range partials of one (query row, KV head, 64 head dims): with
+// range r's maximum m_r, sum l_r and normalised output o_r / l_r,
+//   out = sum_r exp2(m_r - m) l_r (o_r / l_r) / sum_r exp2(m_r - m) l_r.
 // 256 threads = 16 groups of 16 lanes; lane i of a group owns head dims
 // 4i..4i+3 of the block's 64 and group g sums the ranges g, g+16, ...; the
 // groups' sums are added in LDS in a fixed order (deterministic).
@@ -444,7 +454,7 @@ constexpr int kCombineGroups = 16;
 constexpr int kMaxSplits = 1024;
 
 __global__ __launch_bounds__(256) void attn_combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, int M_max, int Hq, int Hkv, int D,
+    const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml, int M_max, int Hq, int Hkv, int D,
     int splits, uint16_t* __restrict__ out, int64_t out_rs, const AttnBatch bt, int rows_stride, int T_max) {
   __shared__ float w_lds[kMaxSplits];
   __shared__ float red[256 / 64];
@@ -468,12 +478,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   constexpr int kFirst = 8;
   const int grp = tid >> 4;
   const int d = d0 + 4 * (tid & 15);
-  const float* po = part_o + base * D + d;
+  const uint16_t* po = part_o + base * D + d;
+  // Four bf16 partial values (8 bytes) widened to float.
+  auto load4 = [&](int sp) __attribute__((always_inline)) -> float4 {
+    const uint2 w = *reinterpret_cast<const uint2*>(po + sp * s_stride * D);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                       __uint_as_float(w.y & 0xFFFF0000u));
+  };
   float4 v0[kFirst];
 #pragma unroll
   for (int u = 0; u < kFirst; ++u) {
     const int sp = grp + u * kCombineGroups;
-    v0[u] = sp < splits ? *reinterpret_cast<const float4*>(po + sp * s_stride * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    v0[u] = sp < splits ? load4(sp) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   constexpr int kMLPT = kMaxSplits / 256;
   float2 ml[kMLPT];
@@ -483,7 +499,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     ml[k] = sp < splits ? *reinterpret_cast<const float2*>(part_ml + (sp * s_stride + base) * 2)
                         : make_float2(-INFINITY, 0.f);
   }
-  // Range weights exp2(m_s - max) and the merged denominator.
+  // Range weights exp2(m_s - max) * l_s and the merged denominator (their sum).
   float mloc = -INFINITY;
 #pragma unroll
   for (int k = 0; k < kMLPT; ++k) mloc = fmaxf(mloc, ml[k].x);
@@ -496,9 +512,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   for (int k = 0; k < kMLPT; ++k) {
     const int sp = tid + 256 * k;
     if (sp < splits) {
-      const float w = ml[k].x == -INFINITY ? 0.f : exp2f(ml[k].x - mmax);
+      const float w = ml[k].x == -INFINITY ? 0.f : exp2f(ml[k].x - mmax) * ml[k].y;
       w_lds[sp] = w;
-      dloc += w * ml[k].y;
+      dloc += w;
     }
   }
   for (int off = 32; off > 0; off >>= 1) dloc += __shfl_xor(dloc, off);
@@ -523,8 +539,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   for (; s + 3 * kCombineGroups < splits; s += 4 * kCombineGroups) {
     float4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      v[u] = *reinterpret_cast<const float4*>(po + (s + u * kCombineGroups) * s_stride * D);
+    for (int u = 0; u < 4; ++u) v[u] = load4(s + u * kCombineGroups);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float w = w_lds[s + u * kCombineGroups];
@@ -535,7 +550,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     }
   }
   for (; s < splits; s += kCombineGroups) {
-    const float4 v = *reinterpret_cast<const float4*>(po + s * s_stride * D);
+    const float4 v = load4(s);
     const float w = w_lds[s];
     acc.x += w * v.x;
     acc.y += w * v.y;
@@ -582,7 +597,8 @@ AttnPlan attn_plan(int M, int Hq, int Hkv, int D, int T, int B) {
   p.keys_per_split = tiles_per * kTileKeys;
   p.splits = (T + p.keys_per_split - 1) / p.keys_per_split;
   p.partial_bytes =
-      p.splits > 1 ? align_up((size_t)p.splits * B * Hkv * p.rows * (D + 2) * sizeof(float), 256) : 0;
+      p.splits > 1 ? align_up((size_t)p.splits * B * Hkv * p.rows * (D * sizeof(uint16_t) + 2 * sizeof(float)), 256)
+                   : 0;
   return p;
 }
 
@@ -597,9 +613,9 @@ hipError_t attn_launch(const AttnPlan& plan, const void* q, int64_t q_rs, const 
   // With an append the caches are written (rows T-M .. T-1) as well as read.
   auto* kw = k_new ? const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(k)) : nullptr;
   auto* vw = k_new ? const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(v)) : nullptr;
-  float* part_o = reinterpret_cast<float*>(workspace);
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(workspace);
   float* part_ml = plan.splits > 1
-                       ? part_o + (size_t)plan.splits * bt.B * Hkv * plan.rows * D
+                       ? reinterpret_cast<float*>(part_o + (size_t)plan.splits * bt.B * Hkv * plan.rows * D)
                        : nullptr;
   dim3 grid(plan.splits, Hkv, bt.B);
   auto* qp = reinterpret_cast<const uint16_t*>(q);
