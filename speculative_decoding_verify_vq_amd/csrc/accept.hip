@@ -174,8 +174,9 @@ struct SelectLds {
 };
 
 // ------------------------------------------- state of the chunked pipeline
-constexpr int kChunk = 8192;
+constexpr int kChunk = 4096;      // elements per (chunk, row) workgroup (4096 measured fastest of 2048-32768)
 constexpr int kCT = 256;           // threads of the chunk kernels
+constexpr int kStage = 8192;       // keys a compact pass stages in LDS
 constexpr int kCandCap = 16384;    // keys gathered per row (2^14: a level-2 region never holds more)
 constexpr int kTopShift = 38;      // level 0: the histogram bin of a key is key >> 38 (12 bits)
 constexpr int kLevels = 3;         // histogram levels: shifts 38, 26, 14 (12 bits each)
@@ -1036,7 +1037,7 @@ __global__ __launch_bounds__(kCT) void rows_compact_kernel(const float* __restri
                                                            int input_kind, int64_t ps, int64_t qs, int K, int V,
                                                            int C, const float* __restrict__ probs,
                                                            RowState* __restrict__ st, u64* __restrict__ cand) {
-  __shared__ u64 keys[kChunk];
+  __shared__ u64 keys[kStage];
   __shared__ uint32_t n_lds, base;
   const int c = blockIdx.x % C, r = blockIdx.x / C;
   if (!st[r].pending) return;
@@ -1044,30 +1045,34 @@ __global__ __launch_bounds__(kCT) void rows_compact_kernel(const float* __restri
   const int shift = st[r].shift;
   const float* row = input_kind == 1 ? probs + (int64_t)r * V : row_ptr(p, q, ps, qs, K, V, r);
   const int x0 = c * kChunk, x1 = min(V, x0 + kChunk);
-  if (threadIdx.x == 0) n_lds = 0u;
-  __syncthreads();
-  // The chunk's keys of the region, staged in LDS: one LDS atomic per wave and
-  // element position (ballot of the matching lanes), then one reservation in
-  // the row's gather buffer and a coalesced copy.
+  // The chunk's keys of the region, kStage elements at a time, staged in LDS:
+  // one LDS atomic per wave and element position (ballot of the matching
+  // lanes), then one reservation in the row's gather buffer and a coalesced copy.
   const uint32_t lane = threadIdx.x & 63;
-  for_range(row, x0, x1, [&](int x, float v) {
-    const u64 key = key_of(v, x, V);
-    const bool hit = (key >> shift) == prefix;
-    const u64 m = __ballot(hit);
-    if (!m) return;
-    const int lead = __ffsll((long long)m) - 1;
-    uint32_t off = 0;
-    if ((int)lane == lead) off = atomicAdd(&n_lds, (uint32_t)__popcll(m));
-    off = __shfl(off, lead);
-    if (hit) keys[off + __popcll(m & ((1ull << lane) - 1ull))] = key;
-  });
-  __syncthreads();
-  const uint32_t n = n_lds;
-  if (n == 0) return;
-  if (threadIdx.x == 0) base = atomicAdd(&st[r].cand_n, n);
-  __syncthreads();
-  u64* dst = cand + (int64_t)r * kCandCap + base;
-  for (uint32_t i = threadIdx.x; i < n; i += kCT) dst[i] = keys[i];
+  for (int s0 = x0; s0 < x1; s0 += kStage) {
+    if (threadIdx.x == 0) n_lds = 0u;
+    __syncthreads();
+    for_range(row, s0, min(x1, s0 + kStage), [&](int x, float v) {
+      const u64 key = key_of(v, x, V);
+      const bool hit = (key >> shift) == prefix;
+      const u64 m = __ballot(hit);
+      if (!m) return;
+      const int lead = __ffsll((long long)m) - 1;
+      uint32_t off = 0;
+      if ((int)lane == lead) off = atomicAdd(&n_lds, (uint32_t)__popcll(m));
+      off = __shfl(off, lead);
+      if (hit) keys[off + __popcll(m & ((1ull << lane) - 1ull))] = key;
+    });
+    __syncthreads();
+    const uint32_t n = n_lds;
+    if (n) {
+      if (threadIdx.x == 0) base = atomicAdd(&st[r].cand_n, n);
+      __syncthreads();
+      u64* dst = cand + (int64_t)r * kCandCap + base;
+      for (uint32_t i = threadIdx.x; i < n; i += kCT) dst[i] = keys[i];
+    }
+    __syncthreads();  // keys and n_lds are reused by the next pass
+  }
 }
 
 __device__ __forceinline__ float key_value(u64 key) { return __uint_as_float((uint32_t)(key >> 20)); }
@@ -1343,7 +1348,7 @@ __global__ __launch_bounds__(kRowThreads) void draw_pick_kernel(
   const float* Q = probs_q + (int64_t)b * qq_stride;
   const int32_t* dr = draft + (int64_t)b * K;
   const float* us = uniforms + (int64_t)b * (K + 1);
-  // Every chunk's two sums go out with the accept tests (V <= 2^20, so C <= 128
+  // Every chunk's two sums go out with the accept tests (V <= 2^20, so C <= 256
   // chunks, one per thread).
   u128 w0 = 0, w1 = 0;
   if (tid < C) {
