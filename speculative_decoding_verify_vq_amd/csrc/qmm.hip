@@ -72,7 +72,6 @@ constexpr int kTileN = 32;                // columns per wave
 constexpr int kColsWG = kWaves * kTileN;  // columns per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kCG = 16;                   // groups per LDS chunk of x
-constexpr int kXUnits = kCG * 8 + 1;      // 16-byte units per LDS row of x (+1 pad)
 constexpr int kRowBytes = 128;            // bytes per row per pipeline block
 constexpr int kLoads = 32 * kRowBytes / (64 * 16);  // dwordx4 per lane per block (= 4)
 constexpr size_t kCounterBytes = 32768;   // completion counters (split-K only)
@@ -179,9 +178,11 @@ __device__ __forceinline__ bf16x8 unpack8(uint32_t w0, uint32_t w1) {
 // over all LDS banks.
 __device__ __forceinline__ int tslot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
-// CHUNK: the workgroup's range of groups may exceed one LDS chunk of x (kCG
+// CHUNK: the workgroup's range of groups may exceed one LDS chunk of x (CG
 // groups); the next chunk is then prefetched into registers while the current
-// one is computed. Without it the range is at most kCG groups.
+// one is computed. Without it the range is at most CG groups. CG is kCG, or
+// half of it for 16 rows with CHUNK, so that the prefetch registers are those
+// of 8 rows and the occupancy stays.
 template <int BITS, int MT, int LAYOUT, int EPI, bool NORM, bool CHUNK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void qmm_kernel(const QmmArgs a) {
   constexpr int GB = BlockCfg<BITS>::GB;
@@ -189,9 +190,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   // Accumulator registers that hold rows < MT: with the 32x32 output layout,
   // register r of lane half h holds row 8*(r/4) + 4*h + r%4.
   constexpr int kUseful = MT <= 8 ? 4 : 8;
+  constexpr int CG = (CHUNK && MT == 16) ? kCG / 2 : kCG;  // groups per LDS chunk of x
+  constexpr int XU = CG * 8 + 1;                            // 16-byte units per LDS row of x (+1 pad)
 
-  __shared__ u32x4 xl[MT * kXUnits];
-  __shared__ float xsum[kCG][16];
+  __shared__ u32x4 xl[MT * XU];
+  __shared__ float xsum[CG][16];
   __shared__ u32x4 tl[LAYOUT == kLayoutTiled ? 1 : kWaves][32 * 8];
   __shared__ float red[kWaves][16];
   __shared__ float inv_rms[16];
@@ -308,12 +311,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   // wait counts the compiler derives are exact.
   Regs R[kInFlight];
 
-  // ---- x, staged in chunks of kCG groups in the element order of the unpack,
-  // with per-group sums. Chunk ch covers groups [g0 + ch*kCG, g0 + (ch+1)*kCG)
+  // ---- x, staged in chunks of CG groups in the element order of the unpack,
+  // with per-group sums. Chunk ch covers groups [g0 + ch*CG, g0 + (ch+1)*CG)
   // of this workgroup's range; the next chunk is loaded into registers while the
   // current one is computed, and written to LDS between two barriers.
-  constexpr int kIters = MT * kCG * 8 / kThreads;
-  static_assert(kIters * kThreads == MT * kCG * 8, "staging loop must be uniform");
+  constexpr int kIters = MT * CG * 8 / kThreads;
+  static_assert(kIters * kThreads == MT * CG * 8, "staging loop must be uniform");
   const int gx1 = min(g1, G);  // groups past G exist only as zero padding of the tiled layout
   u32x4 xv[kIters];
   static_assert(!CHUNK || LAYOUT == kLayoutTiled, "chunked ranges are planned for the tiled layout only");
@@ -321,9 +324,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
       const int t = tid + it * kThreads;
-      const int m = t / (kCG * 8);
-      const int c = t % (kCG * 8);
-      const int gg = max(0, min(g0 + ch * kCG + (c >> 3), gx1 - 1));
+      const int m = t / (CG * 8);
+      const int c = t % (CG * 8);
+      const int gg = max(0, min(g0 + ch * CG + (c >> 3), gx1 - 1));
       xv[it] = *reinterpret_cast<const u32x4*>(a.x + (size_t)min(m, M - 1) * a.ldx + (size_t)gg * 64 + (c & 7) * 8);
     }
   };
@@ -331,9 +334,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
       const int t = tid + it * kThreads;
-      const int m = t / (kCG * 8);
-      const int c = t % (kCG * 8);
-      const int gg = g0 + ch * kCG + (c >> 3);
+      const int m = t / (CG * 8);
+      const int c = t % (CG * 8);
+      const int gg = g0 + ch * CG + (c >> 3);
       u32x4 w = (m < M && gg < gx1) ? xv[it] : u32x4{0, 0, 0, 0};
       if constexpr (NORM) {
         if (m < M) {
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
         o[3] = __builtin_amdgcn_perm(w[3], w[1], 0x07060302u);
         w = o;
       }
-      xl[m * kXUnits + c] = w;
+      xl[m * XU + c] = w;
     }
   };
   load_x(0);
@@ -436,7 +439,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int unit = (BITS == 4) ? gx * 8 + half * 4 + i : gx * 8 + (i >> 1) * 4 + half * 2 + (i & 1);
-        av[i] = __builtin_bit_cast(bf16x8, xl[(l32 & (MT - 1)) * kXUnits + unit]);
+        av[i] = __builtin_bit_cast(bf16x8, xl[(l32 & (MT - 1)) * XU + unit]);
       }
       u32x4 wv0, wv1;
       if constexpr (LAYOUT == kLayoutTiled) {
@@ -480,9 +483,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
   };
 
-  constexpr int kBPC = kCG / GB;  // blocks per x chunk
+  constexpr int kBPC = CG / GB;  // blocks per x chunk
   static_assert(kBPC % kInFlight == 0, "the register ring must restart at every chunk");
-  const int nch = CHUNK ? (ng + kCG - 1) / kCG : 1;
+  const int nch = CHUNK ? (ng + CG - 1) / CG : 1;
   for (int ch = 0; ch < nch; ++ch) {
     const bool next_x = CHUNK && ch + 1 < nch;
     if (next_x) load_x(ch + 1);
@@ -818,11 +821,12 @@ QmmPlan qmm_plan(int bits, int M, int N, int K, bool tiled) {
   // output such as the vocabulary projection) K is not split at all: every
   // split writes M x N float32 partial sums, and writes interleaved with the
   // weight stream cost read bandwidth out of proportion to their size. A
-  // workgroup then walks the whole of K in LDS chunks of x (rows <= 8 only: the
-  // prefetch registers of a 16-row chunk would halve occupancy). Otherwise K is
+  // workgroup then walks the whole of K in LDS chunks of x (for 16 rows, chunks
+  // of half as many groups, so that the prefetch registers do not cost
+  // occupancy). Otherwise K is
   // split into ranges of at most one chunk (kCG groups), split boundaries on
   // multiples of 4 groups (the scale/bias vector unit and the tiled block).
-  if (tiled && p.mt <= 8 && p.n_blocks >= kPlanWGs) {
+  if (tiled && p.n_blocks >= kPlanWGs) {
     p.chunked = true;
     p.groups_per_split = G;
     p.splits = 1;
@@ -914,7 +918,7 @@ hipError_t qmm_launch(const QmmPlan& plan, const QmmCall& c, hipStream_t stream)
   } else if (plan.mt == 8) {                                            \
     VQ_EPI_NORM(B, 8)                                                   \
   } else {                                                              \
-    VQ_EPI_NORM_CH(B, 16, false)                                        \
+    VQ_EPI_NORM(B, 16)                                                  \
   }
   if (c.bits == 4) {
     VQ_BITS(4)

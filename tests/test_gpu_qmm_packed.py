@@ -111,7 +111,9 @@ def test_packed_matches_row_major_bits(vq, bits, M, N, K):
 
 
 @pytest.mark.parametrize("bits,M,N,K", [(4, 4, 5120, 6144), (8, 3, 200, 192), (4, 12, 65536, 512),
-                                        (4, 16, 640, 17408)])
+                                        (4, 16, 640, 17408),
+                                        # 512 column blocks: the unsplit chunked path at 4 and 8 rows
+                                        (4, 4, 65536, 512), (8, 8, 65536, 1024)])
 @pytest.mark.parametrize("inplace", [False, True])
 def test_residual_epilogue(vq, bits, M, N, K, inplace):
     w = qmm_weights(14, N, K, bits)
@@ -142,7 +144,9 @@ def test_residual_epilogue(vq, bits, M, N, K, inplace):
 
 
 @pytest.mark.parametrize("bits,M,I,K", [(4, 4, 1024, 1024), (8, 8, 320, 2048), (4, 16, 32768, 512),
-                                        (4, 1, 64, 5120)])
+                                        (4, 1, 64, 5120),
+                                        # 512 column blocks: the unsplit chunked path at 4 and 8 rows
+                                        (4, 4, 32768, 512), (8, 8, 32768, 1024)])
 def test_swiglu_epilogue(vq, bits, M, I, K):
     wg = qmm_weights(16, I, K, bits, layer=0)
     wu = qmm_weights(16, I, K, bits, layer=1)
@@ -205,6 +209,24 @@ def test_residual_then_norm_chain(vq):
     assert_close(y, ref, "residual -> rmsnorm chain")
 
 
+@pytest.mark.parametrize("bits,M", [(4, 4), (8, 8), (4, 16), (8, 13)])
+def test_wide_norm_residual(vq, bits, M):
+    """RMSNorm prologue and residual epilogue together on an output wide enough for
+    the unsplit chunked path (N = 65536: 512 column blocks), against the oracle."""
+    N, K = 65536, 1024
+    w = qmm_weights(17, N, K, bits, layer=M)
+    xb = qmm_activations(17, M, K, extra=M)
+    rb = qmm_activations(18, M, N, extra=M)
+    x = bf16_tensor(xb)
+    ss = vq.row_sumsq(x)
+    a = ostack.to_bf16_bits(ostack.rmsnorm(to_f64(x)))
+    y = to_f64(vq.qmm_packed(x, _pack(vq, w), bits, N, K, x_sumsq=ss, eps=1e-6, epilogue=vq.VQ_EPI_RESIDUAL,
+                             residual=bf16_tensor(rb)))
+    ref = ostack.round_bf16(to_f64(bf16_tensor(rb)) + ostack.round_bf16(
+        oq.skinny_qmm(a, w["wq"], w["scales"], w["biases"], bits, 64, M, N, K)))
+    assert_close(y, ref, f"{bits}-bit M={M} norm + residual")
+
+
 def test_packed_deterministic(vq):
     w = qmm_weights(22, 1024, 8192, 4)
     x = qmm_activations(22, 8, 8192)
@@ -217,7 +239,7 @@ def test_packed_deterministic(vq):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("bits,M", [(4, 4), (8, 8)])
+@pytest.mark.parametrize("bits,M", [(4, 4), (8, 8), (4, 16), (8, 16)])
 def test_step_projections_full_shape_sampled(vq, bits, M):
     """The five projections of the verify step at 27B shapes on the tiled pack, in
     the launch configuration of the step (RMSNorm prologue on q|k|v, gate|up and
