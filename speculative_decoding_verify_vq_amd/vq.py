@@ -14,7 +14,9 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libvq.so")
+# VQ_LIBRARY names another build of the same library (e.g. one with host-side
+# sanitizers); by default the in-tree libvq.so.
+LIB_PATH = os.environ.get("VQ_LIBRARY") or os.path.join(_HERE, "libvq.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m speculative_decoding_verify_vq_amd.build`")
 lib = ctypes.CDLL(LIB_PATH)
