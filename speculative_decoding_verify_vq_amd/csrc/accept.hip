@@ -26,6 +26,7 @@
 //   shared rows    (both batch strides 0, e.g. 10^6 trials of one verify) the
 //                  running sums of every position's residual are tabulated once
 //                  and each trial is one thread: K tests and a binary search.
+#include "vq.h"
 #include "vq_internal.h"
 
 namespace vq {
@@ -773,6 +774,23 @@ __global__ __launch_bounds__(kCT) void rows_stats_kernel(const float* __restrict
   if (threadIdx.x == 0) stats[(int64_t)r * C + c] = make_float2(cmx, csum);
 }
 
+// The softmax normaliser of row r from its chunk statistics: the row's largest
+// scaled logit and 1 / (sum of exp2(a - largest)). Thread i takes chunks i,
+// i + kCT, ..., then a fixed reduction tree, so every workgroup of the row gets
+// the same values.
+__device__ __forceinline__ void row_normaliser(const float2* __restrict__ stats, int r, int C, float* redf,
+                                               float& gmx, float& inv) {
+  float mx = -INFINITY;
+  for (int i = threadIdx.x; i < C; i += kCT) mx = fmaxf(mx, stats[(int64_t)r * C + i].x);
+  gmx = block_reduce_max(mx, redf);
+  float part = 0.f;
+  for (int i = threadIdx.x; i < C; i += kCT) {
+    const float2 s2 = stats[(int64_t)r * C + i];
+    part += (s2.x == -INFINITY) ? 0.f : s2.y * exp2f(s2.x - gmx);
+  }
+  inv = 1.f / block_reduce_sum(part, redf);
+}
+
 __global__ __launch_bounds__(kCT) void rows_hist_kernel(
     const float* __restrict__ p, const float* __restrict__ q, int input_kind, int64_t ps, int64_t qs, int K, int V,
     int C, float t_scale, int use_hist, float* __restrict__ probs, const float2* __restrict__ stats,
@@ -789,20 +807,7 @@ __global__ __launch_bounds__(kCT) void rows_hist_kernel(
   float* dst = probs + (int64_t)r * V;
   if (tid == 0) s_bad = 0;
   float gmx = 0.f, inv = 0.f;
-  if (input_kind == 1) {
-    // The row's max and sum from the chunk statistics (thread i takes chunks i,
-    // i + kCT, ..., then a fixed reduction tree): every workgroup of the row
-    // gets the same values.
-    float mx = -INFINITY;
-    for (int i = tid; i < C; i += kCT) mx = fmaxf(mx, stats[(int64_t)r * C + i].x);
-    gmx = block_reduce_max(mx, redf);
-    float part = 0.f;
-    for (int i = tid; i < C; i += kCT) {
-      const float2 s2 = stats[(int64_t)r * C + i];
-      part += (s2.x == -INFINITY) ? 0.f : s2.y * exp2f(s2.x - gmx);
-    }
-    inv = 1.f / block_reduce_sum(part, redf);
-  }
+  if (input_kind == 1) row_normaliser(stats, r, C, redf, gmx, inv);
   if (use_hist) {
     for (int b = tid; b < kBins; b += kCT) {
       cnt[b] = 0u;
@@ -1241,6 +1246,260 @@ __global__ __launch_bounds__(kRowThreads) void rows_resolve_kernel(int V, int to
   }
 }
 
+// ------------------------------------------- small top-k: per-chunk candidates
+// For top_k <= kTopKMax, the row's top_k keys are among the union of the chunks'
+// own top_k keys: a key that top_k keys of its own chunk outrank is outranked by
+// top_k keys of the row. One workgroup per (chunk, row) selects its chunk's
+// top_k keys into fixed slots of the row's gather buffer; one workgroup per row
+// then selects the row's top_k keys from those slots and runs the top-p walk
+// over them. Two launches replace the histogram levels, the compacts and the
+// resolves, and a crowd of keys that agree in their high bits (every zero
+// probability of a near one-hot row) costs one select level, not three
+// chip-wide passes.
+constexpr int kTopKMax = 64;
+constexpr u64 kNoKey = ~0ull;  // an empty slot: above every 50-bit key, so in no region
+constexpr int kSelJ = 16;      // keys per thread in the selects: 16 * kCT = kChunk, 16 * 1024 = kCandCap
+static_assert(kSelJ * kCT == kChunk && kSelJ * kRowThreads == kCandCap, "select capacities");
+static_assert(kTopKMax <= 64, "the top-p walk over the kept keys takes one lane each");
+static_assert((int64_t)kTopKMax * ((VQ_MAX_VOCAB + kChunk - 1) / kChunk) <= kCandCap,
+              "every chunk's candidates fit one row's gather buffer");
+
+struct TopLds {
+  uint32_t hist[256];
+  u64 r_or[kRowThreads / 64];
+  u64 r_and[kRowThreads / 64];
+  u64 scan[kRowThreads / 64 + 1];
+  int digit;
+  uint32_t excl, cnt;
+};
+
+__device__ __forceinline__ u64 shfl_xor_u64(u64 v, int off) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, off), hi = __shfl_xor((uint32_t)(v >> 32), off);
+  return ((u64)hi << 32) | lo;
+}
+
+__device__ __forceinline__ u64 shfl_u64(u64 v, int src_lane) {
+  const uint32_t lo = __shfl((uint32_t)v, src_lane), hi = __shfl((uint32_t)(v >> 32), src_lane);
+  return ((u64)hi << 32) | lo;
+}
+
+// Among the keys held kSelJ per thread (kNoKey in empty slots), the bound T with
+// exactly `need` keys >= T, for 1 <= need < number of keys. Radix select from the
+// top over the region of keys that share the bits above `shift`: each level
+// first extends the region's prefix over the bits on which all of its keys agree
+// (their bitwise OR and AND), then counts the next (up to) 8 bits, so every
+// level separates at least two keys whatever their high bits are. Keys are
+// distinct, so the walk ends at a digit that holds exactly the keys still needed.
+template <int NT>
+__device__ u64 select_top(const u64 (&key)[kSelJ], uint32_t need, TopLds& s) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  u64 prefix = 0;
+  int shift = 50;
+  // Every level lowers `shift` by at least one, so at most 50 levels run.
+  for (;;) {
+    const u64 low = (1ull << shift) - 1ull;
+    u64 o = 0ull, a = low;
+#pragma unroll
+    for (int j = 0; j < kSelJ; ++j) {
+      if ((key[j] >> shift) == prefix) {
+        o |= key[j] & low;
+        a &= key[j] & low;
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      o |= shfl_xor_u64(o, off);
+      a &= shfl_xor_u64(a, off);
+    }
+    __syncthreads();  // the previous level's readers of s are done
+    if (lane == 0) {
+      s.r_or[wave] = o;
+      s.r_and[wave] = a;
+    }
+    for (int b = tid; b < 256; b += NT) s.hist[b] = 0u;
+    if (tid == 0) {
+      s.digit = 0;
+      s.excl = 0u;
+      s.cnt = need;  // stands only if no digit crosses (never for distinct keys): ends the walk
+    }
+    __syncthreads();
+    o = 0ull;
+    a = low;
+    for (int w = 0; w < NT / 64; ++w) {
+      o |= s.r_or[w];
+      a &= s.r_and[w];
+    }
+    // The region holds more than need >= 1 distinct keys, so they differ
+    // somewhere below `shift` (> 0); the guard only bounds the loop.
+    if ((o ^ a) == 0ull || shift == 0) return prefix << shift;
+    const int h = 63 - __clzll((long long)(o ^ a));
+    prefix = (prefix << (shift - h - 1)) | (a >> (h + 1));
+    shift = h + 1;
+    const int lo = h >= 7 ? h - 7 : 0;
+    const int w = h - lo + 1;
+    const uint32_t dmask = (1u << w) - 1u;
+    // Counts of the digit [h .. lo]: a thread's run of keys in one digit is one
+    // LDS atomic (a crowd that shares a digit would serialise on one address).
+    uint32_t run_d = 0u, run_c = 0u;
+#pragma unroll
+    for (int j = 0; j < kSelJ; ++j) {
+      if ((key[j] >> shift) == prefix) {
+        const uint32_t d = (uint32_t)(key[j] >> lo) & dmask;
+        if (run_c && d != run_d) {
+          atomicAdd(&s.hist[run_d], run_c);
+          run_c = 0u;
+        }
+        run_d = d;
+        ++run_c;
+      }
+    }
+    if (run_c) atomicAdd(&s.hist[run_d], run_c);
+    __syncthreads();
+    // Thread t < 2^w owns digit 2^w - 1 - t (descending).
+    const int nb = 1 << w;
+    const int d = nb - 1 - tid;
+    const uint32_t c = tid < nb ? s.hist[d] : 0u;
+    u64 tot;
+    const u64 excl = block_excl_scan<u64, NT>((u64)c, s.scan, tot);
+    if (tid < nb && excl < need && need <= excl + c) {
+      s.digit = d;
+      s.excl = (uint32_t)excl;
+      s.cnt = c;
+    }
+    __syncthreads();
+    need -= s.excl;
+    prefix = (prefix << w) | (u64)s.digit;
+    shift = lo;
+    if (s.cnt == need) return prefix << shift;
+  }
+}
+
+// Per (chunk, row): the probabilities (logits mode: written to probs), their
+// validity, and the chunk's top min(top_k, length) keys in slots [0, top_k) of
+// cand[row * kCandCap + chunk * top_k] (kNoKey in the rest).
+__global__ __launch_bounds__(kCT) void rows_chunk_topk_kernel(
+    const float* __restrict__ p, const float* __restrict__ q, int input_kind, int64_t ps, int64_t qs, int K, int V,
+    int C, float t_scale, float* __restrict__ probs, const float2* __restrict__ stats, int top_k,
+    u64* __restrict__ cand, uint32_t* __restrict__ badf) {
+  __shared__ u64 keys[kChunk];
+  __shared__ TopLds s;
+  __shared__ float redf[kCT / 64];
+  __shared__ uint32_t n_out;
+  const int c = blockIdx.x % C, r = blockIdx.x / C;
+  const int tid = threadIdx.x;
+  const int x0 = c * kChunk, x1 = min(V, x0 + kChunk), n = x1 - x0;
+  const float* src = row_ptr(p, q, ps, qs, K, V, r);
+  float* dst = probs + (int64_t)r * V;
+  float gmx = 0.f, inv = 0.f;
+  if (input_kind == 1) row_normaliser(stats, r, C, redf, gmx, inv);
+  if (tid == 0) n_out = 0u;
+  int bad = 0;
+  auto visit = [&](int x, float pv) {
+    const bool ok = prob_ok(pv);
+    bad |= !ok;
+    // An invalid probability marks the row invalid; its key keeps only the id
+    // part, so the keys stay distinct and below 2^50 whatever the input.
+    keys[x - x0] = key_of(ok ? pv : 0.f, x, V);
+  };
+  if (input_kind == 1) {
+    for_range(src, x0, x1, [&](int x, float v) {
+      const float pv = exp2f(scaled_logit(v, t_scale) - gmx) * inv;
+      dst[x] = pv;
+      visit(x, pv);
+    });
+  } else {
+    for_range(src, x0, x1, visit);
+  }
+  const int any_bad = __syncthreads_or(bad);
+  u64 kr[kSelJ];
+#pragma unroll
+  for (int j = 0; j < kSelJ; ++j) {
+    const int i = j * kCT + tid;
+    kr[j] = i < n ? keys[i] : kNoKey;
+  }
+  const uint32_t kk = (uint32_t)min(top_k, n);
+  const u64 T = kk < (uint32_t)n ? select_top<kCT>(kr, kk, s) : 0ull;
+  u64* out = cand + (int64_t)r * kCandCap + (int64_t)c * top_k;
+#pragma unroll
+  for (int j = 0; j < kSelJ; ++j) {
+    if (kr[j] != kNoKey && kr[j] >= T) {
+      const uint32_t slot = atomicAdd(&n_out, 1u);  // < kk: exactly kk keys are >= T
+      if (slot < kk) out[slot] = kr[j];
+    }
+  }
+  for (int i = (int)kk + tid; i < top_k; i += kCT) out[i] = kNoKey;
+  if (tid == 0) badf[(int64_t)r * C + c] = any_bad ? 1u : 0u;
+}
+
+// Per row: the top_k keys of the row from the chunks' candidates, their mass
+// Z_k, then top-p over them: sorted descending (top_k <= 64, one per lane of the
+// first wave), the first key whose running mass reaches ceil(tp * Z_k / 2^24).
+__global__ __launch_bounds__(kRowThreads) void rows_topk_merge_kernel(int C, int top_k, uint32_t tp,
+                                                                      const u64* __restrict__ cand,
+                                                                      const uint32_t* __restrict__ badf,
+                                                                      RowMeta* __restrict__ meta) {
+  __shared__ TopLds s;
+  __shared__ u64 kept[kTopKMax];
+  __shared__ u64 sorted[kTopKMax];
+  __shared__ uint32_t n_kept;
+  __shared__ uint32_t cnt_lds[kRowThreads / 64];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  int bad = 0;
+  for (int i = tid; i < C; i += kRowThreads) bad |= badf[(int64_t)r * C + i] != 0u;
+  if (tid == 0) n_kept = 0u;
+  if (__syncthreads_or(bad)) {
+    if (tid == 0) meta[r] = RowMeta{0ull, 0ull, 1, {0, 0, 0}};
+    return;
+  }
+  const int n = C * top_k;
+  u64 kr[kSelJ];
+  uint32_t present = 0u;
+#pragma unroll
+  for (int j = 0; j < kSelJ; ++j) {
+    const int i = j * kRowThreads + tid;
+    kr[j] = i < n ? cand[(int64_t)r * kCandCap + i] : kNoKey;
+    present += kr[j] != kNoKey;
+  }
+  const uint32_t n_present = wg_sum<uint32_t>(present, cnt_lds);  // >= top_k (top_k < V)
+  const u64 T = n_present > (uint32_t)top_k ? select_top<kRowThreads>(kr, (uint32_t)top_k, s) : 0ull;
+#pragma unroll
+  for (int j = 0; j < kSelJ; ++j) {
+    if (kr[j] != kNoKey && kr[j] >= T) {
+      const uint32_t slot = atomicAdd(&n_kept, 1u);  // < top_k: exactly top_k keys are >= T
+      if (slot < (uint32_t)top_k) kept[slot] = kr[j];
+    }
+  }
+  __syncthreads();
+  const int kc = min((int)n_kept, top_k);  // == top_k
+  if (kc == 0) {  // not reached: top_k >= 1 keys are present
+    if (tid == 0) meta[r] = RowMeta{0ull, 0ull, 1, {0, 0, 0}};
+    return;
+  }
+  const int lane = tid & 63;
+  if (tid < kc) {
+    const u64 mine = kept[lane];
+    int rank = 0;
+    for (int i = 0; i < kc; ++i) rank += kept[i] > mine;
+    sorted[rank] = mine;
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  const u64 key = lane < kc ? sorted[lane] : 0ull;
+  const u64 m = lane < kc ? mass_of(key_value(key)) : 0ull;
+  u64 incl = m;
+  for (int off = 1; off < 64; off <<= 1) {
+    const u64 o = shfl_up_u64(incl, off);
+    if (lane >= off) incl += o;
+  }
+  const u64 zk = shfl_u64(incl, kc - 1);
+  if (tp >= (1u << 24) || zk == 0) {
+    // No top-p, or nothing kept: the threshold is the smallest kept key.
+    if (lane == kc - 1) meta[r] = RowMeta{key, zk, zk == 0 ? 1 : 0, {0, 0, 0}};
+    return;
+  }
+  const u64 thr = (u64)(((u128)tp * zk + ((u128)1 << 24) - 1) >> 24);  // 1 <= thr <= zk
+  if (lane < kc && incl - m < thr && thr <= incl) meta[r] = RowMeta{key, incl, 0, {0, 0, 0}};
+}
+
 // ------------------------------------------------------- chunked draw (entries)
 // Per (chunk, entry): the accept tests (every workgroup of the entry repeats
 // them: K pairs of loads), then the chunk's sums of the draw weights of the
@@ -1593,7 +1852,22 @@ hipError_t accept_launch(const AcceptPlan& plan, const float* p, const float* q,
   const bool use_p = tp < (1u << 24);
   const int C = plan.chunks;
   hipError_t e;
-  if (plan.chunked) {
+  if (plan.chunked && use_k && top_k <= kTopKMax) {
+    // Small top-k: per-chunk candidates, then one select per row over them
+    // (the per-chunk validity flags go where the histograms would).
+    const unsigned cg = (unsigned)(C * R);
+    if (input_kind == 1) {
+      hipLaunchKernelGGL(rows_stats_kernel, dim3(cg), dim3(kCT), 0, stream, p, q, p_stride, q_stride, K, V, C,
+                         t_scale, stats, st, hcnt, hmass);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(rows_chunk_topk_kernel, dim3(cg), dim3(kCT), 0, stream, p, q, input_kind, p_stride, q_stride,
+                       K, V, C, t_scale, probs, stats, top_k, cand, hcnt);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(rows_topk_merge_kernel, dim3((unsigned)R), dim3(kRowThreads), 0, stream, C, top_k, tp, cand,
+                       hcnt, meta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else if (plan.chunked) {
     const unsigned cg = (unsigned)(C * R);
     if (input_kind == 1) {  // the statistics pass also clears the rows' state and level-0 histograms
       hipLaunchKernelGGL(rows_stats_kernel, dim3(cg), dim3(kCT), 0, stream, p, q, p_stride, q_stride, K, V, C,

@@ -243,3 +243,56 @@ def test_refined_regions(vq, kind, top_k, top_p):
     got = _gpu(vq, P, Q, D, U, top_k=top_k, top_p=top_p)
     ref = _oracle(P, Q, D, U, top_k, top_p)
     assert np.array_equal(got[1], ref[1]) and np.array_equal(got[0], ref[0]), (got, ref)
+
+
+def _small_k_row(kind: str, V: int, rng) -> np.ndarray:
+    if kind == "random":
+        p = rng.random(V) ** 8
+        return (p / p.sum()).astype(np.float32)
+    if kind == "flat":
+        return np.full(V, np.float32(1.0 / V))
+    return _structured_row(kind, V, rng)
+
+
+@pytest.mark.parametrize("V,top_k,top_p,kind", [
+    (3 * 4096 + 5, 20, 0.95, "random"),     # last chunk shorter than top_k
+    (3 * 4096 + 5, 64, 1.0, "random"),
+    (100, 64, 0.9, "random"),               # a single chunk
+    (65, 64, 1.0, "random"),                # every key but one kept
+    (5000, 63, 0.8, "flat"),                # equal probabilities: the ids decide
+    (248320, 20, 0.95, "flat"),
+    (248320, 1, 1.0, "one_hot"),
+    (248320, 64, 0.95, "one_hot"),          # fewer nonzero than top_k: zeros in id order
+    (248320, 65, 0.95, "one_hot"),          # just above the per-chunk candidate path
+    (40000, 50, 0.5, "random"),
+])
+def test_small_top_k(vq, V, top_k, top_p, kind):
+    """Top-k of at most 64 goes through per-chunk candidates and one select per
+    row over them: short and single chunks, ties broken by id across chunks,
+    rows with fewer nonzero probabilities than top_k. Bit-exact, K = 3."""
+    K, B = 3, 3
+    rng = np.random.default_rng(V + 7 * top_k + sum(map(ord, kind)))
+    P = np.stack([np.stack([_small_k_row(kind, V, rng) for _ in range(K + 1)]) for _ in range(B)])
+    Q = np.stack([np.stack([_small_k_row(kind, V, rng) for _ in range(K)]) for _ in range(B)])
+    Q[0] = P[0, :K]          # every draft accepted, then the bonus draw
+    ud = uniforms24(11, (B, K), stream="draft-u")
+    U = uniforms24(11, (B, K + 1))
+    D = np.array([[oacc.sample_truncated(Q[b, i], top_k, top_p, ud[b, i]) for i in range(K)] for b in range(B)])
+    got = _gpu(vq, P, Q, D, U, top_k=top_k, top_p=top_p)
+    ref = _oracle(P, Q, D, U, top_k, top_p)
+    assert np.array_equal(got[1], ref[1]) and np.array_equal(got[0], ref[0]), (got, ref)
+
+
+def test_small_top_k_invalid_rows(vq):
+    """Invalid probabilities and an all-zero row under top-k 20: the entries they
+    touch report -1, the others match the oracle."""
+    K, V = 3, 10000
+    P, Q, D, U = _entries(0, 6, K, V, 1.0, 20, 0.95)
+    P[1, 2, 17] = np.nan
+    Q[2, 0, 3] = -1e-8
+    P[3, 1, :] = 0.0
+    Q[4, 2, 9999] = 1.5
+    got = _gpu(vq, P, Q, D, U, top_k=20, top_p=0.95)
+    ref = _oracle(P, Q, D, U, 20, 0.95)
+    assert np.array_equal(got[1], ref[1]) and np.array_equal(got[0], ref[0])
+    assert list(got[1][1:5]) == [-1] * 4 and got[1][0] >= 0 and got[1][5] >= 0
