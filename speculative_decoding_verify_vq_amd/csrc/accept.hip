@@ -1264,13 +1264,16 @@ static_assert(kTopKMax <= 64, "the top-p walk over the kept keys takes one lane 
 static_assert((int64_t)kTopKMax * ((VQ_MAX_VOCAB + kChunk - 1) / kChunk) <= kCandCap,
               "every chunk's candidates fit one row's gather buffer");
 
+struct TopRes {
+  uint32_t digit, excl, cnt;
+};
+
 struct TopLds {
   uint32_t hist[256];
   u64 r_or[kRowThreads / 64];
   u64 r_and[kRowThreads / 64];
-  u64 scan[kRowThreads / 64 + 1];
-  int digit;
-  uint32_t excl, cnt;
+  uint32_t wsum[4];
+  TopRes res[2];  // by level parity, so that a level needs no barrier before it writes its own
 };
 
 __device__ __forceinline__ u64 shfl_xor_u64(u64 v, int off) {
@@ -1283,66 +1286,67 @@ __device__ __forceinline__ u64 shfl_u64(u64 v, int src_lane) {
   return ((u64)hi << 32) | lo;
 }
 
-// Among the keys held kSelJ per thread (kNoKey in empty slots), the bound T with
-// exactly `need` keys >= T, for 1 <= need < number of keys. Radix select from the
-// top over the region of keys that share the bits above `shift`: each level
-// first extends the region's prefix over the bits on which all of its keys agree
-// (their bitwise OR and AND), then counts the next (up to) 8 bits, so every
-// level separates at least two keys whatever their high bits are. Keys are
-// distinct, so the walk ends at a digit that holds exactly the keys still needed.
+// A workgroup barrier that orders LDS accesses only: global stores still in
+// flight (the probabilities the chunk pass writes) are not waited for.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Among the keys held kSelJ per thread in slots j < nj (kNoKey: empty), the
+// bound T with exactly `need` keys >= T, for 1 <= need < number of keys. Radix
+// select from the top over the keys still in the running (one bit per slot):
+// each level takes the highest bit in which those keys differ (from their
+// bitwise OR and AND), counts the digit of up to 8 bits from there down, and
+// keeps the keys of the digit where the count from the top reaches `need`.
+// Bits that every remaining key shares cost nothing, so a crowd of equal
+// probabilities takes one level; keys are distinct, so the walk ends at a digit
+// that holds exactly the keys still needed.
 template <int NT>
-__device__ u64 select_top(const u64 (&key)[kSelJ], uint32_t need, TopLds& s) {
+__device__ u64 select_top(const u64 (&key)[kSelJ], int nj, uint32_t need, TopLds& s) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  u64 prefix = 0;
-  int shift = 50;
-  // Every level lowers `shift` by at least one, so at most 50 levels run.
-  for (;;) {
-    const u64 low = (1ull << shift) - 1ull;
-    u64 o = 0ull, a = low;
+  uint32_t alive = 0u;
+#pragma unroll
+  for (int j = 0; j < kSelJ; ++j)
+    if (j < nj && key[j] != kNoKey) alive |= 1u << j;
+  // Each level lowers the highest bit in which the remaining keys differ, and
+  // keys are below 2^50: at most 50 levels.
+  for (int level = 0; level < 64; ++level) {
+    TopRes& res = s.res[level & 1];
+    u64 o = 0ull, a = ~0ull;
 #pragma unroll
     for (int j = 0; j < kSelJ; ++j) {
-      if ((key[j] >> shift) == prefix) {
-        o |= key[j] & low;
-        a &= key[j] & low;
+      if (j < nj && ((alive >> j) & 1u)) {
+        o |= key[j];
+        a &= key[j];
       }
     }
     for (int off = 32; off > 0; off >>= 1) {
       o |= shfl_xor_u64(o, off);
       a &= shfl_xor_u64(a, off);
     }
-    __syncthreads();  // the previous level's readers of s are done
     if (lane == 0) {
       s.r_or[wave] = o;
       s.r_and[wave] = a;
     }
     for (int b = tid; b < 256; b += NT) s.hist[b] = 0u;
-    if (tid == 0) {
-      s.digit = 0;
-      s.excl = 0u;
-      s.cnt = need;  // stands only if no digit crosses (never for distinct keys): ends the walk
-    }
-    __syncthreads();
+    if (tid == 0) res = TopRes{0u, 0u, need};  // stands only if no digit crosses (never for distinct keys)
+    lds_barrier();
     o = 0ull;
-    a = low;
+    a = ~0ull;
     for (int w = 0; w < NT / 64; ++w) {
       o |= s.r_or[w];
       a &= s.r_and[w];
     }
-    // The region holds more than need >= 1 distinct keys, so they differ
-    // somewhere below `shift` (> 0); the guard only bounds the loop.
-    if ((o ^ a) == 0ull || shift == 0) return prefix << shift;
-    const int h = 63 - __clzll((long long)(o ^ a));
-    prefix = (prefix << (shift - h - 1)) | (a >> (h + 1));
-    shift = h + 1;
+    if (o < a) return 0ull;  // no key left (not reached)
+    const u64 diff = o ^ a;
+    if (diff == 0ull) return a;  // one key left (not reached for need < count)
+    const int h = 63 - __clzll((long long)diff);
     const int lo = h >= 7 ? h - 7 : 0;
-    const int w = h - lo + 1;
-    const uint32_t dmask = (1u << w) - 1u;
-    // Counts of the digit [h .. lo]: a thread's run of keys in one digit is one
-    // LDS atomic (a crowd that shares a digit would serialise on one address).
+    const uint32_t dmask = (2u << (h - lo)) - 1u;
+    // Counts of the digit: a thread's run of keys in one digit is one LDS atomic
+    // (a crowd that shares a digit would serialise on one address).
     uint32_t run_d = 0u, run_c = 0u;
 #pragma unroll
     for (int j = 0; j < kSelJ; ++j) {
-      if ((key[j] >> shift) == prefix) {
+      if (j < nj && ((alive >> j) & 1u)) {
         const uint32_t d = (uint32_t)(key[j] >> lo) & dmask;
         if (run_c && d != run_d) {
           atomicAdd(&s.hist[run_d], run_c);
@@ -1353,37 +1357,45 @@ __device__ u64 select_top(const u64 (&key)[kSelJ], uint32_t need, TopLds& s) {
       }
     }
     if (run_c) atomicAdd(&s.hist[run_d], run_c);
-    __syncthreads();
-    // Thread t < 2^w owns digit 2^w - 1 - t (descending).
-    const int nb = 1 << w;
-    const int d = nb - 1 - tid;
-    const uint32_t c = tid < nb ? s.hist[d] : 0u;
-    u64 tot;
-    const u64 excl = block_excl_scan<u64, NT>((u64)c, s.scan, tot);
-    if (tid < nb && excl < need && need <= excl + c) {
-      s.digit = d;
-      s.excl = (uint32_t)excl;
-      s.cnt = c;
+    lds_barrier();
+    // Thread t <= dmask owns digit dmask - t (descending): a scan over the first
+    // four waves (at most 256 digits).
+    const int d = (int)dmask - tid;
+    const uint32_t c = d >= 0 ? s.hist[d] : 0u;
+    uint32_t inc = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o2 = __shfl_up(inc, off);
+      if (lane >= off) inc += o2;
     }
-    __syncthreads();
-    need -= s.excl;
-    prefix = (prefix << w) | (u64)s.digit;
-    shift = lo;
-    if (s.cnt == need) return prefix << shift;
+    if (lane == 63 && wave < 4) s.wsum[wave] = inc;
+    lds_barrier();
+    uint32_t excl = inc - c;
+    for (int w2 = 0; w2 < wave && w2 < 4; ++w2) excl += s.wsum[w2];
+    if (d >= 0 && excl < need && need <= excl + c) res = TopRes{(uint32_t)d, excl, c};
+    lds_barrier();
+    const TopRes got = res;
+    need -= got.excl;
+    if (got.cnt == need) return ((a >> (h + 1)) << (h + 1)) | ((u64)got.digit << lo);
+#pragma unroll
+    for (int j = 0; j < kSelJ; ++j)
+      if (j < nj && ((alive >> j) & 1u) && ((uint32_t)(key[j] >> lo) & dmask) != got.digit) alive &= ~(1u << j);
   }
+  return 0ull;  // not reached
 }
 
 // Per (chunk, row): the probabilities (logits mode: written to probs), their
-// validity, and the chunk's top min(top_k, length) keys in slots [0, top_k) of
-// cand[row * kCandCap + chunk * top_k] (kNoKey in the rest).
+// validity, the chunk's top min(top_k, length) keys in slots [0, top_k) of
+// cand[row * kCandCap + chunk * top_k] (kNoKey in the rest), and a bound T with
+// exactly min(top_k, length) of the chunk's keys >= T (0 if it keeps them all).
 __global__ __launch_bounds__(kCT) void rows_chunk_topk_kernel(
     const float* __restrict__ p, const float* __restrict__ q, int input_kind, int64_t ps, int64_t qs, int K, int V,
     int C, float t_scale, float* __restrict__ probs, const float2* __restrict__ stats, int top_k,
-    u64* __restrict__ cand, uint32_t* __restrict__ badf) {
+    u64* __restrict__ cand, uint32_t* __restrict__ badf, u64* __restrict__ bound) {
   __shared__ u64 keys[kChunk];
   __shared__ TopLds s;
   __shared__ float redf[kCT / 64];
-  __shared__ uint32_t n_out;
+  __shared__ uint32_t n_out, s_bad;
   const int c = blockIdx.x % C, r = blockIdx.x / C;
   const int tid = threadIdx.x;
   const int x0 = c * kChunk, x1 = min(V, x0 + kChunk), n = x1 - x0;
@@ -1391,11 +1403,15 @@ __global__ __launch_bounds__(kCT) void rows_chunk_topk_kernel(
   float* dst = probs + (int64_t)r * V;
   float gmx = 0.f, inv = 0.f;
   if (input_kind == 1) row_normaliser(stats, r, C, redf, gmx, inv);
-  if (tid == 0) n_out = 0u;
-  int bad = 0;
+  if (tid == 0) {
+    n_out = 0u;
+    s_bad = 0u;
+  }
+  lds_barrier();
+  uint32_t bad = 0u;
   auto visit = [&](int x, float pv) {
     const bool ok = prob_ok(pv);
-    bad |= !ok;
+    bad |= ok ? 0u : 1u;
     // An invalid probability marks the row invalid; its key keeps only the id
     // part, so the keys stay distinct and below 2^50 whatever the input.
     keys[x - x0] = key_of(ok ? pv : 0.f, x, V);
@@ -1409,7 +1425,9 @@ __global__ __launch_bounds__(kCT) void rows_chunk_topk_kernel(
   } else {
     for_range(src, x0, x1, visit);
   }
-  const int any_bad = __syncthreads_or(bad);
+  if (bad) atomicOr(&s_bad, 1u);
+  lds_barrier();  // keys and s_bad complete; the probability stores drain meanwhile
+  const uint32_t any_bad = s_bad;
   u64 kr[kSelJ];
 #pragma unroll
   for (int j = 0; j < kSelJ; ++j) {
@@ -1417,7 +1435,7 @@ __global__ __launch_bounds__(kCT) void rows_chunk_topk_kernel(
     kr[j] = i < n ? keys[i] : kNoKey;
   }
   const uint32_t kk = (uint32_t)min(top_k, n);
-  const u64 T = kk < (uint32_t)n ? select_top<kCT>(kr, kk, s) : 0ull;
+  const u64 T = kk < (uint32_t)n ? select_top<kCT>(kr, kSelJ, kk, s) : 0ull;
   u64* out = cand + (int64_t)r * kCandCap + (int64_t)c * top_k;
 #pragma unroll
   for (int j = 0; j < kSelJ; ++j) {
@@ -1427,65 +1445,81 @@ __global__ __launch_bounds__(kCT) void rows_chunk_topk_kernel(
     }
   }
   for (int i = (int)kk + tid; i < top_k; i += kCT) out[i] = kNoKey;
-  if (tid == 0) badf[(int64_t)r * C + c] = any_bad ? 1u : 0u;
+  if (tid == 0) {
+    badf[(int64_t)r * C + c] = any_bad ? 1u : 0u;
+    bound[(int64_t)r * C + c] = T;
+  }
 }
 
 // Per row: the top_k keys of the row from the chunks' candidates, their mass
-// Z_k, then top-p over them: sorted descending (top_k <= 64, one per lane of the
-// first wave), the first key whose running mass reaches ceil(tp * Z_k / 2^24).
+// Z_k, then top-p over them in descending order: the first key whose running
+// mass reaches ceil(tp * Z_k / 2^24). The largest chunk bound L is a lower bound
+// of the row's top_k-th key (its chunk holds top_k keys >= L), so candidates
+// below L are dropped before the select (for a near one-hot row, every chunk's
+// run of zero probabilities but the first).
 __global__ __launch_bounds__(kRowThreads) void rows_topk_merge_kernel(int C, int top_k, uint32_t tp,
                                                                       const u64* __restrict__ cand,
                                                                       const uint32_t* __restrict__ badf,
+                                                                      const u64* __restrict__ bound,
                                                                       RowMeta* __restrict__ meta) {
   __shared__ TopLds s;
   __shared__ u64 kept[kTopKMax];
   __shared__ u64 sorted[kTopKMax];
+  __shared__ u64 red[kRowThreads / 64];
   __shared__ uint32_t n_kept;
-  __shared__ uint32_t cnt_lds[kRowThreads / 64];
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int bad = 0;
-  for (int i = tid; i < C; i += kRowThreads) bad |= badf[(int64_t)r * C + i] != 0u;
+  u64 lb = 0ull;
+  for (int i = tid; i < C; i += kRowThreads) {
+    bad |= badf[(int64_t)r * C + i] != 0u;
+    lb = max(lb, bound[(int64_t)r * C + i]);
+  }
+  for (int off = 32; off > 0; off >>= 1) lb = max(lb, shfl_xor_u64(lb, off));
+  if (lane == 0) red[wave] = lb;
   if (tid == 0) n_kept = 0u;
   if (__syncthreads_or(bad)) {
     if (tid == 0) meta[r] = RowMeta{0ull, 0ull, 1, {0, 0, 0}};
     return;
   }
+  u64 L = 0ull;
+  for (int w = 0; w < kRowThreads / 64; ++w) L = max(L, red[w]);
   const int n = C * top_k;
+  const int nj = (n + kRowThreads - 1) / kRowThreads;  // slots in use per thread
   u64 kr[kSelJ];
-  uint32_t present = 0u;
+  uint32_t live = 0u;
 #pragma unroll
   for (int j = 0; j < kSelJ; ++j) {
     const int i = j * kRowThreads + tid;
-    kr[j] = i < n ? cand[(int64_t)r * kCandCap + i] : kNoKey;
-    present += kr[j] != kNoKey;
+    const u64 k = i < n ? cand[(int64_t)r * kCandCap + i] : kNoKey;
+    kr[j] = (k != kNoKey && k >= L) ? k : kNoKey;  // only keys >= L can be kept
+    live += kr[j] != kNoKey;
   }
-  const uint32_t n_present = wg_sum<uint32_t>(present, cnt_lds);  // >= top_k (top_k < V)
-  const u64 T = n_present > (uint32_t)top_k ? select_top<kRowThreads>(kr, (uint32_t)top_k, s) : 0ull;
+  const uint32_t m = wg_sum<uint32_t>(live, reinterpret_cast<uint32_t*>(red));  // >= top_k
+  const u64 T = m > (uint32_t)top_k ? select_top<kRowThreads>(kr, nj, (uint32_t)top_k, s) : 0ull;
 #pragma unroll
   for (int j = 0; j < kSelJ; ++j) {
-    if (kr[j] != kNoKey && kr[j] >= T) {
+    if (j < nj && kr[j] != kNoKey && kr[j] >= T) {
       const uint32_t slot = atomicAdd(&n_kept, 1u);  // < top_k: exactly top_k keys are >= T
       if (slot < (uint32_t)top_k) kept[slot] = kr[j];
     }
   }
   __syncthreads();
   const int kc = min((int)n_kept, top_k);  // == top_k
-  if (kc == 0) {  // not reached: top_k >= 1 keys are present
-    if (tid == 0) meta[r] = RowMeta{0ull, 0ull, 1, {0, 0, 0}};
-    return;
-  }
-  const int lane = tid & 63;
   if (tid < kc) {
-    const u64 mine = kept[lane];
+    const u64 mine = kept[tid];
     int rank = 0;
     for (int i = 0; i < kc; ++i) rank += kept[i] > mine;
     sorted[rank] = mine;
   }
   __syncthreads();
   if (tid >= 64) return;
+  if (kc == 0) {  // not reached: top_k >= 1 keys are present
+    if (tid == 0) meta[r] = RowMeta{0ull, 0ull, 1, {0, 0, 0}};
+    return;
+  }
   const u64 key = lane < kc ? sorted[lane] : 0ull;
-  const u64 m = lane < kc ? mass_of(key_value(key)) : 0ull;
-  u64 incl = m;
+  const u64 ms = lane < kc ? mass_of(key_value(key)) : 0ull;
+  u64 incl = ms;
   for (int off = 1; off < 64; off <<= 1) {
     const u64 o = shfl_up_u64(incl, off);
     if (lane >= off) incl += o;
@@ -1497,7 +1531,7 @@ __global__ __launch_bounds__(kRowThreads) void rows_topk_merge_kernel(int C, int
     return;
   }
   const u64 thr = (u64)(((u128)tp * zk + ((u128)1 << 24) - 1) >> 24);  // 1 <= thr <= zk
-  if (lane < kc && incl - m < thr && thr <= incl) meta[r] = RowMeta{key, incl, 0, {0, 0, 0}};
+  if (lane < kc && incl - ms < thr && thr <= incl) meta[r] = RowMeta{key, incl, 0, {0, 0, 0}};
 }
 
 // ------------------------------------------------------- chunked draw (entries)
@@ -1854,7 +1888,7 @@ hipError_t accept_launch(const AcceptPlan& plan, const float* p, const float* q,
   hipError_t e;
   if (plan.chunked && use_k && top_k <= kTopKMax) {
     // Small top-k: per-chunk candidates, then one select per row over them
-    // (the per-chunk validity flags go where the histograms would).
+    // (the per-chunk validity flags and bounds go where the histograms would).
     const unsigned cg = (unsigned)(C * R);
     if (input_kind == 1) {
       hipLaunchKernelGGL(rows_stats_kernel, dim3(cg), dim3(kCT), 0, stream, p, q, p_stride, q_stride, K, V, C,
@@ -1862,10 +1896,10 @@ hipError_t accept_launch(const AcceptPlan& plan, const float* p, const float* q,
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(rows_chunk_topk_kernel, dim3(cg), dim3(kCT), 0, stream, p, q, input_kind, p_stride, q_stride,
-                       K, V, C, t_scale, probs, stats, top_k, cand, hcnt);
+                       K, V, C, t_scale, probs, stats, top_k, cand, hcnt, hmass);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(rows_topk_merge_kernel, dim3((unsigned)R), dim3(kRowThreads), 0, stream, C, top_k, tp, cand,
-                       hcnt, meta);
+                       hcnt, hmass, meta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else if (plan.chunked) {
     const unsigned cg = (unsigned)(C * R);
