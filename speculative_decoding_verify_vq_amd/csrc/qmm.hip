@@ -306,9 +306,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
   };
 
-  // Code blocks in flight per wave. Every block load is issued unconditionally
-  // (block index clamped) and the blocks of an x chunk are unrolled, so the
-  // wait counts the compiler derives are exact.
+  // Code blocks in flight per wave. In the split variants every block load is
+  // issued unconditionally (block index clamped into the range, so past its end
+  // the loads re-read its last block) and the blocks of an x chunk are
+  // unrolled, so the wait counts the compiler derives are exact: with a
+  // conditional issue it cannot count the loads in flight at the next block and
+  // waits for all of them, which leaves one block in flight instead of two. The
+  // chunked variant issues only blocks inside the range.
   Regs R[kInFlight];
 
   // ---- x, staged in chunks of CG groups in the element order of the unpack,
@@ -494,7 +498,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
       const int b = ch * kBPC + bc;
       if (b >= nblk) break;
       Regs& Rb = R[bc % kInFlight];
-      const bool more = b + kInFlight < nblk;
+      const bool more = CHUNK ? b + kInFlight < nblk : true;  // see the block ring above
       consume(Rb);
       if constexpr (LAYOUT == kLayoutTiled) {
         if (more) issue_sb(Rb, b + kInFlight);
