@@ -845,6 +845,11 @@ QmmPlan qmm_plan(int bits, int M, int N, int K, bool tiled) {
   int gps = (G + s - 1) / s;
   gps = (gps + 2) / 4 * 4;  // nearest multiple of 4
   if (gps < 4) gps = 4;
+  // At least three blocks per range for long K (64 groups or more, the shapes
+  // this was measured on): the ring issues two blocks up front and then one per
+  // block consumed (clamped past the range), so a two-block range pays two
+  // re-read blocks and gains nothing from the ring.
+  if (gps < 3 * GB && G >= 64) gps = (3 * GB + 3) / 4 * 4;
   if (gps > kCG) gps = kCG;
   p.groups_per_split = gps;
   p.splits = (G + gps - 1) / gps;

@@ -78,11 +78,22 @@ def test_stack_step_matches_oracle(vq, bits, M, layers, unit):
     torch.cuda.synchronize()
 
     # oracle composition on the same weights and caches, layer by layer
+    kv_tf = [{k: v.copy() for k, v in c.items()} for c in kv]
     hs = ostack.stack_forward(to_f64(bf16_tensor(hb)), ora_w, kv, cfg.ctx, cfg.Hq, cfg.Hkv, cfg.D, cfg.inter,
                               attn_every=cfg.attn_every)
     assert len(per_layer) == layers
     for li in range(layers):
         assert_close(to_f64(per_layer[li]), hs[li], f"hidden rows after layer {li}")
+    # Each layer alone: the oracle layer fed the device's own hidden rows of the
+    # layer before (no bf16 rounding differences carried in from earlier layers).
+    h_in, ai = to_f64(bf16_tensor(hb)), 0
+    for li in range(layers):
+        attn = ostack.is_attention_layer(li, cfg.attn_every)
+        ho = ostack.layer_forward(h_in, ora_w[li], attn, kv_tf[ai] if attn else None, cfg.ctx, cfg.Hq, cfg.Hkv,
+                                  cfg.D, cfg.inter)
+        ai += int(attn)
+        assert_close(to_f64(per_layer[li]), ho, f"layer {li} on the device's own input")
+        h_in = to_f64(per_layer[li])
     h = hs[-1]
     if unit:
         assert np.abs(h).max() < 64.0, "activations of order 1"
