@@ -850,7 +850,10 @@ QmmPlan qmm_plan(int bits, int M, int N, int K, bool tiled) {
   // block consumed (clamped past the range), so a two-block range pays two
   // re-read blocks and gains nothing from the ring.
   if (gps < 3 * GB && G >= 64) gps = (3 * GB + 3) / 4 * 4;
-  if (gps > kCG) gps = kCG;
+  // Outputs of fewer than 64 column blocks (the 5120-wide o projection) split K
+  // into full x chunks: the last workgroup of a column block sums fewer
+  // partials, which outweighs the workgroups lost (o: 240 instead of 480).
+  if (gps > kCG || (p.n_blocks < 64 && G > kCG)) gps = kCG;
   p.groups_per_split = gps;
   p.splits = (G + gps - 1) / gps;
   // n_blocks <= kCounterBytes / 4 follows from the N <= 2^20 limit of the ABI.
