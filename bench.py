@@ -995,7 +995,7 @@ def main() -> int:
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the verify step; runs on more than one GPU are not "
-              "part of this build (see DESIGN.md for how the path would shard).", file=sys.stderr)
+              "supported by this library.", file=sys.stderr)
         return 2
 
     import torch
