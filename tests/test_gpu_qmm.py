@@ -41,6 +41,11 @@ def test_config0_all_rows(vq, bits, M):
     (8, 9, 96, 8192),
     (4, 1, 4000, 64),           # single group
     (8, 12, 1000, 1088),
+    # plan rules for long K: narrow outputs take full 16-group ranges (ragged last
+    # range), wider ones at least three blocks per range
+    (4, 4, 300, 64 * 97),
+    (8, 8, 5120, 64 * 75),
+    (4, 4, 8256, 64 * 70),
 ])
 def test_ragged_and_split_shapes(vq, bits, M, N, K):
     w = qmm_weights(11, N, K, bits, layer=N)

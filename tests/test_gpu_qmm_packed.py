@@ -88,6 +88,11 @@ def test_packed_store_config0(vq, bits, M):
     (4, 1, 4000, 64),
     (8, 12, 1000, 1088),
     (4, 4, 65536, 512),         # one K split (no cross-workgroup reduction)
+    # plan rules for long K: narrow outputs take full 16-group ranges (ragged last
+    # range), wider ones at least three blocks per range
+    (4, 4, 300, 64 * 97),
+    (8, 8, 5120, 64 * 75),
+    (4, 4, 8256, 64 * 70),
 ])
 def test_packed_store_ragged(vq, bits, M, N, K):
     w = qmm_weights(11, N, K, bits, layer=N)
