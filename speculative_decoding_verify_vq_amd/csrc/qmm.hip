@@ -612,13 +612,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   __syncthreads();
   if (!s_last) return;
   // Sum the partials in split order, kBatch splits x kVPT x kPair loads in
-  // flight per thread (36 or fewer). Thread t, value i covers element t + i * 256
-  // of the block's [M][128] (store, residual) or of its [M][64] gate/up column
-  // pairs (SwiGLU).
+  // flight per thread (at most 36, 64 for 16 rows: each batch is a round trip,
+  // and the 16-row variant reads twice the partials per split; a budget of 64
+  // at 4 and 8 rows measured slower). Thread t, value i covers element
+  // t + i * 256 of the block's [M][128] (store, residual) or of its [M][64]
+  // gate/up column pairs (SwiGLU).
   constexpr int kCols = EPI == kEpiSwiGLU ? kColsWG / 2 : kColsWG;
   constexpr int kVPT = MT * kCols / kThreads;
   constexpr int kPair = EPI == kEpiSwiGLU ? 2 : 1;
-  constexpr int kBatch = 36 / (kVPT * kPair);
+  constexpr int kBatch = (MT == 16 ? 64 : 36) / (kVPT * kPair);
   float v[kVPT][kPair];
   size_t idx[kVPT];
   bool ok[kVPT];
@@ -632,13 +634,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
     for (int h = 0; h < kPair; ++h) v[i][h] = 0.f;
   }
-  // The residual rows go out with the first batch of partial loads.
+  // The residual rows go out with the first batch of partial loads. These
+  // loads and the partial loads below are issued unconditionally (indices
+  // clamped into the arrays, unused values discarded at the sum): a load under
+  // a per-lane condition is followed by a full wait in the compiled code, which
+  // turned the residual loads into one round trip each.
   uint32_t rv[EPI == kEpiResidual ? kVPT : 1];
   if constexpr (EPI == kEpiResidual) {
 #pragma unroll
     for (int i = 0; i < kVPT; ++i) {
       const int t = tid + i * kThreads;
-      rv[i] = ok[i] ? a.res[(size_t)(t / kCols) * a.ldr + cb * kColsWG + t % kCols] : 0u;
+      const int m = min(t / kCols, M - 1);
+      const int col = min(cb * kColsWG + t % kCols, N - 1);
+      rv[i] = a.res[(size_t)m * a.ldr + col];
     }
   }
   const size_t sstride = (size_t)M * N;
@@ -646,14 +654,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     float pv[kBatch][kVPT][kPair];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
+      const size_t su = (size_t)min(sp + u, a.splits - 1) * sstride;
 #pragma unroll
       for (int i = 0; i < kVPT; ++i) {
 #pragma unroll
         for (int h = 0; h < kPair; ++h)
-          pv[u][i][h] = (ok[i] && sp + u < a.splits)
-                            ? __hip_atomic_load(&a.partial[(sp + u) * sstride + idx[i] + h * 64], __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT)
-                            : 0.f;
+          pv[u][i][h] = __hip_atomic_load(&a.partial[su + (ok[i] ? idx[i] + h * 64 : 0)], __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
       }
     }
 #pragma unroll
@@ -661,7 +668,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
       for (int i = 0; i < kVPT; ++i) {
 #pragma unroll
-        for (int h = 0; h < kPair; ++h) v[i][h] += pv[u][i][h];
+        for (int h = 0; h < kPair; ++h) v[i][h] += (ok[i] && sp + u < a.splits) ? pv[u][i][h] : 0.f;
       }
     }
   }
