@@ -485,19 +485,19 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
                        __uint_as_float(w.y & 0xFFFF0000u));
   };
+  // Every load of this first batch is issued (range index clamped, values past
+  // the last range unused): a load under a per-lane condition is followed by a
+  // full wait in the compiled code, which made the batch one round trip per load.
   float4 v0[kFirst];
 #pragma unroll
-  for (int u = 0; u < kFirst; ++u) {
-    const int sp = grp + u * kCombineGroups;
-    v0[u] = sp < splits ? load4(sp) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  for (int u = 0; u < kFirst; ++u) v0[u] = load4(min(grp + u * kCombineGroups, splits - 1));
   constexpr int kMLPT = kMaxSplits / 256;
   float2 ml[kMLPT];
 #pragma unroll
   for (int k = 0; k < kMLPT; ++k) {
     const int sp = tid + 256 * k;
-    ml[k] = sp < splits ? *reinterpret_cast<const float2*>(part_ml + (sp * s_stride + base) * 2)
-                        : make_float2(-INFINITY, 0.f);
+    const float2 x = *reinterpret_cast<const float2*>(part_ml + ((size_t)min(sp, splits - 1) * s_stride + base) * 2);
+    ml[k] = sp < splits ? x : make_float2(-INFINITY, 0.f);
   }
   // Range weights exp2(m_s - max) * l_s and the merged denominator (their sum).
   float mloc = -INFINITY;
