@@ -554,24 +554,23 @@ __device__ int entry_decide(const float* P, const float* Q, const RowMeta* mrow,
   // Called by one whole wave (K <= 15, so lane i holds draft i, uniform i and the
   // meta of rows i and K + 1 + i): the loads of every test go out together and
   // the first rejection is the lowest lane whose test fails.
+  // Indices are clamped so that every lane loads (a load under a per-lane
+  // condition is followed by a full wait in the compiled code, one round trip
+  // each); lanes past the data select the defaults.
   const int lane = threadIdx.x & 63;
+  const RowMeta mp_l = mrow[min(lane, 2 * K)];
+  const RowMeta mq_l = mrow[min(K + 1 + lane, 2 * K)];
+  const float u_l = us[min(lane, K)];
+  int d_l = 0;
+  if (K > 0) d_l = dr[min(lane, K - 1)];  // K is the same for the whole wave
+  const RowMeta mp = lane < 2 * K + 1 ? mp_l : RowMeta{};
+  const RowMeta mq = lane < K ? mq_l : RowMeta{};
+  const float u = lane <= K ? u_l : 0.f;
+  const int d = lane < K ? d_l : 0;
   int bad = 0;
-  RowMeta mp{}, mq{};
-  int d = 0;
-  float u = 0.f;
-  if (lane < 2 * K + 1) {
-    mp = mrow[lane];
-    bad |= mp.status;
-  }
-  if (lane < K) mq = mrow[K + 1 + lane];
-  if (lane <= K) {
-    u = us[lane];
-    bad |= !uniform_ok(u);
-  }
-  if (lane < K) {
-    d = dr[lane];
-    bad |= (d < 0 || d >= V);
-  }
+  if (lane < 2 * K + 1) bad |= mp.status;
+  if (lane <= K) bad |= !uniform_ok(u);
+  if (lane < K) bad |= (d < 0 || d >= V);
   const bool any_bad = __ballot(bad != 0) != 0ull;
   int j = K;
   if (!any_bad) {
@@ -778,16 +777,15 @@ __global__ __launch_bounds__(kCT) void rows_stats_kernel(const float* __restrict
 // scaled logit and 1 / (sum of exp2(a - largest)). Thread i takes chunks i,
 // i + kCT, ..., then a fixed reduction tree, so every workgroup of the row gets
 // the same values.
+static_assert(VQ_MAX_VOCAB / kChunk <= kCT, "a row's chunk statistics fit one per thread");
 __device__ __forceinline__ void row_normaliser(const float2* __restrict__ stats, int r, int C, float* redf,
                                                float& gmx, float& inv) {
-  float mx = -INFINITY;
-  for (int i = threadIdx.x; i < C; i += kCT) mx = fmaxf(mx, stats[(int64_t)r * C + i].x);
-  gmx = block_reduce_max(mx, redf);
-  float part = 0.f;
-  for (int i = threadIdx.x; i < C; i += kCT) {
-    const float2 s2 = stats[(int64_t)r * C + i];
-    part += (s2.x == -INFINITY) ? 0.f : s2.y * exp2f(s2.x - gmx);
-  }
+  // One chunk per thread (C <= kCT), loaded once for both reductions.
+  const int i = threadIdx.x;
+  const float2 ld = stats[(int64_t)r * C + min(i, C - 1)];
+  const float2 s2 = i < C ? ld : make_float2(-INFINITY, 0.f);
+  gmx = block_reduce_max(s2.x, redf);
+  const float part = (s2.x == -INFINITY) ? 0.f : s2.y * exp2f(s2.x - gmx);
   inv = 1.f / block_reduce_sum(part, redf);
 }
 
