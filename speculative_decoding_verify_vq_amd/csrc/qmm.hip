@@ -58,6 +58,8 @@
 //     rows per 128-row block; y = bf16(silu(bf16(g)) * bf16(u)), N/2 columns).
 #include <math.h>
 
+#include <type_traits>
+
 #include "vq_internal.h"
 
 namespace vq {
@@ -433,12 +435,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     cur_b[1] = R.b[1];
   };
   // Compute block bi of this workgroup's range, block bc of its x chunk.
-  auto compute = [&](Regs& R, int bi, int bc, bool more) __attribute__((always_inline)) {
+  // `tail`: the block may run past the range (a run-time test per group).
+  auto compute = [&](Regs& R, int bi, int bc, bool more, bool tail) __attribute__((always_inline)) {
 #pragma unroll
     for (int jb = 0; jb < GB; ++jb) {
       const int gl = bi * GB + jb;  // group index within this workgroup's range
       const int gx = bc * GB + jb;  // group index within the staged x chunk
-      if (gl >= ng) break;
+      if (tail && gl >= ng) break;
       bf16x8 av[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -489,28 +492,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 
   constexpr int kBPC = CG / GB;  // blocks per x chunk
   static_assert(kBPC % kInFlight == 0, "the register ring must restart at every chunk");
-  const int nch = CHUNK ? (ng + CG - 1) / CG : 1;
-  for (int ch = 0; ch < nch; ++ch) {
-    const bool next_x = CHUNK && ch + 1 < nch;
-    if (next_x) load_x(ch + 1);
+  // The blocks of x chunk ch. KIND 0: a chunk followed by another one (every
+  // next block is issued; the issues past the range of the split variants are
+  // clamped re-reads, see the block ring above); 1: the last chunk of a walk,
+  // full (the issues stop kInFlight blocks before its end, known at compile
+  // time); 2: the last chunk, ragged (a run-time test). Issues under a
+  // compile-time condition keep the compiler's wait counts exact; a run-time
+  // test makes it wait for every load in flight.
+  auto chunk_blocks = [&](int ch, auto kind) __attribute__((always_inline)) {
+    constexpr int KIND = decltype(kind)::value;
 #pragma unroll
     for (int bc = 0; bc < kBPC; ++bc) {
       const int b = ch * kBPC + bc;
       if (b >= nblk) break;
       Regs& Rb = R[bc % kInFlight];
-      const bool more = CHUNK ? b + kInFlight < nblk : true;  // see the block ring above
+      const bool more = KIND == 0 ? true : KIND == 1 ? bc + kInFlight < kBPC : b + kInFlight < nblk;
       consume(Rb);
       if constexpr (LAYOUT == kLayoutTiled) {
         if (more) issue_sb(Rb, b + kInFlight);
       } else {
         if (more) issue(Rb, b + kInFlight);
       }
-      compute(Rb, b, bc, more);
+      compute(Rb, b, bc, more, KIND == 2);
     }
-    if (next_x) {
+  };
+  if constexpr (CHUNK) {
+    // A walk over the whole of K: the next chunk of x is loaded into registers
+    // while this one is computed, and written to LDS between two barriers.
+    const int nch = (ng + CG - 1) / CG;
+    for (int ch = 0; ch + 1 < nch; ++ch) {
+      load_x(ch + 1);
+      chunk_blocks(ch, std::integral_constant<int, 0>{});
       __syncthreads();  // every wave is done with this chunk of x
       store_x(ch + 1);
       __syncthreads();
+    }
+    if (nblk - (nch - 1) * kBPC == kBPC)
+      chunk_blocks(nch - 1, std::integral_constant<int, 1>{});
+    else
+      chunk_blocks(nch - 1, std::integral_constant<int, 2>{});
+  } else {
+#pragma unroll
+    for (int bc = 0; bc < kBPC; ++bc) {
+      if (bc >= nblk) break;
+      Regs& Rb = R[bc % kInFlight];
+      consume(Rb);
+      if constexpr (LAYOUT == kLayoutTiled) {
+        issue_sb(Rb, bc + kInFlight);
+      } else {
+        issue(Rb, bc + kInFlight);
+      }
+      compute(Rb, bc, bc, true, true);
     }
   }
 

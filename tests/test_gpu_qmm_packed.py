@@ -232,6 +232,24 @@ def test_wide_norm_residual(vq, bits, M):
     assert_close(y, ref, f"{bits}-bit M={M} norm + residual")
 
 
+@pytest.mark.parametrize("bits,M", [(4, 3), (8, 8), (4, 13), (8, 16)])
+def test_chunked_walk_ragged(vq, bits, M):
+    """The unsplit path (N = 65536: 512 column blocks) over K = 37 groups: the
+    workgroup walks several chunks of x, the last one shorter than a chunk (and,
+    at 4 bits, ending in zero-padded groups), with the RMSNorm prologue and
+    float32 output, on sampled columns."""
+    N, K = 65536, 64 * 37
+    w = qmm_weights(19, N, K, bits, layer=M)
+    xb = qmm_activations(19, M, K, extra=M)
+    x = bf16_tensor(xb)
+    ss = vq.row_sumsq(x)
+    a = ostack.to_bf16_bits(ostack.rmsnorm(to_f64(x)))
+    y = to_f64(vq.qmm_packed(x, _pack(vq, w), bits, N, K, x_sumsq=ss, eps=1e-6, out_dtype=torch.float32))
+    c = np.unique(np.concatenate([np.random.default_rng(19 + M).choice(N, size=48, replace=False), [0, N - 1]]))
+    ref = oq.skinny_qmm(a, w["wq"], w["scales"], w["biases"], bits, 64, M, N, K, cols=c)
+    assert_close(y[:, c], ref, f"{bits}-bit M={M} chunked walk, K = 37 groups")
+
+
 def test_packed_deterministic(vq):
     w = qmm_weights(22, 1024, 8192, 4)
     x = qmm_activations(22, 8, 8192)
