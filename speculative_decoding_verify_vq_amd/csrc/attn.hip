@@ -267,8 +267,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
     __syncthreads();
   };
-  if (j0 < j1) fetch(r0, j0);
-  if (j0 + kTileKeys < j1) fetch(r1, j0 + kTileKeys);
 
   const int rt = wave / C::DS;
   const int dpart = wave % C::DS;
@@ -376,7 +374,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
   };
   static_assert(KV8 || C::UNITS % kThreads == 0, "every thread moves whole 16-byte units of a tile");
-  for (int t0 = j0; t0 < j1; t0 += 2 * kTileKeys) {
+  // While at least four tiles remain, both fetches of a pair of tiles are in
+  // the range and go out unconditionally, so the compiler's wait counts stay
+  // exact and two tiles stay in flight across each staging; a fetch under a
+  // run-time test makes it wait for every load in flight. The last one to
+  // three tiles (and ranges that short) take the tested loop.
+  int t0 = j0;
+  if (j0 + 3 * kTileKeys < j1) {
+    fetch(r0, j0);
+    fetch(r1, j0 + kTileKeys);
+    do {
+      stage(r0);
+      fetch(r0, t0 + 2 * kTileKeys);
+      tile(t0);
+      stage(r1);
+      fetch(r1, t0 + 3 * kTileKeys);
+      tile(t0 + kTileKeys);
+      t0 += 2 * kTileKeys;
+    } while (t0 + 3 * kTileKeys < j1);
+  } else {
+    if (j0 < j1) fetch(r0, j0);
+    if (j0 + kTileKeys < j1) fetch(r1, j0 + kTileKeys);
+  }
+  for (; t0 < j1; t0 += 2 * kTileKeys) {
     stage(r0);
     if (t0 + 2 * kTileKeys < j1) fetch(r0, t0 + 2 * kTileKeys);
     tile(t0);
