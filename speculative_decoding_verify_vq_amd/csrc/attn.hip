@@ -76,6 +76,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// The values of lanes i and i ^ 32, in one VALU instruction: gfx950's
+// v_permlane32_swap exchanges the upper half of the first operand with the
+// lower half of the second, so with both operands v each lane ends up holding
+// v[i] and v[i ^ 32] (an LDS permute takes a round trip through the LDS unit).
+struct LanePair {
+  float a, b;
+};
+__device__ __forceinline__ LanePair xor32_pair(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   // v_cvt_pk_bf16_f32: both values rounded to nearest even in one instruction.
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -324,7 +336,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
         mx = fmaxf(mx, s[r]);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    {
+      const LanePair p = xor32_pair(mx);  // the row's other 16 keys are in lane l ^ 32
+      mx = fmaxf(p.a, p.b);
+    }
     // Online softmax with a lazily moved reference: m_run changes only when some
     // row's maximum exceeds it by more than 8 (or at a row's first visible key),
     // so the probabilities exp2(s - m_run) stay below 2^8 and the rescale of O
@@ -344,7 +359,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
       s[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
       psum += s[r];
     }
-    psum += __shfl_xor(psum, 32);
+    {
+      const LanePair p = xor32_pair(psum);  // a + b == b + a: both lanes get the same sum
+      psum = p.a + p.b;
+    }
     l_run = l_run * alpha + psum;
     u32x4 pw0, pw1;
     pw0[0] = pack_bf16x2(s[0], s[1]);
