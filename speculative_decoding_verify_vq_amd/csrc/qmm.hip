@@ -145,6 +145,19 @@ __device__ __forceinline__ float sum8_lanes(float v) {
   return v + dpp_f32<0x141>(v);
 }
 
+// Sum over the whole wave, the same value in every lane, with no LDS round
+// trip: groups of 8, then 16 (DPP row_mirror, lane i <-> 15 - i), then rows
+// paired by gfx950's permlane swaps (16 and 32 lanes apart; each hands a lane
+// both values, and a + b == b + a, so every lane gets the same sum).
+__device__ __forceinline__ float sum64_lanes(float v) {
+  v = sum8_lanes(v);
+  v += dpp_f32<0x140>(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 // Eight nibbles -> eight bf16 values 128 + q, in the element order
 // (q0, q4, q1, q5, q2, q6, q3, q7).
 __device__ __forceinline__ bf16x8 unpack4(uint32_t w, uint32_t m, uint32_t c) {
@@ -727,10 +740,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
     if (a.y_ss) {
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-#pragma unroll
-        for (int i = 0; i < kVPT; ++i) sq[i] += __shfl_xor(sq[i], off);
-      }
+      for (int i = 0; i < kVPT; ++i) sq[i] = sum64_lanes(sq[i]);
 #pragma unroll
       for (int i = 0; i < kVPT; ++i)
         if (lane == 0) red[wave & 1][2 * i + (wave >> 1)] = sq[i];
