@@ -235,6 +235,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     else
       return *reinterpret_cast<const u32x4*>(p);
   };
+  // Keys below lim_plain are read from the cache itself (not from the rows
+  // being appended). A tile wholly below it is one contiguous run per K and
+  // V: thread t's unit e is 16-byte unit t + e * kThreads of the run, so its
+  // address is one add, not the per-key clamp and source test of the general
+  // fetch (those were about a quarter of the tile loop's vector instructions).
+  const int lim_plain = k_new ? min(j1, T - M) : j1;
   auto fetch = [&](KV& r, int t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < C::PER_THREAD; ++e) {
@@ -260,6 +266,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
       }
       r.k[e] = ld16(ks + dc * 8);
       r.v[e] = ld16(vs + dc * 8);
+    }
+  };
+  auto fetch_plain = [&](KV& r, int t0) __attribute__((always_inline)) {
+    if constexpr (C::UNITS % kThreads != 0) {
+      fetch(r, t0);  // a tile that does not split into whole units per thread
+    } else if constexpr (KV8) {
+      const size_t base = (size_t)kvh * kv_head_stride + (size_t)t0 * D;  // bytes of codes
+      const uint8_t* kt = reinterpret_cast<const uint8_t*>(kc) + base;
+      const uint8_t* vt = reinterpret_cast<const uint8_t*>(vc) + base;
+#pragma unroll
+      for (int e = 0; e < C::PER_THREAD; ++e) {
+        const int u = tid + e * kThreads;
+        r.k[e] = ld16(kt + (size_t)u * 16);
+        r.v[e] = ld16(vt + (size_t)u * 16);
+        r.ks[e] = ksb[base / 64 + u / 4];
+        r.vs[e] = vsb[base / 64 + u / 4];
+      }
+    } else {
+      const uint16_t* kt = kh + (size_t)t0 * D;
+      const uint16_t* vt = vh + (size_t)t0 * D;
+#pragma unroll
+      for (int e = 0; e < C::PER_THREAD; ++e) {
+        const int u = tid + e * kThreads;
+        r.k[e] = ld16(kt + (size_t)u * 8);
+        r.v[e] = ld16(vt + (size_t)u * 8);
+      }
     }
   };
   auto stage = [&](const KV& r) __attribute__((always_inline)) {
@@ -402,24 +434,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
   };
   static_assert(KV8 || C::UNITS % kThreads == 0, "every thread moves whole 16-byte units of a tile");
-  // While at least four tiles remain, both fetches of a pair of tiles are in
-  // the range and go out unconditionally, so the compiler's wait counts stay
-  // exact and two tiles stay in flight across each staging; a fetch under a
-  // run-time test makes it wait for every load in flight. The last one to
-  // three tiles (and ranges that short) take the tested loop.
+  // While four more whole tiles of plain cache rows remain, both fetches of
+  // a pair are in the range and go out unconditionally, so the compiler's
+  // wait counts stay exact and two tiles stay in flight across each staging;
+  // a fetch under a run-time test makes it wait for every load in flight. The
+  // last tiles (at most three, plus the one holding appended rows) and short
+  // ranges take the tested loop.
   int t0 = j0;
-  if (j0 + 3 * kTileKeys < j1) {
-    fetch(r0, j0);
-    fetch(r1, j0 + kTileKeys);
+  if (j0 + 4 * kTileKeys <= lim_plain) {
+    fetch_plain(r0, j0);
+    fetch_plain(r1, j0 + kTileKeys);
     do {
       stage(r0);
-      fetch(r0, t0 + 2 * kTileKeys);
+      fetch_plain(r0, t0 + 2 * kTileKeys);
       tile(t0);
       stage(r1);
-      fetch(r1, t0 + 3 * kTileKeys);
+      fetch_plain(r1, t0 + 3 * kTileKeys);
       tile(t0 + kTileKeys);
       t0 += 2 * kTileKeys;
-    } while (t0 + 3 * kTileKeys < j1);
+    } while (t0 + 4 * kTileKeys <= lim_plain);
   } else {
     if (j0 < j1) fetch(r0, j0);
     if (j0 + kTileKeys < j1) fetch(r1, j0 + kTileKeys);
