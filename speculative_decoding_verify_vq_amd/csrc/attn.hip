@@ -49,6 +49,7 @@
 // score.
 #include <math.h>
 
+#include "lanes.h"
 #include "vq_internal.h"
 
 namespace vq {
@@ -74,18 +75,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
-}
-
-// The values of lanes i and i ^ 32, in one VALU instruction: gfx950's
-// v_permlane32_swap exchanges the upper half of the first operand with the
-// lower half of the second, so with both operands v each lane ends up holding
-// v[i] and v[i ^ 32] (an LDS permute takes a round trip through the LDS unit).
-struct LanePair {
-  float a, b;
-};
-__device__ __forceinline__ LanePair xor32_pair(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -584,7 +573,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   float mloc = -INFINITY;
 #pragma unroll
   for (int k = 0; k < kMLPT; ++k) mloc = fmaxf(mloc, ml[k].x);
-  for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+  mloc = max64_lanes(mloc);
   if ((tid & 63) == 0) red[tid >> 6] = mloc;
   __syncthreads();
   const float mmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -598,7 +587,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
       dloc += w;
     }
   }
-  for (int off = 32; off > 0; off >>= 1) dloc += __shfl_xor(dloc, off);
+  dloc = sum64_lanes(dloc);
   __syncthreads();
   if ((tid & 63) == 0) red[tid >> 6] = dloc;
   __syncthreads();

@@ -60,6 +60,7 @@
 
 #include <type_traits>
 
+#include "lanes.h"
 #include "vq_internal.h"
 
 namespace vq {
@@ -128,35 +129,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 __device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_rne(f)); }
-
-// Lane exchange within rows of 16 lanes (DPP; no LDS round trip). Controls:
-// 0xB1 quad_perm [1,0,3,2] (lane ^ 1), 0x4E quad_perm [2,3,0,1] (lane ^ 2),
-// 0x141 row_half_mirror (lane i <-> 7 - i within each 8 lanes).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over each aligned group of 8 lanes, the same value in all 8 (the pairs
-// of each step are those of an xor-1, xor-2, xor-4 butterfly).
-__device__ __forceinline__ float sum8_lanes(float v) {
-  v += dpp_f32<0xB1>(v);
-  v += dpp_f32<0x4E>(v);
-  return v + dpp_f32<0x141>(v);
-}
-
-// Sum over the whole wave, the same value in every lane, with no LDS round
-// trip: groups of 8, then 16 (DPP row_mirror, lane i <-> 15 - i), then rows
-// paired by gfx950's permlane swaps (16 and 32 lanes apart; each hands a lane
-// both values, and a + b == b + a, so every lane gets the same sum).
-__device__ __forceinline__ float sum64_lanes(float v) {
-  v = sum8_lanes(v);
-  v += dpp_f32<0x140>(v);
-  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
-}
 
 // Eight nibbles -> eight bf16 values 128 + q, in the element order
 // (q0, q4, q1, q5, q2, q6, q3, q7).
