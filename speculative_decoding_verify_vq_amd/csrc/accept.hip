@@ -27,6 +27,7 @@
 //                  running sums of every position's residual are tabulated once
 //                  and each trial is one thread: K tests and a binary search.
 #include "vq.h"
+#include "lanes.h"
 #include "vq_internal.h"
 
 namespace vq {
@@ -143,7 +144,7 @@ __device__ T block_excl_scan(T v, T* lds /* NT/64 + 1 entries */, T& total) {
 }
 
 __device__ float block_reduce_max(float v, float* lds) {
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  v = max64_lanes(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) lds[wave] = v;
@@ -154,7 +155,7 @@ __device__ float block_reduce_max(float v, float* lds) {
 }
 
 __device__ float block_reduce_sum(float v, float* lds) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  v = sum64_lanes(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) lds[wave] = v;
@@ -1316,10 +1317,9 @@ __device__ u64 select_top(const u64 (&key)[kSelJ], int nj, uint32_t need, TopLds
         a &= key[j];
       }
     }
-    for (int off = 32; off > 0; off >>= 1) {
-      o |= shfl_xor_u64(o, off);
-      a &= shfl_xor_u64(a, off);
-    }
+    // Over the wave, each 32-bit half on its own (the operations are bitwise).
+    o = ((u64)or64_lanes((uint32_t)(o >> 32)) << 32) | or64_lanes((uint32_t)o);
+    a = ((u64)and64_lanes((uint32_t)(a >> 32)) << 32) | and64_lanes((uint32_t)a);
     if (lane == 0) {
       s.r_or[wave] = o;
       s.r_and[wave] = a;

@@ -63,4 +63,30 @@ __device__ __forceinline__ float max64_lanes(float v) {
   return fmaxf(q.a, q.b);
 }
 
+// Bitwise OR and AND of a 32-bit value over the whole wave, in the same steps.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t or64_lanes(uint32_t v) {
+  v |= dpp_u32<0xB1>(v);
+  v |= dpp_u32<0x4E>(v);
+  v |= dpp_u32<0x141>(v);
+  v |= dpp_u32<0x140>(v);
+  const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = p[0] | p[1];
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return q[0] | q[1];
+}
+__device__ __forceinline__ uint32_t and64_lanes(uint32_t v) {
+  v &= dpp_u32<0xB1>(v);
+  v &= dpp_u32<0x4E>(v);
+  v &= dpp_u32<0x141>(v);
+  v &= dpp_u32<0x140>(v);
+  const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = p[0] & p[1];
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return q[0] & q[1];
+}
+
 }  // namespace vq
