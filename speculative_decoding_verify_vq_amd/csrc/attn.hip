@@ -69,6 +69,12 @@ __device__ __forceinline__ v4i16 ds_read_tr16(const uint16_t* p) {
 
 constexpr int kThreads = 256;
 constexpr int kTileKeys = 32;
+// Sixteen zero bytes in global memory: read in place of a tree mask word when
+// there is none, and of query rows past the last one.
+__device__ __attribute__((aligned(16))) uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
+typedef const uint32_t __attribute__((address_space(1))) global_u32;
+typedef const u32x4 __attribute__((address_space(1))) global_u32x4;
+typedef const bf16x8 __attribute__((address_space(1))) global_bf16x8;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -97,6 +103,16 @@ struct AttnCfg {
   static constexpr int UPK = KV8 ? D / 16 : D / 8;         // 16-byte units per key row
   static constexpr int UNITS = kTileKeys * UPK;             // 16-byte units per K (or V) tile
   static constexpr int PER_THREAD = (UNITS + kThreads - 1) / kThreads;
+  // One row tile: every wave holds the whole of Q (D/4 registers per lane) as
+  // the B operand of S, instead of reading it from LDS on every tile.
+  static constexpr bool QREG = RT == 1;
+  static constexpr int Q_LDS = QREG ? 1 : RT * 32 * LD;         // elements
+  static constexpr int KV_LDS = kTileKeys * (LD + LDV);          // elements per K/V tile pair
+  // Two K/V buffers (the next tile is written while the current one is read,
+  // one barrier per tile) where they fit: two workgroups per compute unit
+  // within 80 KB, or D = 256 with three or four row tiles (one per unit).
+  static constexpr int LDS1 = 2 * (Q_LDS + KV_LDS);
+  static constexpr int NBUF = (LDS1 + 2 * KV_LDS <= 80 * 1024 || (D >= 256 && RT >= 3)) ? 2 : 1;
 };
 
 // 16 codes and their (scale, bias) word -> 16 bf16 values s * q + b.
@@ -131,7 +147,7 @@ __device__ __forceinline__ bool seq_bounds(const AttnBatch& bt, int b, int M_max
 }
 
 template <int D, int RT, bool KV8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_partial_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((D >= 256 && RT >= 3) ? 1 : 2, 8))) void attn_partial_kernel(
     const uint16_t* __restrict__ q, int64_t q_rs, const uint16_t* kc, const uint16_t* vc, int64_t kv_head_stride,
     int M_max, int Hq, int Hkv, int T_max, float scale_log2, int keys_per_split, int splits, uint16_t* __restrict__ out,
     int64_t out_rs, uint16_t* __restrict__ part_o, float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
@@ -166,9 +182,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
     if (tree) tree += row0;
   }
-  __shared__ uint16_t q_lds[RT * 32 * C::LD];
-  __shared__ uint16_t k_lds[kTileKeys * C::LD];
-  __shared__ uint16_t v_lds[kTileKeys * C::LDV];
+  __shared__ uint16_t q_lds[C::Q_LDS];
+  __shared__ uint16_t k_lds[C::NBUF][kTileKeys * C::LD];
+  __shared__ uint16_t v_lds[C::NBUF][kTileKeys * C::LDV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -182,27 +198,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   const int j0 = split * keys_per_split;
   const int j1 = min(T, j0 + keys_per_split);
 
-  // Stage the query rows of this KV head: row i = (position i / G, head kvh*G + i % G).
-  // All loads go out together (rows past `rows` read row 0 and store zeros), so
-  // staging costs one memory round trip.
-  {
-    constexpr int kQPT = RT * 32 * (D / 8) / kThreads;
-    static_assert(kQPT * kThreads == RT * 32 * (D / 8), "query staging must be uniform");
-    uint4 qv[kQPT];
+  // The query rows of this KV head: row i = (position i / G, head kvh*G + i % G).
+  // All loads go out together, before the first K/V tiles are fetched (the
+  // wait for them comes after those fetches are issued, so the ramp is one
+  // memory round trip, not two).
+  // This lane's row and its word of the tree mask, then the query rows of
+  // this KV head (row i = position i / G, head kvh*G + i % G), all loaded
+  // before the first K/V tiles are fetched and waited for only after those
+  // fetches are issued, so the ramp is one memory round trip, not two. Every
+  // load goes out unconditionally: a word past the last row, and the mask
+  // word without a mask, come from a zero vector (the pointer is chosen, not
+  // the loaded value: code that chooses between a loaded value and another
+  // waits for every load in flight first). The mask word is used only in
+  // masked tiles.
+  const int rt = wave / C::DS;
+  const int row = rt * 32 + l32;  // this lane's query row (softmax owner)
+  const bool row_ok = row < rows;
+  const int mpos = row_ok ? row / G : 0;
+  const uint32_t tword = *(tree ? (const global_u32*)(tree + mpos) : (const global_u32*)kZero16);
+  constexpr int kQPT = C::QREG ? 1 : RT * 32 * (D / 8) / kThreads;
+  static_assert(C::QREG || kQPT * kThreads == RT * 32 * (D / 8), "query staging must be uniform");
+  bf16x8 qr[C::QREG ? D / 16 : 1];
+  u32x4 qv[kQPT];
+  if constexpr (C::QREG) {
+    // Lane l: row l % 32, head dims 16c + 8(l / 32) .. +7 of step c (the B
+    // operand layout of S).
+    const uint16_t* qrow = q + (size_t)(row / G) * q_rs + ((size_t)kvh * G + row % G) * D + 8 * kq;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      qr[c] = *(row_ok ? (const global_bf16x8*)(qrow + 16 * c) : (const global_bf16x8*)kZero16);
+  } else {
 #pragma unroll
     for (int e = 0; e < kQPT; ++e) {
       const int u = tid + e * kThreads;
       const int i = u / (D / 8), dc = u % (D / 8);
-      const int ic = i < rows ? i : 0;
-      qv[e] = *reinterpret_cast<const uint4*>(q + (size_t)(ic / G) * q_rs + ((size_t)kvh * G + ic % G) * D + dc * 8);
-    }
-#pragma unroll
-    for (int e = 0; e < kQPT; ++e) {
-      const int u = tid + e * kThreads;
-      const int i = u / (D / 8), dc = u % (D / 8);
-      *reinterpret_cast<uint4*>(&q_lds[i * C::LD + dc * 8]) = i < rows ? qv[e] : make_uint4(0, 0, 0, 0);
+      const uint16_t* src = q + (size_t)(i / G) * q_rs + ((size_t)kvh * G + i % G) * D + dc * 8;
+      qv[e] = *(i < rows ? (const global_u32x4*)src : (const global_u32x4*)kZero16);
     }
   }
+  // Called right after the first two fetches, ahead of the barrier before the
+  // first tile.
+  auto q_to_lds = [&]() __attribute__((always_inline)) {
+    if constexpr (!C::QREG) {
+#pragma unroll
+      for (int e = 0; e < kQPT; ++e) {
+        const int u = tid + e * kThreads;
+        const int i = u / (D / 8), dc = u % (D / 8);
+        *reinterpret_cast<u32x4*>(&q_lds[i * C::LD + dc * 8]) = qv[e];
+      }
+    }
+  };
 
   const uint16_t* kh = kc + (size_t)kvh * kv_head_stride;
   const uint16_t* vh = vc + (size_t)kvh * kv_head_stride;
@@ -283,42 +328,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
       }
     }
   };
-  auto stage = [&](const KV& r) __attribute__((always_inline)) {
-    __syncthreads();
+  // Write a fetched tile into K/V buffer `buf` (8-bit codes dequantized here).
+  auto put = [&](const KV& r, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < C::PER_THREAD; ++e) {
       if constexpr (KV8) {
         const int u = tid + e * kThreads;
-        if (u < C::UNITS) {
+        if (C::UNITS % kThreads == 0 || u < C::UNITS) {  // a test only where the tile is not whole units per thread
           const int key = u / C::UPK;
           const int dc = u % C::UPK;
           u32x4 lo, hi;
           dequant16(r.k[e], r.ks[e], lo, hi);
-          *reinterpret_cast<u32x4*>(&k_lds[key * C::LD + dc * 16]) = lo;
-          *reinterpret_cast<u32x4*>(&k_lds[key * C::LD + dc * 16 + 8]) = hi;
+          *reinterpret_cast<u32x4*>(&k_lds[buf][key * C::LD + dc * 16]) = lo;
+          *reinterpret_cast<u32x4*>(&k_lds[buf][key * C::LD + dc * 16 + 8]) = hi;
           dequant16(r.v[e], r.vs[e], lo, hi);
-          *reinterpret_cast<u32x4*>(&v_lds[key * C::LDV + dc * 16]) = lo;
-          *reinterpret_cast<u32x4*>(&v_lds[key * C::LDV + dc * 16 + 8]) = hi;
+          *reinterpret_cast<u32x4*>(&v_lds[buf][key * C::LDV + dc * 16]) = lo;
+          *reinterpret_cast<u32x4*>(&v_lds[buf][key * C::LDV + dc * 16 + 8]) = hi;
         }
         continue;
       }
       const int u = tid + e * kThreads;
       const int key = u / (D / 8);
       const int dc = u % (D / 8);
-      *reinterpret_cast<u32x4*>(&k_lds[key * C::LD + dc * 8]) = r.k[e];
-      *reinterpret_cast<u32x4*>(&v_lds[key * C::LDV + dc * 8]) = r.v[e];
+      *reinterpret_cast<u32x4*>(&k_lds[buf][key * C::LD + dc * 8]) = r.k[e];
+      *reinterpret_cast<u32x4*>(&v_lds[buf][key * C::LDV + dc * 8]) = r.v[e];
     }
+  };
+  // With one buffer: wait until every wave is done with the tile in it, write
+  // the next one, wait until every wave can see it.
+  auto stage = [&](const KV& r) __attribute__((always_inline)) {
+    __syncthreads();
+    put(r, 0);
     __syncthreads();
   };
 
-  const int rt = wave / C::DS;
   const int dpart = wave % C::DS;
   const bool active = wave < RT * C::DS;
-  const int row = rt * 32 + l32;             // this lane's query row (softmax owner)
-  const bool row_ok = row < rows;
-  const int mpos = row_ok ? row / G : 0;
-  // Drafted keys T-M+t this lane's row sees: bit t (the row itself always).
-  const uint32_t seen = (tree ? tree[mpos] : (0xFFFFFFFFu >> (31 - mpos))) | (1u << mpos);
+  const bool causal = tree == nullptr;
   const int t_new = T - M;  // first drafted key
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -326,15 +372,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
   for (int t = 0; t < C::DT; ++t) o[t] = f32x16{};
 
-  auto tile = [&](int t0) __attribute__((always_inline)) {
+  auto tile = [&](int t0, int buf) __attribute__((always_inline)) {
     if (!active) return;
 
     // S^T[key][row] = sum_d K[key][d] Q[row][d]
     f32x16 s = {};
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[l32 * C::LD + 16 * i + 8 * kq]);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&q_lds[row * C::LD + 16 * i + 8 * kq]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[buf][l32 * C::LD + 16 * i + 8 * kq]);
+      bf16x8 b;
+      if constexpr (C::QREG)
+        b = qr[i];
+      else
+        b = *reinterpret_cast<const bf16x8*>(&q_lds[row * C::LD + 16 * i + 8 * kq]);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s, 0, 0, 0);
     }
     // Scale and mask, for this lane's row (keys split between lanes l, l^32). A
@@ -352,7 +402,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
       for (int r = 0; r < 16; ++r) {
         const int j = t0 + 8 * (r >> 2) + 4 * kq + (r & 3);
         const int jr = j - t_new;
-        const uint32_t vis = (uint32_t)(j < j1) & ((uint32_t)(jr < 0) | ((seen >> (jr & 31)) & 1u));
+        // Drafted key T-M+t is seen by row position i if t == i, if bit t of
+        // the row's mask word is set, or (without a mask) if t < i.
+        const uint32_t vis = (uint32_t)(j < j1) & ((uint32_t)(jr < 0) | (uint32_t)(jr == mpos) |
+                                                   (uint32_t)(causal & (jr < mpos)) | ((tword >> (jr & 31)) & 1u));
         s[r] = vis ? s[r] * scale_log2 : -INFINITY;
         mx = fmaxf(mx, s[r]);
       }
@@ -415,45 +468,91 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int kb = 16 * c + 4 * kq + (tg >> 2);
-        const v4i16 lo = ds_read_tr16(&v_lds[kb * C::LDV + dcol]);
-        const v4i16 hi = ds_read_tr16(&v_lds[(kb + 8) * C::LDV + dcol]);
+        const v4i16 lo = ds_read_tr16(&v_lds[buf][kb * C::LDV + dcol]);
+        const v4i16 hi = ds_read_tr16(&v_lds[buf][(kb + 8) * C::LDV + dcol]);
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, c ? pb1 : pb0, o[t], 0, 0, 0);
       }
     }
   };
   static_assert(KV8 || C::UNITS % kThreads == 0, "every thread moves whole 16-byte units of a tile");
-  // While four more whole tiles of plain cache rows remain, both fetches of
-  // a pair are in the range and go out unconditionally, so the compiler's
-  // wait counts stay exact and two tiles stay in flight across each staging;
-  // a fetch under a run-time test makes it wait for every load in flight. The
-  // last tiles (at most three, plus the one holding appended rows) and short
-  // ranges take the tested loop.
+  // While enough whole tiles of plain cache rows remain, the fetches go out
+  // unconditionally, so the compiler's wait counts stay exact and two tiles
+  // stay in flight across each staging; a fetch under a run-time test makes it
+  // wait for every load in flight. The last tiles (plus the one holding
+  // appended rows) and short ranges take the tested loop.
   int t0 = j0;
-  if (j0 + 4 * kTileKeys <= lim_plain) {
-    fetch_plain(r0, j0);
-    fetch_plain(r1, j0 + kTileKeys);
-    do {
-      stage(r0);
-      fetch_plain(r0, t0 + 2 * kTileKeys);
-      tile(t0);
-      stage(r1);
-      fetch_plain(r1, t0 + 3 * kTileKeys);
-      tile(t0 + kTileKeys);
-      t0 += 2 * kTileKeys;
-    } while (t0 + 4 * kTileKeys <= lim_plain);
-  } else {
-    if (j0 < j1) fetch(r0, j0);
-    if (j0 + kTileKeys < j1) fetch(r1, j0 + kTileKeys);
-  }
-  for (; t0 < j1; t0 += 2 * kTileKeys) {
-    stage(r0);
-    if (t0 + 2 * kTileKeys < j1) fetch(r0, t0 + 2 * kTileKeys);
-    tile(t0);
-    if (t0 + kTileKeys < j1) {
-      stage(r1);
+  if constexpr (C::NBUF == 2) {
+    // At the top of each pair: buffer 0 holds tile t0 (visible to all waves),
+    // r1 tile t0 + 32 and r0 tile t0 + 64 (in flight). A buffer is rewritten
+    // only after the barrier that follows the last reads of it.
+    if (j0 + 5 * kTileKeys <= lim_plain) {
+      fetch_plain(r0, j0);
+      fetch_plain(r1, j0 + kTileKeys);
+      q_to_lds();
+      put(r0, 0);
+      fetch_plain(r0, j0 + 2 * kTileKeys);
+      __syncthreads();
+      do {
+        tile(t0, 0);
+        put(r1, 1);
+        fetch_plain(r1, t0 + 3 * kTileKeys);
+        __syncthreads();
+        tile(t0 + kTileKeys, 1);
+        put(r0, 0);
+        fetch_plain(r0, t0 + 4 * kTileKeys);
+        __syncthreads();
+        t0 += 2 * kTileKeys;
+      } while (t0 + 5 * kTileKeys <= lim_plain);
+    } else if (j0 < j1) {
+      fetch(r0, j0);
+      if (j0 + kTileKeys < j1) fetch(r1, j0 + kTileKeys);
+      q_to_lds();
+      put(r0, 0);
+      if (j0 + 2 * kTileKeys < j1) fetch(r0, j0 + 2 * kTileKeys);
+      __syncthreads();
+    }
+    while (t0 < j1) {
+      tile(t0, 0);
+      if (t0 + kTileKeys >= j1) break;
+      put(r1, 1);
       if (t0 + 3 * kTileKeys < j1) fetch(r1, t0 + 3 * kTileKeys);
-      tile(t0 + kTileKeys);
+      __syncthreads();
+      tile(t0 + kTileKeys, 1);
+      if (t0 + 2 * kTileKeys >= j1) break;
+      put(r0, 0);
+      if (t0 + 4 * kTileKeys < j1) fetch(r0, t0 + 4 * kTileKeys);
+      __syncthreads();
+      t0 += 2 * kTileKeys;
+    }
+  } else {
+    if (j0 + 4 * kTileKeys <= lim_plain) {
+      fetch_plain(r0, j0);
+      fetch_plain(r1, j0 + kTileKeys);
+      q_to_lds();
+      do {
+        stage(r0);
+        fetch_plain(r0, t0 + 2 * kTileKeys);
+        tile(t0, 0);
+        stage(r1);
+        fetch_plain(r1, t0 + 3 * kTileKeys);
+        tile(t0 + kTileKeys, 0);
+        t0 += 2 * kTileKeys;
+      } while (t0 + 4 * kTileKeys <= lim_plain);
+    } else {
+      if (j0 < j1) fetch(r0, j0);
+      if (j0 + kTileKeys < j1) fetch(r1, j0 + kTileKeys);
+      q_to_lds();
+    }
+    for (; t0 < j1; t0 += 2 * kTileKeys) {
+      stage(r0);
+      if (t0 + 2 * kTileKeys < j1) fetch(r0, t0 + 2 * kTileKeys);
+      tile(t0, 0);
+      if (t0 + kTileKeys < j1) {
+        stage(r1);
+        if (t0 + 3 * kTileKeys < j1) fetch(r1, t0 + 3 * kTileKeys);
+        tile(t0 + kTileKeys, 0);
+      }
     }
   }
 

@@ -276,3 +276,34 @@ def test_batched_append_and_empty_sequence(vq):
         ref = oa.multirow_attention(qs[b], ka, va, m, Hq, Hkv, D, T, T_cap, 0.09)
         assert_close(out[r0: r0 + m], ref, f"sequence {b} with append")
         r0 += m
+
+
+# Long key ranges (16 KV heads, ten tiles per range: the unconditional main
+# loop and the tested tail both run) at every row-tile count, for the head
+# sizes the 27B shape does not use. Every row of the last KV head is compared
+# (every row position of every row tile).
+LONG_RANGES = [
+    (4, 32, 64), (8, 96, 64), (16, 80, 64), (16, 128, 64),     # 8 / 48 / 80 / 128 rows per KV head
+    (4, 32, 128), (8, 96, 128), (16, 80, 128), (16, 128, 128),
+]
+LONG_HKV, LONG_CTX = 16, 5000
+
+
+@pytest.mark.parametrize("M,Hq,D", LONG_RANGES)
+@pytest.mark.parametrize("tree", [False, True])
+def test_long_ranges_every_row_tile(vq, M, Hq, D, tree):
+    from synth import tree_masks
+    Hkv, T = LONG_HKV, LONG_CTX + M
+    G = Hq // Hkv
+    q, k, v = attn_inputs(60 + M, M, Hq, Hkv, D, T, extra=D)
+    scale = 1 / math.sqrt(D)
+    mask = tree_masks(60, M, extra=D) if tree else None
+    got = to_f64(_tree(vq, q, k, v, T, scale, mask)) if tree else _run(vq, q, k, v, T, scale)
+    # The oracle on the last KV head alone (heads are independent): its G query
+    # heads against that head's cache.
+    qs, ks, vs = np.ascontiguousarray(q[:, Hq - G:]), k[Hkv - 1:], v[Hkv - 1:]
+    if tree:
+        ref = oa.tree_attention(qs, ks, vs, M, G, 1, D, T, T, scale, mask)
+    else:
+        ref = oa.multirow_attention(qs, ks, vs, M, G, 1, D, T, T, scale)
+    assert_close(got[:, Hq - G:], ref, f"long ranges M={M} Hq={Hq} D={D} tree={tree}")

@@ -142,3 +142,22 @@ def test_int8_config_sampled(vq):
     pairs = [(m, int(h)) for m in range(M) for h in rng.choice(Hq, 2, replace=False)]
     ref = okv.int8_attention(q, kc, ks, vc, vs, M, Hq, Hkv, D, T, T, 1 / 16, pairs=pairs)
     assert_close(np.stack([out[m, h] for m, h in pairs]), ref, "int8 at 16k")
+
+
+@pytest.mark.parametrize("M,Hq,D", [(4, 32, 64), (16, 128, 64), (4, 32, 128), (8, 96, 128), (16, 80, 128),
+                                    (16, 128, 128)])
+def test_int8_long_ranges(vq, M, Hq, D):
+    """Ten tiles per key range (16 KV heads): the unconditional main loop and
+    the tested tail both run; every row of the last KV head compared."""
+    Hkv, T = 16, 5000 + M
+    q, kc, ks, vc, vs = _oracle_cache(70 + M, M, Hq, Hkv, D, T)
+    scale = 1 / math.sqrt(D)
+    k8, kw = _dev_cache(kc, ks)
+    v8, vw = _dev_cache(vc, vs)
+    out = to_f64(vq.multirow_attn_int8(bf16_tensor(q), k8, kw, v8, vw, T, scale))
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    # The oracle on the last KV head alone (heads are independent).
+    ref = okv.int8_attention(np.ascontiguousarray(q[:, Hq - G:]), kc[Hkv - 1:], ks[Hkv - 1:], vc[Hkv - 1:],
+                             vs[Hkv - 1:], M, G, 1, D, T, T, scale)
+    assert_close(out[:, Hq - G:], ref, f"int8 long ranges M={M} Hq={Hq} D={D}")
