@@ -198,19 +198,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((D >= 
   const int j0 = split * keys_per_split;
   const int j1 = min(T, j0 + keys_per_split);
 
-  // The query rows of this KV head: row i = (position i / G, head kvh*G + i % G).
-  // All loads go out together, before the first K/V tiles are fetched (the
-  // wait for them comes after those fetches are issued, so the ramp is one
-  // memory round trip, not two).
   // This lane's row and its word of the tree mask, then the query rows of
   // this KV head (row i = position i / G, head kvh*G + i % G), all loaded
   // before the first K/V tiles are fetched and waited for only after those
   // fetches are issued, so the ramp is one memory round trip, not two. Every
-  // load goes out unconditionally: a word past the last row, and the mask
-  // word without a mask, come from a zero vector (the pointer is chosen, not
-  // the loaded value: code that chooses between a loaded value and another
-  // waits for every load in flight first). The mask word is used only in
-  // masked tiles.
+  // load goes out unconditionally: a row past the last one, and the mask word
+  // without a mask, come from a zero vector (the pointer is chosen, never
+  // dereferenced out of range; code that chooses between a loaded value and
+  // another waits for every load in flight first). The mask word is used only
+  // in masked tiles.
   const int rt = wave / C::DS;
   const int row = rt * 32 + l32;  // this lane's query row (softmax owner)
   const bool row_ok = row < rows;
