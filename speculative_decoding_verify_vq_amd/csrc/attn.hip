@@ -12,12 +12,14 @@
 //
 // Per 32-key tile:
 //   * the tile is loaded with coalesced 16-byte loads into registers two tiles
-//     ahead, then written to LDS row-major;
+//     ahead, then written to LDS row-major (into the second of two K/V buffers
+//     where they fit, so a tile costs one barrier, not two);
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q rows
-//     from LDS); in the output layout each lane holds 16 keys of one query row,
-//     so the online-softmax statistics of a row live in one lane pair;
+//     from LDS, or from registers with a single row tile); in the output
+//     layout each lane holds 16 keys of one query row, so the online-softmax
+//     statistics of a row live in one lane pair;
 //   * O^T += V^T P^T on the same MFMA: B = P (this lane's own probabilities,
-//     rounded to bf16), A = V gathered from LDS along the key axis with 16-bit
+//     rounded to bf16), A = V read from LDS along the key axis with transposed
 //     reads, so the row rescaling stays lane-local.
 // Waves split the query rows into tiles of 32 and, when there are few rows,
 // the head dimension of O across waves (each of those waves recomputes the
