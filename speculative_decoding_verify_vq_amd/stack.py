@@ -160,11 +160,13 @@ class DenseVerifyStack:
         off = (-buf.data_ptr()) % 256
         return buf[off:]
 
-    def _qmm(self, x, pack: QPack, out, *, norm: bool = False, epilogue: int = vq.VQ_EPI_STORE, y_sumsq=None):
+    def _qmm(self, x, pack: QPack, out, *, norm: bool = False, epilogue: int = vq.VQ_EPI_STORE, y_sumsq=None,
+             residual=None):
+        if epilogue == vq.VQ_EPI_RESIDUAL and residual is None:
+            residual = self.h
         vq.qmm_packed(x, pack.packed, pack.bits, pack.N, pack.K, group_size=pack.group_size,
                       x_sumsq=self.ss if norm else None, eps=self.cfg.eps, epilogue=epilogue,
-                      residual=self.h if epilogue == vq.VQ_EPI_RESIDUAL else None, out=out, y_sumsq=y_sumsq,
-                      workspace=self._wsv("qmm"))
+                      residual=residual, out=out, y_sumsq=y_sumsq, workspace=self._wsv("qmm"))
 
     def forward_hidden(self, h_in: torch.Tensor, after_layer=None) -> torch.Tensor:
         """Runs the layers on h_in [M, hidden] (bf16); returns the final hidden rows
@@ -172,11 +174,15 @@ class DenseVerifyStack:
         ``after_layer(layer, h)``, if given, is called after each layer with the
         hidden rows (on the stream, before the next layer's launches)."""
         cfg = self.cfg
-        self.h.copy_(h_in)
-        vq.row_sumsq(self.h, out=self.ss)
+        # Layer 0 reads h_in directly (its residual epilogue writes the first
+        # hidden rows into self.h), so no copy of h_in is launched.
+        vq.row_sumsq(h_in, out=self.ss)
+        if not self.w.layers:
+            self.h.copy_(h_in)
         ai = 0
         for li, lay in enumerate(self.w.layers):
-            self._qmm(self.h, lay["qkv"], self.qkv, norm=True)
+            src = h_in if li == 0 else self.h
+            self._qmm(src, lay["qkv"], self.qkv, norm=True)
             q = self.qkv[:, : cfg.q_width]
             if cfg.is_attn(li):
                 kc, vc = self.w.k_cache[ai], self.w.v_cache[ai]
@@ -196,7 +202,7 @@ class DenseVerifyStack:
                 c = self.ctx_out
             else:
                 c = q
-            self._qmm(c, lay["o"], self.h, epilogue=vq.VQ_EPI_RESIDUAL, y_sumsq=self.ss)
+            self._qmm(c, lay["o"], self.h, epilogue=vq.VQ_EPI_RESIDUAL, y_sumsq=self.ss, residual=src)
             self._qmm(self.h, lay["gate_up"], self.act, norm=True, epilogue=vq.VQ_EPI_SWIGLU)
             self._qmm(self.act, lay["down"], self.h, epilogue=vq.VQ_EPI_RESIDUAL, y_sumsq=self.ss)
             if after_layer is not None:
