@@ -299,7 +299,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   // unrolled, so the wait counts the compiler derives are exact: with a
   // conditional issue it cannot count the loads in flight at the next block and
   // waits for all of them, which leaves one block in flight instead of two. The
-  // chunked variant issues only blocks inside the range.
+  // chunked variant issues only blocks inside the range, under tests known at
+  // compile time except in a ragged last chunk.
   Regs R[kInFlight];
 
   // ---- x, staged in chunks of CG groups in the element order of the unpack,
