@@ -52,11 +52,13 @@ def test_config2_sampled(vq, ctx, M):
     assert_close(got, ref, f"ctx={ctx} M={M}")
 
 
-def test_config4_context_sampled(vq):
+@pytest.mark.parametrize("M", [8, 2])
+def test_config4_context_sampled(vq, M):
     """The 8-bit step's attention shape: 8 rows over 131072 committed positions
     (T = 131080, 129 key ranges of 32 tiles per KV head and the combine), on
-    sampled (row, head) pairs."""
-    M, Hq, Hkv, D, ctx = 8, 24, 4, 256, 131072
+    sampled (row, head) pairs; and 2 rows (one row tile: queries in registers,
+    two K/V buffers, two workgroups per compute unit)."""
+    Hq, Hkv, D, ctx = 24, 4, 256, 131072
     T = ctx + M
     q, k, v = attn_inputs(4, M, Hq, Hkv, D, T, extra=ctx)
     out = _run(vq, q, k, v, T, 1 / 16)
