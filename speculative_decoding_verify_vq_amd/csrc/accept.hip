@@ -1258,6 +1258,7 @@ __global__ __launch_bounds__(kRowThreads) void rows_resolve_kernel(int V, int to
 constexpr int kTopKMax = 64;
 constexpr u64 kNoKey = ~0ull;  // an empty slot: above every 50-bit key, so in no region
 constexpr int kSelJ = 16;      // keys per thread in the selects: 16 * kCT = kChunk, 16 * 1024 = kCandCap
+constexpr int kFewKeys = 256;  // at most this many merge candidates are ranked directly
 static_assert(kSelJ * kCT == kChunk && kSelJ * kRowThreads == kCandCap, "select capacities");
 static_assert(kTopKMax <= 64, "the top-p walk over the kept keys takes one lane each");
 static_assert((int64_t)kTopKMax * ((VQ_MAX_VOCAB + kChunk - 1) / kChunk) <= kCandCap,
@@ -1463,6 +1464,7 @@ __global__ __launch_bounds__(kRowThreads) void rows_topk_merge_kernel(int C, int
   __shared__ TopLds s;
   __shared__ u64 kept[kTopKMax];
   __shared__ u64 sorted[kTopKMax];
+  __shared__ u64 few[kFewKeys];
   __shared__ u64 red[kRowThreads / 64];
   __shared__ uint32_t n_kept;
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1493,21 +1495,40 @@ __global__ __launch_bounds__(kRowThreads) void rows_topk_merge_kernel(int C, int
     live += kr[j] != kNoKey;
   }
   const uint32_t m = wg_sum<uint32_t>(live, reinterpret_cast<uint32_t*>(red));  // >= top_k
-  const u64 T = m > (uint32_t)top_k ? select_top<kRowThreads>(kr, nj, (uint32_t)top_k, s) : 0ull;
+  int kc;
+  if (m <= (uint32_t)kFewKeys) {
+    // Few candidates (the usual case): a key's rank among them is its place
+    // in descending order (keys are distinct), so the top_k come out sorted
+    // without the digit-by-digit select.
 #pragma unroll
-  for (int j = 0; j < kSelJ; ++j) {
-    if (j < nj && kr[j] != kNoKey && kr[j] >= T) {
-      const uint32_t slot = atomicAdd(&n_kept, 1u);  // < top_k: exactly top_k keys are >= T
-      if (slot < (uint32_t)top_k) kept[slot] = kr[j];
+    for (int j = 0; j < kSelJ; ++j) {
+      if (j < nj && kr[j] != kNoKey) few[atomicAdd(&n_kept, 1u)] = kr[j];  // slots < m
     }
-  }
-  __syncthreads();
-  const int kc = min((int)n_kept, top_k);  // == top_k
-  if (tid < kc) {
-    const u64 mine = kept[tid];
-    int rank = 0;
-    for (int i = 0; i < kc; ++i) rank += kept[i] > mine;
-    sorted[rank] = mine;
+    __syncthreads();
+    if (tid < (int)m) {
+      const u64 mine = few[tid];
+      uint32_t rank = 0;
+      for (uint32_t i = 0; i < m; ++i) rank += few[i] > mine;
+      if (rank < (uint32_t)top_k) sorted[rank] = mine;
+    }
+    kc = (int)min(m, (uint32_t)top_k);
+  } else {
+    const u64 T = select_top<kRowThreads>(kr, nj, (uint32_t)top_k, s);
+#pragma unroll
+    for (int j = 0; j < kSelJ; ++j) {
+      if (j < nj && kr[j] != kNoKey && kr[j] >= T) {
+        const uint32_t slot = atomicAdd(&n_kept, 1u);  // < top_k: exactly top_k keys are >= T
+        if (slot < (uint32_t)top_k) kept[slot] = kr[j];
+      }
+    }
+    __syncthreads();
+    kc = min((int)n_kept, top_k);  // == top_k
+    if (tid < kc) {
+      const u64 mine = kept[tid];
+      int rank = 0;
+      for (int i = 0; i < kc; ++i) rank += kept[i] > mine;
+      sorted[rank] = mine;
+    }
   }
   __syncthreads();
   if (tid >= 64) return;

@@ -251,6 +251,9 @@ def _small_k_row(kind: str, V: int, rng) -> np.ndarray:
         return (p / p.sum()).astype(np.float32)
     if kind == "flat":
         return np.full(V, np.float32(1.0 / V))
+    if kind == "periodic":  # every 4096-element chunk holds the same values
+        p = np.tile(rng.random(4096) ** 8, -(-V // 4096))[:V]
+        return (p / p.sum()).astype(np.float32)
     return _structured_row(kind, V, rng)
 
 
@@ -265,6 +268,11 @@ def _small_k_row(kind: str, V: int, rng) -> np.ndarray:
     (248320, 64, 0.95, "one_hot"),          # fewer nonzero than top_k: zeros in id order
     (248320, 65, 0.95, "one_hot"),          # just above the per-chunk candidate path
     (40000, 50, 0.5, "random"),
+    # every chunk's top values tie with every other chunk's: about 19 (63)
+    # candidates per chunk survive the chunk bound, more than the merge ranks
+    # directly, so the row goes through the digit-by-digit select
+    (248320, 20, 0.95, "periodic"),
+    (248320, 64, 0.9, "periodic"),
 ])
 def test_small_top_k(vq, V, top_k, top_p, kind):
     """Top-k of at most 64 goes through per-chunk candidates and one select per
