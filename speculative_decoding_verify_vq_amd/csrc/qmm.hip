@@ -380,16 +380,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
   for (int i = 0; i < kInFlight; ++i) issue(R[i], i);
   if constexpr (NORM) {
-    // The four rows' butterflies step together: each step is four independent
-    // lane exchanges and one wait, not four dependent ones.
+    // The four rows' wave sums (DPP and permlane steps, no LDS) run
+    // interleaved: four independent chains.
     float t[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t[i] = (ssv[i][0] + ssv[i][1]) + (ssv[i][2] + ssv[i][3]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t[i] += __shfl_xor(t[i], off);
-    }
+    for (int i = 0; i < 4; ++i) t[i] = sum64_lanes((ssv[i][0] + ssv[i][1]) + (ssv[i][2] + ssv[i][3]));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = wave + kWaves * i;
