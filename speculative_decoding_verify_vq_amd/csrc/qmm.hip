@@ -122,11 +122,15 @@ struct Regs {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two floats to bf16, rounded to nearest even, in one instruction
+// (v_cvt_pk_bf16_f32); lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)pack_bf16x2(f, 0.f); }
 
 __device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_rne(f)); }
 
@@ -335,9 +339,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
           const float r = inv_rms[m];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = f32_to_bf16_rne(bf16_bits_to_f32(w[e] & 0xFFFFu) * r);
-            const uint32_t hi = f32_to_bf16_rne(bf16_bits_to_f32(w[e] >> 16) * r);
-            w[e] = lo | (hi << 16);
+            w[e] = pack_bf16x2(bf16_bits_to_f32(w[e] & 0xFFFFu) * r, bf16_bits_to_f32(w[e] >> 16) * r);
           }
         }
       }
