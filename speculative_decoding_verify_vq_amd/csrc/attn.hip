@@ -99,9 +99,12 @@ struct AttnCfg {
   static constexpr int DW = D / DS;                         // head dims per wave
   static constexpr int DT = DW / 32;                        // 32-wide d tiles per wave
   static constexpr int LD = D + 8;                          // K and Q LDS row stride (elements)
-  // V row stride: 8 dwords past a multiple of 64 banks, so that the 16 lanes
-  // of a transposed read (4 keys x 4 8-byte chunks) hit distinct banks.
-  static constexpr int LDV = 128 * ((D - 16 + 127) / 128) + 16;
+  // V row stride: 16 dwords past a multiple of 64 banks. A transposed read
+  // takes, per group of 16 lanes, 4 keys x 4 8-byte chunks (keys 16 banks
+  // apart, so the 16 lanes hit distinct banks), and the two groups of a
+  // 32-lane half, 16 head dims apart, fall into the other 8 banks of each key's
+  // 16 (with 8 dwords past, the second group met the next key's banks).
+  static constexpr int LDV = 128 * ((D - 16 + 127) / 128) + 32;
   static constexpr int UPK = KV8 ? D / 16 : D / 8;         // 16-byte units per key row
   static constexpr int UNITS = kTileKeys * UPK;             // 16-byte units per K (or V) tile
   static constexpr int PER_THREAD = (UNITS + kThreads - 1) / kThreads;
